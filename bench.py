@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""MLA decode on one MI355X: microseconds per call and effective KV HBM bandwidth.
+
+Prints ONE JSON line. The headline workload is fp8-KV decode, batch 32 x kv_len
+1024 (16 heads, 576/512 dims, page size 1, seeded synthetic inputs resident in
+HBM). A "step" is one decode call over the whole batch. Timing:
+
+  * cold (headline): before every timed call a 1 GiB buffer is overwritten,
+    which evicts the 8 x 4 MB L2 and the 256 MB MALL, so the cache rows come
+    from HBM; the call is bracketed by a pair of HIP events on the stream it
+    runs on (the fill keeps the GPU busy while the call is queued, so host
+    submission time is not inside the bracket). value = median over --steps.
+  * warm (secondary, labelled): --steps calls back to back between one event
+    pair; the inputs then sit partly in MALL.
+
+The other four workloads are timed the same way and reported under "grid".
+`roofline` refers to the decode call of the headline workload; `cpu_baseline`
+is the fp64 CPU oracle on a bounded sample of the same workload.
+"""
+import os
+
+os.environ.setdefault("HIP_FORCE_DEV_KERNARG", "1")
+
+import argparse  # noqa: E402
+import hashlib  # noqa: E402
+import json  # noqa: E402
+import platform  # noqa: E402
+import statistics  # noqa: E402
+import sys  # noqa: E402
+import time  # noqa: E402
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+HEADLINE = "fp8_b32_kv1024"
+FLUSH_BYTES = 1 << 30
+KERNEL_SOURCE = os.path.join(ROOT, "mla_decode_02_amd", "csrc", "mla_decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse_args():
+    import synthetic as syn
+
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(syn.WORKLOADS))
+    ap.add_argument("--flags", type=int, default=0, help="MLA_FLAG_* word (0 = library heuristic)")
+    ap.add_argument("--no-grid", action="store_true", help="time only the headline workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--only-gpu-loop", type=int, default=0,
+                    help="skip measurement; run this many back-to-back calls of --workload (for profilers)")
+    return ap.parse_args()
+
+
+def source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def upload(case, dev):
+    import numpy as np
+    import torch
+
+    import synthetic as syn
+
+    q = torch.from_numpy(case.q.view(np.int16)).view(torch.bfloat16).to(dev)
+    if case.kv_dtype == syn.KV_BF16:
+        kv = torch.from_numpy(case.kv.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        kv = torch.from_numpy(case.kv).to(dev)
+    sc = None if case.kv_scales is None else torch.from_numpy(case.kv_scales).to(dev)
+    return q, kv, sc, torch.from_numpy(case.kv_indptr).to(dev), torch.from_numpy(case.kv_indices).to(dev)
+
+
+def measure(name, args, dev, flush):
+    import torch
+
+    import mla_decode_02_amd as mla
+    import synthetic as syn
+
+    case = syn.make_workload(name)
+    q, kv, sc, indptr, indices = upload(case, dev)
+    B = case.batch
+    out = torch.empty((B, 16, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, 16), dtype=torch.float32, device=dev)
+    call = mla.prepare_decode(q, kv, sc, indptr, indices, out, lse, total_kv=case.total_kv,
+                              kv_dtype=case.kv_dtype, flags=args.flags)
+    plan = mla.mla_decode_plan(B, case.total_kv, case.kv_dtype, args.flags)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+
+    # cold: flush, then one bracketed call per step
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for i in range(args.steps):
+        flush.fill_(i & 0xFF)
+        ev[i][0].record()
+        call()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    cold_us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+
+    # warm: back to back behind a fill that lets the queue build up
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    flush.fill_(1)
+    e0.record()
+    for _ in range(args.steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    warm_us = e0.elapsed_time(e1) * 1e3 / args.steps
+
+    med = statistics.median(cold_us)
+    kv_bytes, tot_bytes = case.kv_bytes(), case.total_bytes()
+    return {
+        "workload": name,
+        "kv_format": syn.KV_NAMES[case.kv_dtype],
+        "batch": B,
+        "kv_len": int(case.kv_indptr[1] - case.kv_indptr[0]),
+        "plan": {"mode": "split" if plan.mode == 0 else "persistent", "splits": plan.num_splits,
+                 "grid": plan.grid, "combine_launch": bool(plan.combine)},
+        "cold_us_median": med,
+        "cold_us_p10": cold_us[len(cold_us) // 10],
+        "cold_us_p90": cold_us[(9 * len(cold_us)) // 10],
+        "cold_us_mean": statistics.fmean(cold_us),
+        "warm_us": warm_us,
+        "kv_bytes": kv_bytes,
+        "algorithmic_bytes": tot_bytes,
+        "effective_kv_GBps": kv_bytes / (med * 1e-6) / 1e9,
+        "pct_hbm_peak_kv": 100.0 * kv_bytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+        "algorithmic_GBps": tot_bytes / (med * 1e-6) / 1e9,
+        "wall_ms_per_step_incl_flush": 1e3 * t_wall / args.steps,
+        "_case": case,
+    }
+
+
+def cpu_baseline(case, target_s):
+    """Time the fp64 oracle on a bounded sample of sequences; scale to the whole call."""
+    import oracle
+
+    oracle.build(force=False)
+    B = case.batch
+    t0 = time.perf_counter()
+    oracle.mla_decode(case.q, case.kv_dtype, case.kv, case.kv_scales, case.kv_indptr, case.kv_indices, batches=[0])
+    t_one = time.perf_counter() - t0
+    n = int(max(1, min(B, target_s / max(t_one, 1e-6))))
+    batches = list(range(n))
+    t0 = time.perf_counter()
+    oracle.mla_decode(case.q, case.kv_dtype, case.kv, case.kv_scales, case.kv_indptr, case.kv_indices,
+                      batches=batches)
+    t = time.perf_counter() - t0
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": t * 1e6 * B / n,
+        "unit": "us/call",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": f"{n} of {B} sequences of {case.meta['workload']} (fp64 C oracle, OpenMP over heads), "
+                  f"{t:.1f} s measured, scaled by {B}/{n}",
+        "host_cpu": cpu,
+        "host_nproc": os.cpu_count(),
+    }
+
+
+def load_traffic(name):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = d.get(name)
+    if not ent or ent.get("source_hash") != source_hash():
+        return None  # counters were taken on a different kernel build
+    return ent.get("bytes_per_call")
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(the decode path runs on a single MI355X; see DESIGN.md for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mla_decode_02_amd as mla
+    import synthetic as syn
+
+    dev = torch.device("cuda:0")
+    if args.only_gpu_loop:
+        case = syn.make_workload(args.workload)
+        q, kv, sc, indptr, indices = upload(case, dev)
+        out = torch.empty((case.batch, 16, 512), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((case.batch, 16), dtype=torch.float32, device=dev)
+        call = mla.prepare_decode(q, kv, sc, indptr, indices, out, lse, total_kv=case.total_kv,
+                                  kv_dtype=case.kv_dtype, flags=args.flags)
+        for _ in range(args.only_gpu_loop):
+            call()
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": args.workload, "calls": args.only_gpu_loop}), flush=True)
+        return
+
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    names = [args.workload] + ([] if args.no_grid else [n for n in syn.WORKLOADS if n != args.workload])
+    results = {}
+    for n in names:
+        results[n] = measure(n, args, dev, flush)
+        r = results[n]
+        print(f"# {n}: cold {r['cold_us_median']:.2f} us (p10 {r['cold_us_p10']:.2f}, p90 {r['cold_us_p90']:.2f}), "
+              f"warm {r['warm_us']:.2f} us, {r['effective_kv_GBps']:.0f} GB/s KV ({r['pct_hbm_peak_kv']:.1f}% of 8 TB/s)",
+              file=sys.stderr, flush=True)
+    head = results[args.workload]
+    case = head.pop("_case")
+    for r in results.values():
+        r.pop("_case", None)
+
+    achieved = head["algorithmic_bytes"] / (head["cold_us_mean"] * 1e-6) / 1e9
+    traffic = load_traffic(args.workload)
+    roofline = {
+        "bound": "hbm",
+        "achieved": achieved,
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": achieved / HBM_PEAK_GBPS,
+        "traffic": traffic,
+        "kernel": "mla decode call (stage-1 kernel + combine kernel when the plan has splits)",
+        "bytes_per_launch": head["algorithmic_bytes"],
+        "timing": "HIP events on the launch stream, cold cache, mean over steps",
+    }
+    cpu = None if args.no_cpu_baseline else cpu_baseline(case, args.cpu_seconds)
+    line = {
+        "metric": "us/call and effective KV HBM GB/s (% of peak), MLA decode bs x kv grid",
+        "value": head["cold_us_median"],
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["cold_us_median"] / 1e3,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": syn.KV_NAMES[case.kv_dtype] + "-kv/bf16-q/fp32-acc",
+        "data": "synthetic (seeded N(0,1) q and cache rows, quantised per format)",
+        "config": {"workload": args.workload, "batch": head["batch"], "kv_len": head["kv_len"],
+                   "kv_format": head["kv_format"], "heads": 16, "qk_dim": 576, "v_dim": 512, "page_size": 1,
+                   "plan": head["plan"]},
+        "effective_kv_GBps": head["effective_kv_GBps"],
+        "pct_hbm_peak_kv": head["pct_hbm_peak_kv"],
+        "warm_us": head["warm_us"],
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "grid": results,
+        "kernel_source_hash": source_hash(),
+        "host": platform.node(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

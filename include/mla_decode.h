@@ -1,0 +1,161 @@
+/*
+ * mla_decode.h -- C ABI of the MI355X (gfx950) single-token MLA decode library.
+ *
+ * The operation (amd-mixed-mla pages; submission 593653, "Slow fallback"
+ * `_bmm_reference`, and its module constants): for every sequence b and each
+ * of the 16 query heads h,
+ *
+ *     s_j      = sm_scale * sum_{d<576} q[b,h,d] * x_j[d]
+ *     out[b,h] = sum_j softmax_j(s) * x_j[0:512]
+ *     lse[b,h] = log(sum_j exp(s_j))                  (natural log)
+ *
+ * where x_j = dequant(kv[kv_indices[kv_indptr[b] + j]]) for
+ * j < kv_indptr[b+1] - kv_indptr[b]. One latent KV head is shared by all 16
+ * query heads; the score dimension is 576 (512 no-RoPE + 64 RoPE) and V is
+ * the first 512 columns of the same cache row; one query token per sequence;
+ * page size 1. Dequantisation of the cache formats:
+ *   - bf16: the value itself.
+ *   - fp8 e4m3fn with one per-tensor fp32 scale: code value * scale
+ *     (submission 754939, `quantize_fp8`).
+ *   - MXFP4: e2m1 nibble value * 2^(e8m0 - 127), one e8m0 scale per 32
+ *     consecutive elements, even element in the low nibble (submission
+ *     754939, `_dq4` and the V loop of `mla_s1`).
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are caller-owned device memory; the library never
+ *     allocates, frees or synchronises. Work is enqueued on `stream` (a
+ *     hipStream_t passed as void*, NULL = the null stream); returning means
+ *     "launched". Calls that share a workspace must be ordered on one stream.
+ *   - Errors are returned as negative status codes (no exceptions, nothing
+ *     printed). Arguments are validated on the host before any launch; on an
+ *     error nothing is launched and the outputs are untouched.
+ *   - Thread-safe and reentrant: no per-call global state.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Fixed shape of the operation. */
+#define MLA_NUM_HEADS 16
+#define MLA_QK_DIM 576
+#define MLA_V_DIM 512
+#define MLA_ROPE_DIM 64
+#define MLA_MX_BLOCK 32
+#define MLA_MX_SCALES_PER_ROW 18 /* 576 / 32 */
+
+/* KV cache formats. */
+#define MLA_KV_BF16 0     /* kv: bf16 [rows, 576]; kv_scales: NULL                   */
+#define MLA_KV_FP8_E4M3 1 /* kv: uint8 e4m3fn [rows, 576]; kv_scales: device fp32 [1] */
+#define MLA_KV_MXFP4 2    /* kv: uint8 [rows, 288] (2 e2m1 per byte, even element in the
+                             low nibble); kv_scales: device uint8 e8m0 [rows, 18]       */
+
+/* Status codes. */
+#define MLA_OK 0
+#define MLA_ERR_INVALID_ARG (-1)       /* null required pointer, negative size, bad format,
+                                          misaligned pointer, total_kv out of range */
+#define MLA_ERR_UNSUPPORTED (-2)       /* current device is not gfx950 */
+#define MLA_ERR_WORKSPACE_TOO_SMALL (-3)
+#define MLA_ERR_HIP (-4)               /* a HIP runtime call or kernel launch failed */
+
+/* Flags (bit field). Zero selects the built-in heuristic. */
+#define MLA_FLAG_FORCE_SPLIT 0x1       /* split-K grid: (splits x batch) workgroups      */
+#define MLA_FLAG_FORCE_PERSISTENT 0x2  /* fixed grid, equal token shares over all batches */
+#define MLA_FLAG_SPLITS_SHIFT 8        /* bits 8..15: split count for split-K (1..255)   */
+#define MLA_FLAG_GRID_SHIFT 16         /* bits 16..27: workgroups for persistent (1..4095)*/
+
+/* The launch plan the library would use (host-only, deterministic). */
+typedef struct mla_plan_info {
+    int mode;               /* 0 = split-K, 1 = persistent                              */
+    int num_splits;         /* split-K: splits per sequence; persistent: 0              */
+    int grid;               /* stage-1 workgroups                                       */
+    int num_partials;       /* partial (output, lse) slots held in the workspace        */
+    int combine;            /* 1 when a stage-2 combine launch follows stage 1          */
+    int reserved;
+    size_t workspace_bytes; /* bytes of workspace this plan needs (0 when none)          */
+} mla_plan_info;
+
+/*
+ * mla_decode_plan: fill `plan` with the launch plan for a call with these
+ * sizes. Pure host function (no device query, no HIP call).
+ *   batch     number of sequences (>= 0)
+ *   total_kv  kv_indptr[batch], host copy (0 <= total_kv <= INT32_MAX)
+ *   kv_dtype  MLA_KV_*
+ *   flags     MLA_FLAG_* (0 = heuristic)
+ * Returns MLA_OK or MLA_ERR_INVALID_ARG.
+ * The split count / grid heuristic is this library's own occupancy rule for
+ * 256 compute units; the pages' per-shape tables (e.g. submission 754939
+ * NSPLITS_SMALL / _MED / _LARGE, submission 703488's 256-program grids) were
+ * the prior art for it.
+ */
+int mla_decode_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_info* plan);
+
+/*
+ * mla_decode_workspace_size: bytes of device workspace `mla_decode` needs for
+ * these sizes (the split partials). 0 means no workspace is needed. Pure host
+ * function. Returns 0 as well for invalid arguments (mla_decode reports them).
+ */
+size_t mla_decode_workspace_size(int batch, int64_t total_kv, int kv_dtype, int flags);
+
+/*
+ * mla_decode: the decode attention defined at the top of this file.
+ *   q          device bf16 [batch, 16, 576], contiguous, 16-byte aligned
+ *   kv         device cache rows (layout per kv_dtype above), 16-byte aligned;
+ *              every kv_indices value must be a valid row (not checked)
+ *   kv_scales  per kv_dtype above (device pointer; NULL for bf16)
+ *   kv_indptr  device int32 [batch + 1], non-decreasing, kv_indptr[0] = 0,
+ *              kv_indptr[batch] = total_kv
+ *   kv_indices device int32 [total_kv]: physical row of each logical token
+ *              (may be NULL when total_kv = 0)
+ *   out        device bf16 [batch, 16, 512], 16-byte aligned (written with RNE)
+ *   lse        device fp32 [batch, 16] or NULL to skip; natural-log
+ *              log-sum-exp of the scaled scores
+ *   batch      number of sequences; 0 is a no-op
+ *   total_kv   host copy of kv_indptr[batch] (no device read / sync needed)
+ *   kv_dtype   MLA_KV_*
+ *   sm_scale   softmax scale; <= 0 (or NaN) selects 1/sqrt(576)
+ *   workspace  device scratch of at least mla_decode_workspace_size(...) bytes,
+ *              16-byte aligned (NULL allowed when that size is 0); contents
+ *              need no initialisation and are clobbered
+ *   flags      MLA_FLAG_* (0 = heuristic)
+ *   stream     hipStream_t as void*
+ * An empty sequence (kv_indptr[b+1] == kv_indptr[b]) yields out = 0 and
+ * lse = -inf. Results are deterministic: identical inputs and plan give
+ * bitwise-identical outputs.
+ * Returns MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED,
+ * MLA_ERR_WORKSPACE_TOO_SMALL or MLA_ERR_HIP.
+ */
+int mla_decode(const void* q, const void* kv, const void* kv_scales, const int32_t* kv_indptr,
+               const int32_t* kv_indices, void* out, float* lse, int batch, int64_t total_kv,
+               int kv_dtype, float sm_scale, void* workspace, size_t workspace_bytes, int flags,
+               void* stream);
+
+/*
+ * mla_dequant_debug: decode `rows` physical cache rows to fp32 [rows, 576]
+ * through the attention kernel's own staging and decode routines (test aid
+ * for the bit-exact decoder check). For fp8 the value written is the binary32
+ * product (code value) * kv_scale[0]; for MXFP4 it is the e2m1 value times
+ * 2^(e8m0 - 127); for bf16 the value itself.
+ *   kv, kv_scales  as for mla_decode (row r of the output is physical row r)
+ *   path           0: all columns through the score-operand decode;
+ *                  1: columns 0..511 through the value-operand decode (LDS
+ *                     transpose reads), columns 512..575 as path 0
+ *   out_f32        device fp32 [rows, 576]
+ * Returns MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED or MLA_ERR_HIP.
+ */
+int mla_dequant_debug(int kv_dtype, const void* kv, const void* kv_scales, int64_t rows, int path,
+                      float* out_f32, void* stream);
+
+/* mla_status_string: static, human-readable text for a status code. */
+const char* mla_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

@@ -1,0 +1,30 @@
+"""MI355X (gfx950) single-token MLA decode.
+
+A thin Python binding over ``libmla_decode.so``, whose C ABI is declared in
+``include/mla_decode.h``. The binding only marshals torch device tensors into
+pointers and sizes; every step of the computation runs in the library's HIP
+kernels. There is no fallback: if the library is missing or fails to load,
+importing this package raises.
+"""
+from ._lib import (  # noqa: F401
+    FLAG_FORCE_PERSISTENT,
+    FLAG_FORCE_SPLIT,
+    FLAG_GRID_SHIFT,
+    FLAG_SPLITS_SHIFT,
+    KV_BF16,
+    KV_FP8_E4M3,
+    KV_MXFP4,
+    LIB_PATH,
+    NUM_HEADS,
+    QK_DIM,
+    V_DIM,
+    MlaError,
+    PlanInfo,
+    flags_for,
+    mla_decode,
+    mla_decode_plan,
+    mla_decode_workspace_size,
+    mla_dequant_debug,
+    mla_status_string,
+    prepare_decode,
+)

@@ -1,0 +1,209 @@
+"""ctypes binding for libmla_decode.so (C ABI: include/mla_decode.h).
+
+Argument marshalling only: shape / dtype / device checks that the C side
+cannot make (it only sees pointers), pointer extraction, the current HIP
+stream, and -- when the caller passes none -- a workspace tensor of the size
+the library asks for. No arithmetic of the operation happens here.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla_decode.so")
+
+NUM_HEADS, QK_DIM, V_DIM = 16, 576, 512
+KV_BF16, KV_FP8_E4M3, KV_MXFP4 = 0, 1, 2
+FLAG_FORCE_SPLIT, FLAG_FORCE_PERSISTENT = 0x1, 0x2
+FLAG_SPLITS_SHIFT, FLAG_GRID_SHIFT = 8, 16
+
+_EXPORTS = ("mla_decode", "mla_decode_plan", "mla_decode_workspace_size", "mla_dequant_debug",
+            "mla_status_string")
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {mla_status_string(status)} (status {status})")
+        self.status = status
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int), ("num_splits", ctypes.c_int), ("grid", ctypes.c_int),
+                ("num_partials", ctypes.c_int), ("combine", ctypes.c_int), ("reserved", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+@dataclass(frozen=True)
+class PlanInfo:
+    mode: int            # 0 split-K, 1 persistent
+    num_splits: int
+    grid: int
+    num_partials: int
+    combine: int
+    workspace_bytes: int
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python mla_decode_02_amd/build.py` "
+            "(hipcc, gfx950). There is no non-HIP fallback.")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name in _EXPORTS:
+        if not hasattr(lib, name):
+            raise ImportError(f"{LIB_PATH} does not export {name}")
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    lib.mla_decode.restype = i32
+    lib.mla_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, ctypes.c_float, vp, sz, i32, vp]
+    lib.mla_decode_plan.restype = i32
+    lib.mla_decode_plan.argtypes = [i32, i64, i32, i32, ctypes.POINTER(_Plan)]
+    lib.mla_decode_workspace_size.restype = sz
+    lib.mla_decode_workspace_size.argtypes = [i32, i64, i32, i32]
+    lib.mla_dequant_debug.restype = i32
+    lib.mla_dequant_debug.argtypes = [i32, vp, vp, i64, i32, vp, vp]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_status_string.argtypes = [i32]
+    return lib
+
+
+_lib = _load()
+
+
+def mla_status_string(status: int) -> str:
+    return _lib.mla_status_string(int(status)).decode()
+
+
+def flags_for(splits: int | None = None, persistent: bool | None = None, grid: int | None = None) -> int:
+    """Compose the flags word: force split-K with `splits`, or persistent with `grid` workgroups."""
+    f = 0
+    if persistent:
+        f |= FLAG_FORCE_PERSISTENT
+        if grid:
+            f |= (int(grid) & 0xFFF) << FLAG_GRID_SHIFT
+    elif splits:
+        f |= FLAG_FORCE_SPLIT | ((int(splits) & 0xFF) << FLAG_SPLITS_SHIFT)
+    return f
+
+
+def mla_decode_plan(batch: int, total_kv: int, kv_dtype: int, flags: int = 0) -> PlanInfo:
+    p = _Plan()
+    rc = _lib.mla_decode_plan(int(batch), int(total_kv), int(kv_dtype), int(flags), ctypes.byref(p))
+    if rc != 0:
+        raise MlaError(rc, "mla_decode_plan")
+    return PlanInfo(p.mode, p.num_splits, p.grid, p.num_partials, p.combine, p.workspace_bytes)
+
+
+def mla_decode_workspace_size(batch: int, total_kv: int, kv_dtype: int, flags: int = 0) -> int:
+    return int(_lib.mla_decode_workspace_size(int(batch), int(total_kv), int(kv_dtype), int(flags)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_kv(kv, kv_scales, kv_dtype):
+    _need(kv.is_cuda and kv.is_contiguous(), "kv must be a contiguous device tensor")
+    if kv_dtype == KV_BF16:
+        _need(kv.dtype == torch.bfloat16 and kv.dim() == 2 and kv.shape[1] == QK_DIM, "bf16 kv must be [rows, 576]")
+        _need(kv_scales is None, "bf16 kv takes no scales")
+    elif kv_dtype == KV_FP8_E4M3:
+        _need(kv.dtype in (torch.uint8, torch.float8_e4m3fn) and kv.dim() == 2 and kv.shape[1] == QK_DIM,
+              "fp8 kv must be uint8/float8_e4m3fn [rows, 576]")
+        _need(kv_scales is not None and kv_scales.is_cuda and kv_scales.dtype == torch.float32
+              and kv_scales.numel() >= 1, "fp8 kv needs a device fp32 scale tensor")
+    elif kv_dtype == KV_MXFP4:
+        _need(kv.dtype == torch.uint8 and kv.dim() == 2 and kv.shape[1] == QK_DIM // 2, "mxfp4 kv must be uint8 [rows, 288]")
+        _need(kv_scales is not None and kv_scales.is_cuda and kv_scales.is_contiguous()
+              and kv_scales.dtype in (torch.uint8, torch.float8_e8m0fnu)
+              and tuple(kv_scales.shape) == (kv.shape[0], QK_DIM // 32), "mxfp4 scales must be uint8 [rows, 18]")
+    else:
+        raise ValueError(f"unknown kv_dtype {kv_dtype}")
+
+
+def mla_decode(q, kv, kv_scales, kv_indptr, kv_indices, out, lse=None, *, total_kv: int, kv_dtype: int,
+               sm_scale: float = 0.0, workspace=None, flags: int = 0):
+    """Enqueue MLA decode on the current stream of q's device (see include/mla_decode.h).
+
+    q [B,16,576] bf16, kv / kv_scales per kv_dtype, kv_indptr [B+1] int32,
+    kv_indices [total_kv] int32, out [B,16,512] bf16, lse [B,16] fp32 or None.
+    total_kv is the host copy of kv_indptr[B]. Returns the workspace used.
+    """
+    B = int(kv_indptr.shape[0]) - 1
+    _need(q.is_cuda and q.dtype == torch.bfloat16 and q.is_contiguous() and tuple(q.shape) == (B, NUM_HEADS, QK_DIM),
+          "q must be contiguous bf16 [batch, 16, 576]")
+    _check_kv(kv, kv_scales, kv_dtype)
+    _need(kv_indptr.is_cuda and kv_indptr.dtype == torch.int32 and kv_indptr.is_contiguous(),
+          "kv_indptr must be a contiguous device int32 tensor")
+    _need(kv_indices.is_cuda and kv_indices.dtype == torch.int32 and kv_indices.is_contiguous()
+          and kv_indices.numel() >= total_kv, "kv_indices must be a contiguous device int32 tensor of >= total_kv")
+    _need(out.is_cuda and out.dtype == torch.bfloat16 and out.is_contiguous() and tuple(out.shape) == (B, NUM_HEADS, V_DIM),
+          "out must be contiguous bf16 [batch, 16, 512]")
+    if lse is not None:
+        _need(lse.is_cuda and lse.dtype == torch.float32 and lse.is_contiguous() and tuple(lse.shape) == (B, NUM_HEADS),
+              "lse must be contiguous fp32 [batch, 16]")
+    need = mla_decode_workspace_size(B, total_kv, kv_dtype, flags)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = _lib.mla_decode(_ptr(q), _ptr(kv), _ptr(kv_scales), _ptr(kv_indptr), _ptr(kv_indices), _ptr(out),
+                         _ptr(lse), B, int(total_kv), int(kv_dtype), float(sm_scale), _ptr(workspace), ws_bytes,
+                         int(flags), _stream(q.device))
+    if rc != 0:
+        raise MlaError(rc, "mla_decode")
+    return workspace
+
+
+def prepare_decode(q, kv, kv_scales, kv_indptr, kv_indices, out, lse=None, *, total_kv: int, kv_dtype: int,
+                   sm_scale: float = 0.0, workspace=None, flags: int = 0):
+    """Check and marshal the arguments once; return a zero-argument callable that
+    enqueues the same mla_decode call on the current stream (for serving loops and
+    timing, where per-call Python checks would dominate). The tensors must stay
+    alive and in place while the callable is used."""
+    ws = mla_decode(q, kv, kv_scales, kv_indptr, kv_indices, out, lse, total_kv=total_kv, kv_dtype=kv_dtype,
+                    sm_scale=sm_scale, workspace=workspace, flags=flags)
+    B = int(kv_indptr.shape[0]) - 1
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    args = (_ptr(q), _ptr(kv), _ptr(kv_scales), _ptr(kv_indptr), _ptr(kv_indices), _ptr(out), _ptr(lse), B,
+            int(total_kv), int(kv_dtype), float(sm_scale), _ptr(ws), ws_bytes, int(flags), _stream(q.device))
+    fn = _lib.mla_decode
+    keep = (q, kv, kv_scales, kv_indptr, kv_indices, out, lse, ws)
+
+    def call():
+        rc = fn(*args)
+        if rc != 0:
+            raise MlaError(rc, "mla_decode")
+        return keep
+
+    return call
+
+
+def mla_dequant_debug(kv, kv_scales, kv_dtype: int, path: int = 0, out=None):
+    """Decode every physical cache row to fp32 [rows, 576] with the kernels' decode routines.
+
+    path 0: score-operand decode for all columns; path 1: value-operand decode
+    (transposed LDS reads) for columns 0..511.
+    """
+    _check_kv(kv, kv_scales, kv_dtype)
+    rows = int(kv.shape[0])
+    if out is None:
+        out = torch.empty((rows, QK_DIM), dtype=torch.float32, device=kv.device)
+    _need(out.is_cuda and out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (rows, QK_DIM),
+          "out must be contiguous fp32 [rows, 576]")
+    rc = _lib.mla_dequant_debug(int(kv_dtype), _ptr(kv), _ptr(kv_scales), rows, int(path), _ptr(out),
+                                _stream(kv.device))
+    if rc != 0:
+        raise MlaError(rc, "mla_dequant_debug")
+    return out

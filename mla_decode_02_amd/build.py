@@ -1,0 +1,49 @@
+"""Build libmla_decode.so (HIP, gfx950) in-tree with hipcc.
+
+    python mla_decode_02_amd/build.py   (a script: importing the package needs the built library)
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libmla_decode.so")
+
+# Every HIP translation unit is built for gfx950 only, without packed-fp32
+# instruction selection (v_pk_{add,mul,fma}_f32).
+HIP_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the HIP kernels and the host planner and link the shared library."""
+    obj_dir = os.path.join(PKG, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    plan_o = os.path.join(obj_dir, "mla_plan.o")
+    hip_o = os.path.join(obj_dir, "mla_decode.o")
+    _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-c",
+          os.path.join(CSRC, "mla_plan.cpp"), "-o", plan_o], verbose)
+    _run(["hipcc", *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "mla_decode.hip"),
+          "-o", hip_o], verbose)
+    tmp = LIB + ".tmp"
+    _run(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, hip_o, plan_o], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-q" not in sys.argv))

@@ -1,0 +1,819 @@
+// MI355X (gfx950) single-token MLA decode: split-K / persistent stage 1, the
+// log-sum-exp combine, and a decode-check kernel, behind the C ABI declared in
+// include/mla_decode.h.
+//
+// The operation is the one on the amd-mixed-mla pages (submission 593653,
+// `_bmm_reference` and the module constants): 16 query heads share one latent
+// KV row per token; scores over 576 dims (512 no-RoPE + 64 RoPE), softmax over
+// the tokens, output over the first 512 dims of the same rows.
+//
+// Stage 1, one workgroup = 4 independent waves over one token range. A wave
+// owns 32-token steps (two 16-token tiles) of the range. Per step:
+//   1. The 32 cache rows are gathered through kv_indices straight from HBM
+//      into the wave's LDS ring with LDS-DMA loads (global_load_lds_dwordx4;
+//      MXFP4 scales with byte DMA), one step ahead of use, so no VGPRs hold
+//      data in flight. Lane (G, r) of a 16-row tile fetches bytes 64u + 16G of
+//      row r for load u, which is the MFMA A-operand layout of the scores.
+//   2. Scores S^T[16 tokens x 16 heads] = K . Q^T per tile on
+//      v_mfma_f32_16x16x32_bf16 (18 k-steps; Q^T lives in VGPRs). fp8 and
+//      MXFP4 codes are dequantised in registers with the gfx950 scaled
+//      converts; fp8 -> bf16 is exact and kv_scale is folded into the score
+//      scale and the output; e2m1 * 2^(e8m0 - 127) -> bf16 is exact.
+//   3. Online softmax in the log2 domain with lazy rescaling: the running max
+//      only moves when a score exceeds it by 2^8, so the 16x512 accumulator
+//      is rarely rescaled. The S^T accumulator is already the A-operand
+//      layout of P for the second product.
+//   4. O[16 x 512] += P . V on v_mfma_f32_16x16x32_bf16, one per 16-column
+//      block. The token-major V operand comes from LDS transpose reads
+//      (ds_read_b64_tr_b8 for fp8 / MXFP4 bytes, ds_read_b64_tr_b16 for bf16)
+//      of the same staged rows: V is the first 512 columns of K, so each row is
+//      fetched from HBM once.
+// The four waves' (max, sum, O) are merged through LDS and written either as
+// the final bf16 output + lse or as an fp32 partial (normalised O and its lse)
+// for the combine kernel (flash-decoding split partials and log-sum-exp merge:
+// submission 593653, `_flash_fp8_split_s1` / `_flash_fp8_split_s2`).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "mla_decode.h"
+#include "mla_plan.h"
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 16;                // tokens per MFMA tile
+constexpr int kStepTokens = 2 * kTile;   // tokens per wave step
+constexpr int kKSteps = kDqk / 32;       // 18 MFMA k-steps over the 576 score dims
+constexpr int kBlocks = kDv / 16;        // 32 output blocks of 16 columns per wave
+constexpr float kRescaleThresh = 8.0f;   // log2 units
+constexpr int kIdxWindow = 2048;         // tokens whose indices are staged in LDS at a time
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct Params {
+    const __bf16* q;
+    const uint8_t* kv;
+    const void* kv_scales;
+    const int32_t* indptr;
+    const int32_t* indices;
+    __bf16* out;
+    float* lse;
+    float* part_o;
+    float* part_lse;
+    int batch;
+    int nsplit;  // split-K: splits per sequence
+    int grid;    // persistent: number of workgroups
+    int total;   // kv_indptr[batch]
+    float sm_scale;
+};
+
+// ---------------------------------------------------------------------------
+// Cache formats: staging layout of one 16-row tile in LDS.
+//   codes: load u (0 <= u < kCodeLoads) is one 16-byte DMA per lane; lane
+//          (G, r) = (lane / 16, lane % 16) brings bytes 64u + 16G .. +15 of
+//          tile row r to tile + 1024u + 16 lane.
+//   MXFP4: the 32 RoPE bytes of each row (bytes 256..287) are two dword DMAs
+//          into a [16 rows][8 dwords] block at tile + 4096; the step's e8m0
+//          scales are byte DMAs into one dword per (block, token):
+//          step + 2 * kTileBytes + 4 (32 block + token).
+// ---------------------------------------------------------------------------
+template <int KV>
+struct Fmt;
+template <>
+struct Fmt<MLA_KV_BF16> {
+    static constexpr int kRowBytes = 2 * kDqk;
+    static constexpr int kCodeLoads = 18;
+    static constexpr int kTileBytes = 18 * 1024;
+    static constexpr int kScaleBytes = 0;
+    static constexpr int kRing = 1;         // steps resident per wave (LDS bound)
+    static constexpr int kOpsPerStep = 36;  // VMEM instructions issued per step
+};
+template <>
+struct Fmt<MLA_KV_FP8_E4M3> {
+    static constexpr int kRowBytes = kDqk;
+    static constexpr int kCodeLoads = 9;
+    static constexpr int kTileBytes = 9 * 1024;
+    static constexpr int kScaleBytes = 0;
+    static constexpr int kRing = 2;
+    static constexpr int kOpsPerStep = 18;
+};
+template <>
+struct Fmt<MLA_KV_MXFP4> {
+    static constexpr int kRowBytes = kDqk / 2;
+    static constexpr int kCodeLoads = 4;
+    static constexpr int kTileBytes = 4 * 1024 + 512;
+    static constexpr int kScaleBytes = 18 * kStepTokens * 4;
+    static constexpr int kRing = 3;
+    static constexpr int kOpsPerStep = 2 * (4 + 2) + 9;
+};
+
+template <int KV>
+struct Layout {
+    static constexpr int kStepBytes = 2 * Fmt<KV>::kTileBytes + Fmt<KV>::kScaleBytes;
+    static constexpr int kRingBytes = kWaves * Fmt<KV>::kRing * kStepBytes;
+    static constexpr int kPartialBytes = kWaves * kHeads * kDv * 4;
+    static constexpr int kMainBytes = kRingBytes > kPartialBytes ? kRingBytes : kPartialBytes;
+    static constexpr int kIdxOff = kMainBytes;
+    static constexpr int kStatOff = kIdxOff + kIdxWindow * 4;
+    static constexpr int kBytes = kStatOff + 2 * kWaves * kHeads * 4;
+    static_assert(kBytes <= 160 * 1024, "stage-1 LDS exceeds 160 KiB");
+};
+
+// First score dim of the eight held by lane group G in k-step ks. Q^T is
+// loaded with the same mapping, so every MFMA contracts exactly those dims.
+template <int KV>
+__device__ __forceinline__ constexpr int dbase(int ks, int G) {
+    if (KV == MLA_KV_BF16) return 32 * ks + 8 * G;
+    if (KV == MLA_KV_FP8_E4M3) return 64 * (ks >> 1) + 16 * G + 8 * (ks & 1);
+    return ks < 16 ? 128 * (ks >> 2) + 32 * G + 8 * (ks & 3) : 512 + 16 * G + 8 * (ks - 16);
+}
+
+// Output column held by lane column r in accumulator block blk.
+template <int KV>
+__device__ __forceinline__ int dcol(int blk, int r) {
+    if (KV == MLA_KV_MXFP4) return 32 * (blk >> 1) + 2 * r + (blk & 1);
+    return 16 * blk + r;
+}
+
+// Token (0..31 within a step) of k-slot j for lane group G in the P . V
+// product: slots 0-3 are tile 0's tokens 4G..4G+3, slots 4-7 tile 1's.
+__device__ __forceinline__ int tau(int G, int j) { return j < 4 ? 4 * G + j : 16 + 4 * G + (j - 4); }
+
+// LDS-DMA loads: lane L's `size` bytes from its global address g land at LDS
+// byte lds + size * L (size 16), or in the dword at lds + 4 L, zero-extended
+// (sizes 1 and 4). Issued from inline assembly so that the compiler, which
+// would otherwise drain every outstanding load before each LDS read it cannot
+// prove disjoint, leaves the ordering to the explicit waits below. m0 (the
+// LDS base operand) is restored before the statement ends.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+    uint32_t save;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(save) : "v"(g), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+    uint32_t save;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(save) : "v"(g), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void dma1(const void* g, uint32_t lds) {
+    uint32_t save;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_ubyte %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(save) : "v"(g), "s"(lds) : "memory");
+}
+// Wave-uniform 32-bit LDS address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)p);
+}
+
+// Wait until at most N vector-memory instructions of this wave are in flight.
+// Also a compiler barrier for memory: the compiler does not order LDS reads
+// after the LDS-DMA writes by itself.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// Gather the step starting at window token tok0 into `step`. Tokens at or
+// beyond n re-read the last valid row (always in bounds).
+template <int KV>
+__device__ __forceinline__ void issue_step(const Params& P, const int32_t* idx, int tok0, int n, uint8_t* step,
+                                           int lane) {
+    constexpr int RB = Fmt<KV>::kRowBytes;
+    const int G = lane >> 4, r = lane & 15;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int64_t row = idx[min(tok0 + kTile * t + r, n - 1)];
+        const uint8_t* src = P.kv + row * RB + 16 * G;
+        uint8_t* tile = step + t * Fmt<KV>::kTileBytes;
+#pragma unroll
+        for (int u = 0; u < Fmt<KV>::kCodeLoads; ++u) dma16(src + 64 * u, lds_addr(tile + 1024 * u));
+        if constexpr (KV == MLA_KV_MXFP4) {
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                const int s = 64 * v + lane;  // (row s / 8, dword s % 8) of the RoPE block
+                const int64_t row2 = idx[min(tok0 + kTile * t + (s >> 3), n - 1)];
+                dma4(P.kv + row2 * RB + 256 + 4 * (s & 7), lds_addr(tile + 4096 + 256 * v));
+            }
+        }
+    }
+    if constexpr (KV == MLA_KV_MXFP4) {
+        const uint8_t* sc = reinterpret_cast<const uint8_t*>(P.kv_scales);
+        const int64_t row3 = idx[min(tok0 + (lane & 31), n - 1)];
+#pragma unroll
+        for (int v = 0; v < 9; ++v) {  // dword 64 v + lane = (block 2v + lane / 32, token lane % 32)
+            dma1(sc + row3 * MLA_MX_SCALES_PER_ROW + 2 * v + (lane >> 5),
+                 lds_addr(step + 2 * Fmt<KV>::kTileBytes + 256 * v));
+        }
+    }
+}
+
+// e8m0 code -> fp32 scale operand of the scaled converts (the code is the
+// exponent field: 2^(code - 127)).
+__device__ __forceinline__ float e8m0_scale(uint32_t code) { return __uint_as_float(code << 23); }
+
+__device__ __forceinline__ bf16x8 join(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
+    bf16x8 o;
+    o[0] = a[0]; o[1] = a[1]; o[2] = b[0]; o[3] = b[1];
+    o[4] = c[0]; o[5] = c[1]; o[6] = d[0]; o[7] = d[1];
+    return o;
+}
+
+// Eight e4m3fn codes (element k in byte k of lo:hi) -> bf16, exactly.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+    return join(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false),
+                __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true),
+                __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false),
+                __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+}
+
+// Eight e2m1 codes of one block (element 2k in the low nibble of byte k) -> bf16.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t dw, float scale) {
+    return join(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, scale, 0),
+                __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, scale, 1),
+                __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, scale, 2),
+                __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, scale, 3));
+}
+
+// Score operand: k-step ks of tile t (row r = lane % 16, dims dbase(ks, G)..+7).
+template <int KV>
+__device__ __forceinline__ bf16x8 qk_operand(const uint8_t* step, int t, int ks, int lane) {
+    const uint8_t* tile = step + t * Fmt<KV>::kTileBytes;
+    if constexpr (KV == MLA_KV_BF16) {
+        return *reinterpret_cast<const bf16x8*>(tile + 1024 * ks + 16 * lane);
+    } else if constexpr (KV == MLA_KV_FP8_E4M3) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(tile + 1024 * (ks >> 1) + 16 * lane);
+        return (ks & 1) ? fp8x8_to_bf16(w[2], w[3]) : fp8x8_to_bf16(w[0], w[1]);
+    } else {
+        const int G = lane >> 4, r = lane & 15;
+        const uint32_t* scl = reinterpret_cast<const uint32_t*>(step + 2 * Fmt<KV>::kTileBytes);
+        uint32_t dw, blk;
+        if (ks < 16) {
+            dw = *reinterpret_cast<const uint32_t*>(tile + 1024 * (ks >> 2) + 16 * lane + 4 * (ks & 3));
+            blk = 4 * (ks >> 2) + G;
+        } else {
+            dw = *reinterpret_cast<const uint32_t*>(tile + 4096 + 4 * (8 * r + 2 * G + (ks - 16)));
+            blk = 16 + (G >> 1);
+        }
+        return fp4x8_to_bf16(dw, e8m0_scale(scl[32 * blk + kTile * t + r]));
+    }
+}
+
+// Value operand of 16-column block c (bf16 / fp8): lane (G, n) receives column
+// 16c + n of the eight tokens tau(G, 0..7).
+template <int KV>
+__device__ __forceinline__ bf16x8 pv_operand(const uint8_t* step, int c, int lane) {
+    const int G = lane >> 4, j = lane & 15;
+    if constexpr (KV == MLA_KV_FP8_E4M3) {
+        // Row i of the transposed 8x16-byte block is token tau(G, i); lanes
+        // 2i and 2i+1 supply its bytes 0-7 and 8-15.
+        const int tk = tau(G, j >> 1);
+        const uint8_t* a = step + (tk >> 4) * Fmt<KV>::kTileBytes + 1024 * (c >> 2) +
+                           16 * (16 * (c & 3) + (tk & 15)) + 8 * (j & 1);
+        const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)a);
+        return fp8x8_to_bf16((uint32_t)w[0], (uint32_t)w[1]);
+    } else {
+        // Row i of each transposed 4x16-element block is token tau(G, i) (first
+        // read) or tau(G, 4 + i) (second read); lanes 4i..4i+3 supply its 32 bytes.
+        const int i = j >> 2, q = j & 3;
+        const int g0 = 2 * (c & 1) + (q >> 1);
+        const int t0 = tau(G, i), t1 = tau(G, 4 + i);
+        const uint8_t* base = step + 1024 * (c >> 1) + 16 * (16 * g0) + 8 * (q & 1);
+        const uint8_t* a0 = base + (t0 >> 4) * Fmt<KV>::kTileBytes + 16 * (t0 & 15);
+        const uint8_t* a1 = base + (t1 >> 4) * Fmt<KV>::kTileBytes + 16 * (t1 & 15);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a1);
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+}
+
+// Byte i of dw (two e2m1 codes of one token) scaled by 2^(sc[i] - 127) -> bf16x2.
+__device__ __forceinline__ void cvt_fp4_bytes(uint32_t dw, u32x4 sc, uint32_t* c) {
+    c[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, e8m0_scale(sc[0]), 0));
+    c[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, e8m0_scale(sc[1]), 1));
+    c[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, e8m0_scale(sc[2]), 2));
+    c[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, e8m0_scale(sc[3]), 3));
+}
+
+// Value operands of MXFP4 block b (32 columns): lane (G, n) receives byte n of
+// the block for tokens tau(G, 0..7), i.e. columns 32b + 2n (even) and
+// 32b + 2n + 1 (odd), each token scaled by its own e8m0 code.
+__device__ __forceinline__ void pv_operand_fp4(const uint8_t* step, int b, int lane, bf16x8& even, bf16x8& odd) {
+    constexpr int TB = Fmt<MLA_KV_MXFP4>::kTileBytes;
+    const int G = lane >> 4, j = lane & 15;
+    const int tk = tau(G, j >> 1);
+    const uint8_t* a = step + (tk >> 4) * TB + 1024 * (b >> 2) + 16 * (16 * (b & 3) + (tk & 15)) + 8 * (j & 1);
+    const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)a);
+    const u32x4* scl = reinterpret_cast<const u32x4*>(step + 2 * TB + 4 * (32 * b));
+    const u32x4 s0 = scl[G], s1 = scl[4 + G];  // tokens 4G..4G+3 and 16+4G..16+4G+3
+    uint32_t c[8];
+    cvt_fp4_bytes((uint32_t)w[0], s0, c);
+    cvt_fp4_bytes((uint32_t)w[1], s1, c + 4);
+    u32x4 e, o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        e[k] = __builtin_amdgcn_perm(c[2 * k + 1], c[2 * k], 0x05040100u);  // low halves
+        o[k] = __builtin_amdgcn_perm(c[2 * k + 1], c[2 * k], 0x07060302u);  // high halves
+    }
+    even = __builtin_bit_cast(bf16x8, e);
+    odd = __builtin_bit_cast(bf16x8, o);
+}
+
+// 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+struct WaveAcc {
+    f32x4 o[kBlocks];  // o[blk][i]: head 4G+i, column dcol(blk, r)
+    float m;           // running max of head r (log2 units), same in its 4 lanes
+    float l;           // this lane's share of head r's softmax denominator
+};
+
+template <int KV>
+__device__ __forceinline__ void compute_step(const uint8_t* step, const bf16x8 (&qB)[kKSteps], float qk_scale,
+                                             int nvalid, int lane, WaveAcc& a) {
+    const int G = lane >> 4;
+    // Scores of both tiles: S^T[token 4G+i (+16)][head r] in lane (G, r).
+    f32x4 s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        f32x4 e0 = {0.f, 0.f, 0.f, 0.f}, e1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ks += 2) {
+            e0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qk_operand<KV>(step, t, ks, lane), qB[ks], e0, 0, 0, 0);
+            e1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qk_operand<KV>(step, t, ks + 1, lane), qB[ks + 1], e1, 0, 0, 0);
+        }
+        s[t] = e0 + e1;
+    }
+    float x[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        x[j] = (tau(G, j) < nvalid) ? s[j >> 2][j & 3] * qk_scale : -INFINITY;
+        mx = fmaxf(mx, x[j]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(a.m, mx);
+    if (__any(m_new > a.m + kRescaleThresh)) {
+        const float alpha = (a.m == -INFINITY) ? 0.f : fast_exp2(a.m - m_new);
+        a.m = m_new;
+        a.l *= alpha;
+        float al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * G + i);
+#pragma unroll
+        for (int blk = 0; blk < kBlocks; ++blk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a.o[blk][i] *= al[i];
+    }
+    float p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = fast_exp2(x[j] - a.m);
+    a.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    bf16x8 pa;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pa[j] = (__bf16)p[j];
+
+    if constexpr (KV == MLA_KV_MXFP4) {
+#pragma unroll
+        for (int b = 0; b < kBlocks / 2; ++b) {
+            bf16x8 ev, od;
+            pv_operand_fp4(step, b, lane, ev, od);
+            a.o[2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, ev, a.o[2 * b], 0, 0, 0);
+            a.o[2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, od, a.o[2 * b + 1], 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < kBlocks; ++c)
+            a.o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, pv_operand<KV>(step, c, lane), a.o[c], 0, 0, 0);
+    }
+}
+
+// Wait for the step issued `ahead` steps before the most recently issued one.
+template <int KV>
+__device__ __forceinline__ void wait_step(int ahead) {
+    constexpr int N = Fmt<KV>::kOpsPerStep;
+    if (ahead <= 0) wait_vmcnt<0>();
+    else if (ahead == 1) wait_vmcnt<N>();
+    else wait_vmcnt<2 * N>();
+}
+
+// Attend tokens [t0, t1) of sequence b with the whole workgroup and write the
+// result: final bf16 output + lse when `final`, else partial slot `slot`.
+template <int KV>
+__device__ void run_wg(const Params& P, uint8_t* smem, int b, int t0, int t1, bool final, int slot) {
+    using L = Layout<KV>;
+    constexpr int D = Fmt<KV>::kRing - 1;  // steps in flight ahead of the one computed
+    static_assert(D <= 2, "wait_step handles at most two steps ahead");
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, G = lane >> 4, r = lane & 15;
+    int32_t* idx = reinterpret_cast<int32_t*>(smem + L::kIdxOff);
+    float* sm_m = reinterpret_cast<float*>(smem + L::kStatOff);
+    float* sm_l = sm_m + kWaves * kHeads;
+    float* sm_o = reinterpret_cast<float*>(smem);  // epilogue: [wave][head][512]
+    uint8_t* ring = smem + wave * Fmt<KV>::kRing * L::kStepBytes;
+
+    float kv_scale = 1.0f;
+    if constexpr (KV == MLA_KV_FP8_E4M3) kv_scale = *reinterpret_cast<const float*>(P.kv_scales);
+    const float qk_scale = P.sm_scale * kv_scale * kLog2e;
+
+    bf16x8 qB[kKSteps];
+    {
+        const __bf16* qrow = P.q + ((int64_t)b * kHeads + r) * kDqk;
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks) qB[ks] = *reinterpret_cast<const bf16x8*>(qrow + dbase<KV>(ks, G));
+        // Consume Q^T here so that the compiler's wait for these loads is placed
+        // before the token loop, not inside it.
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" ::"v"(qB[ks]));
+    }
+
+    WaveAcc a;
+#pragma unroll
+    for (int blk = 0; blk < kBlocks; ++blk) a.o[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+    a.m = -INFINITY;
+    a.l = 0.f;
+
+    for (int w0 = t0; w0 < t1; w0 += kIdxWindow) {
+        const int n = min(kIdxWindow, t1 - w0);
+        __syncthreads();  // every wave is done with the previous window / previous range
+        {
+            constexpr int kPer = kIdxWindow / kThreads;
+            int32_t v[kPer];
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) v[k] = (tid + k * kThreads < n) ? P.indices[w0 + tid + k * kThreads] : 0;
+#pragma unroll
+            for (int k = 0; k < kPer; ++k)
+                if (tid + k * kThreads < n) idx[tid + k * kThreads] = v[k];
+        }
+        __syncthreads();
+        const int nsteps = (n + kStepTokens - 1) / kStepTokens;
+        const int nj = nsteps > wave ? (nsteps - wave + kWaves - 1) / kWaves : 0;  // steps wave + j*kWaves
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            if (d < nj) issue_step<KV>(P, idx, (wave + d * kWaves) * kStepTokens, n, ring + d * L::kStepBytes, lane);
+        for (int j = 0; j < nj; ++j) {
+            if (j + D < nj)
+                issue_step<KV>(P, idx, (wave + (j + D) * kWaves) * kStepTokens, n,
+                               ring + ((j + D) % Fmt<KV>::kRing) * L::kStepBytes, lane);
+            wait_step<KV>(min(D, nj - 1 - j));
+            const int tok0 = (wave + j * kWaves) * kStepTokens;
+            compute_step<KV>(ring + (j % Fmt<KV>::kRing) * L::kStepBytes, qB, qk_scale, n - tok0, lane, a);
+        }
+    }
+
+    // ---- merge the four waves: M = max_w m_w, O = sum_w 2^(m_w - M) O_w ----
+    float lt = a.l;
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    __syncthreads();  // all waves done with the ring (aliased by sm_o)
+    if (G == 0) {
+        sm_m[wave * kHeads + r] = a.m;
+        sm_l[wave * kHeads + r] = lt;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int h = 4 * G + i;
+        float M = sm_m[h];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w * kHeads + h]);
+        const float mw = sm_m[wave * kHeads + h];
+        const float c = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+        float* dst = sm_o + (wave * kHeads + h) * kDv;
+#pragma unroll
+        for (int blk = 0; blk < kBlocks; ++blk) dst[dcol<KV>(blk, r)] = a.o[blk][i] * c;
+    }
+    __syncthreads();
+    {
+        const int h = tid >> 4, dc = (tid & 15) * 32;
+        float M = sm_m[h];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w * kHeads + h]);
+        float Lsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float mw = sm_m[w * kHeads + h];
+            Lsum += (mw == -INFINITY) ? 0.f : fast_exp2(mw - M) * sm_l[w * kHeads + h];
+        }
+        const float inv = (Lsum > 0.f) ? kv_scale / Lsum : 0.f;
+        const float lse_nat = (Lsum > 0.f) ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
+        float v[32];
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+            const int d = dc + e;
+            v[e] = (((sm_o[(0 * kHeads + h) * kDv + d] + sm_o[(1 * kHeads + h) * kDv + d]) +
+                     sm_o[(2 * kHeads + h) * kDv + d]) + sm_o[(3 * kHeads + h) * kDv + d]) * inv;
+        }
+        if (final) {
+            __bf16* o = P.out + ((int64_t)b * kHeads + h) * kDv + dc;
+#pragma unroll
+            for (int e = 0; e < 32; e += 8) {
+                bf16x8 pk;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) pk[k] = (__bf16)v[e + k];
+                *reinterpret_cast<bf16x8*>(o + e) = pk;
+            }
+            if ((tid & 15) == 0 && P.lse) P.lse[(int64_t)b * kHeads + h] = lse_nat;
+        } else {
+            float* o = P.part_o + ((int64_t)slot * kHeads + h) * kDv + dc;
+#pragma unroll
+            for (int e = 0; e < 32; e += 4) *reinterpret_cast<f32x4*>(o + e) = f32x4{v[e], v[e + 1], v[e + 2], v[e + 3]};
+            if ((tid & 15) == 0) P.part_lse[(int64_t)slot * kHeads + h] = lse_nat;
+        }
+    }
+}
+
+template <int KV>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void split_kernel(Params P) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Layout<KV>::kBytes];
+    const int b = blockIdx.x / P.nsplit, s = blockIdx.x % P.nsplit;
+    const int start = P.indptr[b], end = P.indptr[b + 1];
+    const int L = end - start;
+    const int chunk = ((L + P.nsplit - 1) / P.nsplit + kStepTokens - 1) / kStepTokens * kStepTokens;
+    const int t0 = min(end, start + s * chunk);
+    const int t1 = min(end, t0 + chunk);
+    run_wg<KV>(P, smem, b, t0, t1, P.nsplit == 1, b * P.nsplit + s);
+}
+
+// Largest p whose share [floor(p T / G), floor((p+1) T / G)) starts at or before t.
+__device__ __forceinline__ int share_of(int64_t t, int64_t T, int64_t G) { return (int)(((t + 1) * G - 1) / T); }
+__device__ __forceinline__ int64_t share_start(int64_t p, int64_t T, int64_t G) { return p * T / G; }
+
+template <int KV>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void persistent_kernel(Params P) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Layout<KV>::kBytes];
+    const int64_t T = P.total, Gn = P.grid;
+    const int p = blockIdx.x;
+    const int64_t g0 = share_start(p, T, Gn), g1 = share_start(p + 1, T, Gn);
+    if (g0 >= g1) return;
+    // first sequence b with indptr[b] <= g0 < indptr[b+1]
+    int lo = 0, hi = P.batch - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (P.indptr[mid] <= g0) lo = mid; else hi = mid - 1;
+    }
+    for (int b = lo; b < P.batch; ++b) {
+        const int s = P.indptr[b], e = P.indptr[b + 1];
+        if (s >= g1) break;
+        const int t0 = (int)max<int64_t>(g0, s), t1 = (int)min<int64_t>(g1, e);
+        if (t0 >= t1) continue;
+        const bool whole = (s >= g0) && (e <= g1);
+        __syncthreads();  // the previous sequence's epilogue has finished reading LDS
+        run_wg<KV>(P, smem, b, t0, t1, whole, p + b);
+    }
+}
+
+// Stage 2: out[b,h] = sum_s w_s O_s / sum_s w_s, w_s = exp(lse_s - max lse),
+// lse = max + ln sum w_s; empty partials (lse = -inf) carry no weight.
+// (Submission 703488, `_reduce_splitk_parallel_*`.)
+struct CombineParams {
+    const float* part_o;
+    const float* part_lse;
+    const int32_t* indptr;
+    __bf16* out;
+    float* lse;
+    int batch;
+    int mode;    // 0 split-K, 1 persistent
+    int nsplit;  // split-K
+    int grid;    // persistent
+    int total;
+};
+
+__global__ __launch_bounds__(128) void combine_kernel(CombineParams C) {
+    const int h = blockIdx.x & 15, b = blockIdx.x >> 4;
+    const int d = threadIdx.x * 4;
+    int first, last, base;
+    if (C.mode == 0) {
+        first = 0;
+        last = C.nsplit - 1;
+        base = b * C.nsplit;
+    } else {
+        const int s = C.indptr[b], e = C.indptr[b + 1];
+        if (e > s) {
+            first = share_of(s, C.total, C.grid);
+            last = share_of(e - 1, C.total, C.grid);
+            if (first == last) return;  // one workgroup held the whole sequence and wrote it
+        } else {
+            first = 0;
+            last = -1;
+        }
+        base = b;  // slot of workgroup p for sequence b is p + b
+    }
+    float M = -INFINITY;
+    for (int p = first; p <= last; ++p) {
+        if (C.mode == 1 && share_start(p, C.total, C.grid) == share_start(p + 1, C.total, C.grid)) continue;
+        M = fmaxf(M, C.part_lse[(int64_t)(base + p) * kHeads + h]);
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float W = 0.f;
+    if (M != -INFINITY) {
+        for (int p = first; p <= last; ++p) {
+            if (C.mode == 1 && share_start(p, C.total, C.grid) == share_start(p + 1, C.total, C.grid)) continue;
+            const int64_t slot = base + p;
+            const float l = C.part_lse[slot * kHeads + h];
+            if (l == -INFINITY) continue;
+            const float w = __expf(l - M);
+            W += w;
+            const f32x4 o = *reinterpret_cast<const f32x4*>(C.part_o + (slot * kHeads + h) * kDv + d);
+            acc += w * o;
+        }
+    }
+    const float inv = (W > 0.f) ? 1.f / W : 0.f;
+    bf16x4 pk;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(acc[e] * inv);
+    *reinterpret_cast<bf16x4*>(C.out + ((int64_t)b * kHeads + h) * kDv + d) = pk;
+    if (threadIdx.x == 0 && C.lse) C.lse[(int64_t)b * kHeads + h] = (W > 0.f) ? M + logf(W) : -INFINITY;
+}
+
+// Decode check: rows -> fp32 through the stage-1 staging (issue_step) and the
+// two decode routines of the attention kernel. path 0: every column through
+// the score operand (qk_operand); path 1: columns 0..511 through the value
+// operand (pv_operand / pv_operand_fp4), columns 512..575 through path 0.
+// One wave per 32 rows; fp8 values are multiplied by kv_scale in fp32.
+template <int KV>
+__global__ __launch_bounds__(64) void dequant_kernel(Params P, int64_t rows, int path, float* out) {
+    __shared__ __attribute__((aligned(16))) uint8_t step[Layout<KV>::kStepBytes];
+    __shared__ int32_t idx[kStepTokens];
+    const int lane = threadIdx.x, G = lane >> 4, r = lane & 15;
+    const int64_t row0 = (int64_t)blockIdx.x * kStepTokens;
+    const int n = (int)min<int64_t>(kStepTokens, rows - row0);
+    if (lane < kStepTokens) idx[lane] = (int32_t)(row0 + min(lane, n - 1));
+    __syncthreads();
+    issue_step<KV>(P, idx, 0, n, step, lane);
+    wait_vmcnt<0>();
+    __syncthreads();
+    float mul = 1.0f;
+    if constexpr (KV == MLA_KV_FP8_E4M3) mul = *reinterpret_cast<const float*>(P.kv_scales);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int64_t row = row0 + kTile * t + r;
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks) {
+            const int d0 = dbase<KV>(ks, G);
+            if (path == 1 && d0 < kDv) continue;
+            const bf16x8 v = qk_operand<KV>(step, t, ks, lane);
+            if (kTile * t + r < n)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) out[row * kDqk + d0 + e] = (float)v[e] * mul;
+        }
+    }
+    if (path == 1) {
+        // lane (G, n) holds column n of block c for tokens tau(G, 0..7)
+#pragma unroll
+        for (int c = 0; c < (KV == MLA_KV_MXFP4 ? kBlocks / 2 : kBlocks); ++c) {
+            bf16x8 v0, v1;
+            if constexpr (KV == MLA_KV_MXFP4) pv_operand_fp4(step, c, lane, v0, v1);
+            else v0 = pv_operand<KV>(step, c, lane);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int tk = tau(G, e);
+                if (tk >= n) continue;
+                float* o = out + (row0 + tk) * kDqk;
+                if constexpr (KV == MLA_KV_MXFP4) {
+                    o[32 * c + 2 * r] = (float)v0[e];
+                    o[32 * c + 2 * r + 1] = (float)v1[e];
+                } else {
+                    o[16 * c + r] = (float)v0[e] * mul;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+static bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+static int check_device() {
+    static std::atomic<int> cache[64];  // 0 unknown, 1 gfx950, 2 other
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+    if (dev >= 0 && dev < 64) {
+        int c = cache[dev].load(std::memory_order_relaxed);
+        if (c == 1) return MLA_OK;
+        if (c == 2) return MLA_ERR_UNSUPPORTED;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MLA_ERR_HIP;
+    const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev >= 0 && dev < 64) cache[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? MLA_OK : MLA_ERR_UNSUPPORTED;
+}
+
+template <int KV>
+static int launch(const mla_plan_info& plan, const Params& P, hipStream_t stream) {
+    if (plan.mode == 0)
+        hipLaunchKernelGGL(split_kernel<KV>, dim3(plan.grid), dim3(kThreads), 0, stream, P);
+    else
+        hipLaunchKernelGGL(persistent_kernel<KV>, dim3(plan.grid), dim3(kThreads), 0, stream, P);
+    if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+    if (plan.combine) {
+        CombineParams C;
+        C.part_o = P.part_o;
+        C.part_lse = P.part_lse;
+        C.indptr = P.indptr;
+        C.out = P.out;
+        C.lse = P.lse;
+        C.batch = P.batch;
+        C.mode = plan.mode;
+        C.nsplit = plan.num_splits;
+        C.grid = plan.grid;
+        C.total = P.total;
+        hipLaunchKernelGGL(combine_kernel, dim3(kHeads * P.batch), dim3(128), 0, stream, C);
+        if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+    }
+    return MLA_OK;
+}
+
+}  // namespace mla
+
+extern "C" int mla_decode(const void* q, const void* kv, const void* kv_scales, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, void* out, float* lse, int batch, int64_t total_kv,
+                          int kv_dtype, float sm_scale, void* workspace, size_t workspace_bytes, int flags,
+                          void* stream) {
+    using namespace mla;
+    mla_plan_info plan;
+    int rc = make_plan(batch, total_kv, kv_dtype, flags, &plan);
+    if (rc != MLA_OK) return rc;
+    if (batch == 0) return MLA_OK;
+    if (!q || !kv || !kv_indptr || !out) return MLA_ERR_INVALID_ARG;
+    if (total_kv > 0 && !kv_indices) return MLA_ERR_INVALID_ARG;
+    if (kv_dtype != MLA_KV_BF16 && !kv_scales) return MLA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 16) || !aligned(kv_indptr, 4) ||
+        (kv_indices && !aligned(kv_indices, 4)) || (lse && !aligned(lse, 4)) ||
+        (kv_dtype == MLA_KV_FP8_E4M3 && !aligned(kv_scales, 4)))
+        return MLA_ERR_INVALID_ARG;
+    if (plan.workspace_bytes > 0) {
+        if (!workspace || workspace_bytes < plan.workspace_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
+        if (!aligned(workspace, 16)) return MLA_ERR_INVALID_ARG;
+    }
+    rc = check_device();
+    if (rc != MLA_OK) return rc;
+
+    Params P;
+    P.q = reinterpret_cast<const __bf16*>(q);
+    P.kv = reinterpret_cast<const uint8_t*>(kv);
+    P.kv_scales = kv_scales;
+    P.indptr = kv_indptr;
+    P.indices = kv_indices;
+    P.out = reinterpret_cast<__bf16*>(out);
+    P.lse = lse;
+    P.part_o = reinterpret_cast<float*>(workspace);
+    P.part_lse = plan.num_partials ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                                             partial_lse_offset(plan.num_partials))
+                                   : nullptr;
+    P.batch = batch;
+    P.nsplit = plan.num_splits;
+    P.grid = plan.grid;
+    P.total = (int)total_kv;
+    P.sm_scale = (sm_scale > 0.f) ? sm_scale : 1.0f / 24.0f;  // NaN compares false -> default
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    switch (kv_dtype) {
+        case MLA_KV_BF16: return launch<MLA_KV_BF16>(plan, P, s);
+        case MLA_KV_FP8_E4M3: return launch<MLA_KV_FP8_E4M3>(plan, P, s);
+        default: return launch<MLA_KV_MXFP4>(plan, P, s);
+    }
+}
+
+extern "C" int mla_dequant_debug(int kv_dtype, const void* kv, const void* kv_scales, int64_t rows, int path,
+                                 float* out_f32, void* stream) {
+    using namespace mla;
+    if (kv_dtype < MLA_KV_BF16 || kv_dtype > MLA_KV_MXFP4 || rows < 0 || rows > INT32_MAX || path < 0 || path > 1)
+        return MLA_ERR_INVALID_ARG;
+    if (rows == 0) return MLA_OK;
+    if (!kv || !out_f32 || (kv_dtype != MLA_KV_BF16 && !kv_scales)) return MLA_ERR_INVALID_ARG;
+    if (!aligned(kv, 16) || !aligned(out_f32, 4)) return MLA_ERR_INVALID_ARG;
+    int rc = check_device();
+    if (rc != MLA_OK) return rc;
+    Params P;
+    memset(&P, 0, sizeof P);
+    P.kv = reinterpret_cast<const uint8_t*>(kv);
+    P.kv_scales = kv_scales;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)((rows + kStepTokens - 1) / kStepTokens));
+    switch (kv_dtype) {
+        case MLA_KV_BF16: hipLaunchKernelGGL(dequant_kernel<MLA_KV_BF16>, grid, dim3(64), 0, s, P, rows, path, out_f32); break;
+        case MLA_KV_FP8_E4M3: hipLaunchKernelGGL(dequant_kernel<MLA_KV_FP8_E4M3>, grid, dim3(64), 0, s, P, rows, path, out_f32); break;
+        default: hipLaunchKernelGGL(dequant_kernel<MLA_KV_MXFP4>, grid, dim3(64), 0, s, P, rows, path, out_f32); break;
+    }
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}

@@ -1,0 +1,139 @@
+// Launch planning for MLA decode: split count / grid size and workspace layout.
+// Pure host code with no HIP dependency, so it is testable without a GPU.
+//
+// Two grid shapes are planned:
+//   split-K     (splits x batch) workgroups; split s of sequence b covers
+//               tokens [s*chunk, min(L_b, (s+1)*chunk)), chunk = ceil(L_b /
+//               splits) rounded up to the 16-token wave step. One partial
+//               slot per (b, s); a combine launch merges them when splits > 1.
+//               (Flash-decoding split-K: the split partial plus log-sum-exp
+//               merge of amd-mixed-mla submission 593653, `_flash_fp8_split_s1`
+//               and `_flash_fp8_split_s2`.)
+//   persistent  a fixed grid of P workgroups; workgroup p covers the tokens
+//               [floor(p*T/P), floor((p+1)*T/P)) of the concatenated sequences
+//               and writes one partial per sequence it touches, into slot
+//               p + b. The persistent grid of the pages (submission 593653's
+//               cached persistent path; submission 616673's a16w8 persistent
+//               path) needs a metadata kernel; this partition needs none.
+#include "mla_plan.h"
+
+#include <stdint.h>
+
+namespace mla {
+
+static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+static size_t partial_bytes(int num_partials) {
+    // part_o [num_partials][16][512] fp32, then part_lse [num_partials][16] fp32,
+    // each section padded to 256 bytes.
+    size_t o = (size_t)num_partials * kHeads * kDv * sizeof(float);
+    size_t l = (size_t)num_partials * kHeads * sizeof(float);
+    return ((o + 255) / 256) * 256 + ((l + 255) / 256) * 256;
+}
+
+size_t partial_lse_offset(int num_partials) {
+    size_t o = (size_t)num_partials * kHeads * kDv * sizeof(float);
+    return ((o + 255) / 256) * 256;
+}
+
+// Split count for split-K: enough workgroups to give every compute unit one,
+// but never fewer than kMinTokensPerWg tokens per workgroup (the four waves of
+// a workgroup each want at least one 16-token step), and at most kMaxSplits.
+int heuristic_splits(int batch, int64_t total_kv) {
+    if (batch <= 0) return 1;
+    int64_t avg = cdiv(total_kv, batch);
+    int64_t s = cdiv(kNumCUs * kWgsPerCU, batch);
+    int64_t by_len = avg / kMinTokensPerWg;
+    if (s > by_len) s = by_len;
+    if (s > kMaxSplits) s = kMaxSplits;
+    if (s < 1) s = 1;
+    return (int)s;
+}
+
+// Persistent grid: one workgroup per compute unit, fewer when there are not
+// enough tokens to give each at least kMinTokensPerWg.
+int heuristic_grid(int64_t total_kv) {
+    int64_t g = (int64_t)kNumCUs * kWgsPerCU;
+    int64_t by_len = total_kv / kMinTokensPerWg;
+    if (g > by_len) g = by_len;
+    if (g < 1) g = 1;
+    return (int)g;
+}
+
+// The default shape. Split-K when the batch alone fills the chip or when the
+// split grid lands on a whole number of workgroups per compute unit; the
+// persistent grid for large, uneven shapes where the split grid would leave
+// compute units idle.
+static bool prefer_persistent(int batch, int64_t total_kv) {
+    if (total_kv < (int64_t)kNumCUs * kPersistentMinTokensPerCU) return false;
+    int s = heuristic_splits(batch, total_kv);
+    int64_t wgs = (int64_t)s * batch;
+    return (wgs % kNumCUs) != 0;
+}
+
+int make_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_info* p) {
+    if (!p) return MLA_ERR_INVALID_ARG;
+    if (batch < 0 || total_kv < 0 || total_kv > INT32_MAX) return MLA_ERR_INVALID_ARG;
+    if (kv_dtype < MLA_KV_BF16 || kv_dtype > MLA_KV_MXFP4) return MLA_ERR_INVALID_ARG;
+    const bool force_split = (flags & MLA_FLAG_FORCE_SPLIT) != 0;
+    const bool force_pers = (flags & MLA_FLAG_FORCE_PERSISTENT) != 0;
+    if (force_split && force_pers) return MLA_ERR_INVALID_ARG;
+    const int forced_splits = (flags >> MLA_FLAG_SPLITS_SHIFT) & 0xFF;
+    const int forced_grid = (flags >> MLA_FLAG_GRID_SHIFT) & 0xFFF;
+    if (flags & ~(MLA_FLAG_FORCE_SPLIT | MLA_FLAG_FORCE_PERSISTENT | (0xFF << MLA_FLAG_SPLITS_SHIFT) |
+                  (0xFFF << MLA_FLAG_GRID_SHIFT)))
+        return MLA_ERR_INVALID_ARG;
+
+    p->reserved = 0;
+    if (batch == 0) {
+        p->mode = 0;
+        p->num_splits = 1;
+        p->grid = 0;
+        p->num_partials = 0;
+        p->combine = 0;
+        p->workspace_bytes = 0;
+        return MLA_OK;
+    }
+    bool persistent = force_pers || (!force_split && forced_splits == 0 && prefer_persistent(batch, total_kv));
+    if (persistent) {
+        int g = forced_grid ? forced_grid : heuristic_grid(total_kv);
+        p->mode = 1;
+        p->num_splits = 0;
+        p->grid = g;
+        p->num_partials = g + batch - 1;
+        p->combine = 1;
+        p->workspace_bytes = partial_bytes(p->num_partials);
+    } else {
+        int s = forced_splits ? forced_splits : heuristic_splits(batch, total_kv);
+        p->mode = 0;
+        p->num_splits = s;
+        p->grid = s * batch;
+        p->num_partials = (s > 1) ? s * batch : 0;
+        p->combine = (s > 1) ? 1 : 0;
+        p->workspace_bytes = (s > 1) ? partial_bytes(p->num_partials) : 0;
+    }
+    return MLA_OK;
+}
+
+}  // namespace mla
+
+extern "C" int mla_decode_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_info* plan) {
+    return mla::make_plan(batch, total_kv, kv_dtype, flags, plan);
+}
+
+extern "C" size_t mla_decode_workspace_size(int batch, int64_t total_kv, int kv_dtype, int flags) {
+    mla_plan_info p;
+    if (mla::make_plan(batch, total_kv, kv_dtype, flags, &p) != MLA_OK) return 0;
+    return p.workspace_bytes;
+}
+
+extern "C" const char* mla_status_string(int status) {
+    switch (status) {
+        case MLA_OK: return "ok";
+        case MLA_ERR_INVALID_ARG: return "invalid argument";
+        case MLA_ERR_UNSUPPORTED: return "unsupported device (gfx950 required)";
+        case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case MLA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}

@@ -1,0 +1,219 @@
+"""Host-side checks of the C ABI (no GPU needed): exports, planner, validation.
+
+Every entry point declared in include/mla_decode.h must be exported by the
+built library. Argument validation happens on the host before any device call,
+so every error code except MLA_ERR_UNSUPPORTED / MLA_ERR_HIP is reachable here.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+
+@pytest.fixture(scope="module")
+def mla():
+    import mla_decode_02_amd
+
+    return mla_decode_02_amd
+
+
+@pytest.fixture(scope="module")
+def raw_lib(mla):
+    return ctypes.CDLL(mla.LIB_PATH)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(mla_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("mla_decode", "mla_decode_plan", "mla_decode_workspace_size", "mla_dequant_debug", "mla_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(raw_lib):
+    for name in _declared_functions():
+        assert hasattr(raw_lib, name), name
+
+
+def test_status_strings(mla):
+    assert mla.mla_status_string(0) == "ok"
+    for code in (-1, -2, -3, -4):
+        assert mla.mla_status_string(code) not in ("ok", "unknown status")
+    assert mla.mla_status_string(-99) == "unknown status"
+
+
+WORKLOADS = [(4, 1024), (32, 1024), (4, 8192), (64, 8192), (32, 8192), (256, 1024), (256, 8192), (1, 1), (7, 13)]
+
+
+@pytest.mark.parametrize("B,L", WORKLOADS)
+@pytest.mark.parametrize("kv_dtype", [0, 1, 2])
+def test_heuristic_plan_invariants(mla, B, L, kv_dtype):
+    p = mla.mla_decode_plan(B, B * L, kv_dtype)
+    assert p.mode in (0, 1)
+    if p.mode == 0:
+        assert 1 <= p.num_splits <= 64
+        assert p.grid == p.num_splits * B
+        assert p.combine == (1 if p.num_splits > 1 else 0)
+        assert p.num_partials == (p.num_splits * B if p.num_splits > 1 else 0)
+    else:
+        assert 1 <= p.grid <= 4095 and p.num_partials == p.grid + B - 1 and p.combine == 1
+    expect = 0
+    if p.num_partials:
+        o = p.num_partials * 16 * 512 * 4
+        lse = p.num_partials * 16 * 4
+        expect = -(-o // 256) * 256 + -(-lse // 256) * 256
+    assert p.workspace_bytes == expect
+    assert mla.mla_decode_workspace_size(B, B * L, kv_dtype) == expect
+
+
+def test_heuristic_fills_the_chip_for_the_measured_shapes(mla):
+    for B, L in [(32, 1024), (4, 8192), (64, 8192), (32, 8192), (256, 1024)]:
+        p = mla.mla_decode_plan(B, B * L, 1)
+        assert p.grid == 256, (B, L, p)
+
+
+def test_forced_plans(mla):
+    p = mla.mla_decode_plan(4, 4000, 1, mla.flags_for(splits=7))
+    assert (p.mode, p.num_splits, p.grid, p.num_partials) == (0, 7, 28, 28)
+    p = mla.mla_decode_plan(4, 4000, 1, mla.flags_for(splits=1))
+    assert (p.num_splits, p.combine, p.workspace_bytes) == (1, 0, 0)
+    p = mla.mla_decode_plan(4, 4000, 2, mla.flags_for(persistent=True, grid=37))
+    assert (p.mode, p.grid, p.num_partials, p.combine) == (1, 37, 40, 1)
+    p = mla.mla_decode_plan(4, 4000, 2, mla.flags_for(persistent=True))
+    assert p.mode == 1 and p.grid == 4000 // 64
+
+
+@pytest.mark.parametrize("args", [
+    (-1, 10, 1, 0),            # negative batch
+    (2, -1, 1, 0),             # negative total
+    (2, 2 ** 31, 1, 0),        # total beyond int32 indices
+    (2, 10, 3, 0),             # unknown format
+    (2, 10, 1, 0x3),           # both forcing flags
+    (2, 10, 1, 1 << 30),       # unknown flag bit
+])
+def test_plan_rejects_invalid(mla, args):
+    with pytest.raises(mla.MlaError) as e:
+        mla.mla_decode_plan(*args)
+    assert e.value.status == -1
+    assert mla.mla_decode_workspace_size(*args) == 0
+
+
+def test_empty_batch_plan(mla):
+    p = mla.mla_decode_plan(0, 0, 1)
+    assert p.grid == 0 and p.workspace_bytes == 0
+
+
+# ---------------------------------------------------------------- validation
+
+
+def _call(raw_lib, q=16, kv=16, sc=16, indptr=16, indices=16, out=16, lse=None, batch=2, total=64, dtype=1,
+          ws=None, ws_bytes=0, flags=0):
+    f = raw_lib.mla_decode
+    f.restype = ctypes.c_int
+    vp = ctypes.c_void_p
+    f.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_float, vp,
+                  ctypes.c_size_t, ctypes.c_int, vp]
+    return f(q, kv, sc, indptr, indices, out, lse, batch, total, dtype, 0.0, ws, ws_bytes, flags, None)
+
+
+# Pointers are never dereferenced on the host; validation fails before any use.
+A = 0x10000
+
+
+def test_null_and_misaligned_pointers(raw_lib):
+    assert _call(raw_lib, q=None, kv=A, sc=A, indptr=A, indices=A, out=A) == -1
+    assert _call(raw_lib, q=A, kv=None, sc=A, indptr=A, indices=A, out=A) == -1
+    assert _call(raw_lib, q=A, kv=A, sc=None, indptr=A, indices=A, out=A) == -1       # fp8 needs a scale
+    assert _call(raw_lib, q=A, kv=A, sc=A, indptr=None, indices=A, out=A) == -1
+    assert _call(raw_lib, q=A, kv=A, sc=A, indptr=A, indices=None, out=A) == -1       # total > 0 needs indices
+    assert _call(raw_lib, q=A, kv=A, sc=A, indptr=A, indices=A, out=None) == -1
+    assert _call(raw_lib, q=A + 2, kv=A, sc=A, indptr=A, indices=A, out=A) == -1      # q not 16-byte aligned
+    assert _call(raw_lib, q=A, kv=A + 8, sc=A, indptr=A, indices=A, out=A) == -1      # kv not 16-byte aligned
+    assert _call(raw_lib, q=A, kv=A, sc=A, indptr=A + 2, indices=A, out=A) == -1
+    assert _call(raw_lib, q=A, kv=A, sc=A, indptr=A, indices=A, out=A, lse=A + 1) == -1
+    assert _call(raw_lib, q=A, kv=A, sc=A, indptr=A, indices=A, out=A, dtype=7) == -1
+
+
+def test_workspace_too_small(raw_lib, mla):
+    need = mla.mla_decode_workspace_size(2, 64, 1, mla.flags_for(splits=4))
+    assert need > 0
+    f = mla.flags_for(splits=4)
+    assert _call(raw_lib, q=A, kv=A, sc=A, indptr=A, indices=A, out=A, ws=None, ws_bytes=0, flags=f) == -3
+    assert _call(raw_lib, q=A, kv=A, sc=A, indptr=A, indices=A, out=A, ws=A, ws_bytes=need - 1, flags=f) == -3
+    assert _call(raw_lib, q=A, kv=A, sc=A, indptr=A, indices=A, out=A, ws=A + 4, ws_bytes=need, flags=f) == -1
+
+
+def test_batch_zero_is_a_noop(raw_lib):
+    assert _call(raw_lib, q=None, kv=None, sc=None, indptr=None, indices=None, out=None, batch=0, total=0) == 0
+
+
+def test_dequant_debug_validation(raw_lib):
+    f = raw_lib.mla_dequant_debug
+    f.restype = ctypes.c_int
+    vp = ctypes.c_void_p
+    f.argtypes = [ctypes.c_int, vp, vp, ctypes.c_int64, ctypes.c_int, vp, vp]
+    assert f(5, A, A, 4, 0, A, None) == -1
+    assert f(1, A, None, 4, 0, A, None) == -1
+    assert f(1, A, A, -1, 0, A, None) == -1
+    assert f(1, A, A, 4, 2, A, None) == -1
+    assert f(1, A + 8, A, 4, 0, A, None) == -1
+    assert f(1, A, A, 0, 0, A, None) == 0
+
+
+# ---------------------------------------------------------------- persistent partition
+
+
+def _shares(T, G):
+    return [(p * T // G, (p + 1) * T // G) for p in range(G)]
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_persistent_partition_slots(seed):
+    """Workgroup p covers [floor(pT/G), floor((p+1)T/G)); it writes one partial per
+    sequence it touches into slot p + b. Slots are unique, below G + B - 1, and the
+    combine's owner formula floor(((t + 1) G - 1) / T) names the share holding t."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 40))
+    lens = rng.integers(0, 300, size=B) * (rng.random(B) > 0.2)
+    indptr = np.concatenate([[0], np.cumsum(lens)])
+    T = int(indptr[-1])
+    if T == 0:
+        return
+    G = int(rng.integers(1, 300))
+    slots = set()
+    covered = np.zeros(T, dtype=int)
+    for p, (g0, g1) in enumerate(_shares(T, G)):
+        for b in range(B):
+            t0, t1 = max(g0, indptr[b]), min(g1, indptr[b + 1])
+            if t0 < t1:
+                assert p + b not in slots
+                slots.add(p + b)
+                covered[t0:t1] += 1
+    assert np.all(covered == 1)
+    assert max(slots) < G + B - 1 + 1
+    for t in range(0, T, max(1, T // 50)):
+        p = ((t + 1) * G - 1) // T
+        g0, g1 = _shares(T, G)[p]
+        assert g0 <= t < g1
+
+
+@pytest.mark.parametrize("L,S", [(0, 3), (1, 8), (31, 2), (33, 2), (1024, 8), (8192, 64), (100, 7), (5, 64)])
+def test_split_ranges_cover_tokens_once(L, S):
+    """Split s covers [min(L, s*chunk), min(L, s*chunk + chunk)), chunk = ceil(L/S)
+    rounded up to the 32-token wave step."""
+    chunk = -(-(-(-L // S)) // 32) * 32 if L else 0
+    covered = np.zeros(L, dtype=int)
+    for s in range(S):
+        t0 = min(L, s * chunk)
+        t1 = min(L, t0 + chunk)
+        covered[t0:t1] += 1
+    assert np.all(covered == 1)

@@ -1,0 +1,263 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 CPU oracle.
+
+Tolerances: every output element within 2e-2 absolute + 2e-2 relative of the
+oracle and every lse within 1e-3 absolute (the stated acceptance band), plus a
+tighter internal gate, max |gpu - oracle| <= 2e-3 on the outputs, because the
+acceptance band alone would miss a wrong softmax scale. The
+error the arithmetic actually allows is bf16 rounding of P and of the output,
+a few 1e-4 for these value ranges.
+Decoding is checked bit-exactly against the oracle's decoders.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import synthetic as syn
+from helpers import set_one_hot
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL, LSE_TOL, GATE = 2e-2, 2e-2, 1e-3, 2e-3
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def mla(dev):
+    import mla_decode_02_amd
+
+    return mla_decode_02_amd
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+
+    oracle.build(force=False)
+    return oracle
+
+
+def to_dev(case, dev):
+    q = torch.from_numpy(case.q.view(np.int16)).view(torch.bfloat16).to(dev)
+    if case.kv_dtype == syn.KV_BF16:
+        kv = torch.from_numpy(case.kv.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        kv = torch.from_numpy(case.kv).to(dev)
+    sc = None if case.kv_scales is None else torch.from_numpy(case.kv_scales).to(dev)
+    return dict(q=q, kv=kv, kv_scales=sc, kv_indptr=torch.from_numpy(case.kv_indptr).to(dev),
+                kv_indices=torch.from_numpy(case.kv_indices).to(dev))
+
+
+def run_gpu(mla, case, dev, flags=0, sm_scale=0.0, with_lse=True, nan_workspace=True):
+    t = to_dev(case, dev)
+    B = case.batch
+    out = torch.full((B, 16, 512), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((B, 16), float("nan"), dtype=torch.float32, device=dev) if with_lse else None
+    need = mla.mla_decode_workspace_size(B, case.total_kv, case.kv_dtype, flags)
+    ws = None
+    if need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        if nan_workspace:  # unwritten partials would surface as NaN
+            ws.view(torch.float32)[: need // 4].fill_(float("nan"))
+    mla.mla_decode(t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], t["kv_indices"], out, lse,
+                   total_kv=case.total_kv, kv_dtype=case.kv_dtype, sm_scale=sm_scale, workspace=ws, flags=flags)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), (lse.cpu().numpy().astype(np.float64) if with_lse else None)
+
+
+def check(got, ref, name=""):
+    go, gl = got
+    ro, rl = ref
+    assert not np.any(np.isnan(go)), f"{name}: NaN in output"
+    err = np.abs(go - ro)
+    bad = err > ATOL + RTOL * np.abs(ro)
+    assert not np.any(bad), f"{name}: {bad.sum()} outputs outside the band, max err {err.max():.3e}"
+    assert err.max() <= GATE, f"{name}: max output error {err.max():.3e} above the internal gate"
+    if gl is not None:
+        fin = np.isfinite(rl)
+        assert np.array_equal(np.isneginf(gl), np.isneginf(rl)), f"{name}: -inf lse pattern differs"
+        if fin.any():
+            lerr = np.abs(gl[fin] - rl[fin]).max()
+            assert lerr <= LSE_TOL, f"{name}: lse error {lerr:.3e}"
+    return float(err.max())
+
+
+def oracle_ref(orc, case, batches=None, sm_scale=1.0 / 24.0):
+    o, l = orc.mla_decode(case.q, case.kv_dtype, case.kv, case.kv_scales, case.kv_indptr, case.kv_indices,
+                          sm_scale=sm_scale, batches=batches)
+    return o, l
+
+
+DTYPES = [syn.KV_BF16, syn.KV_FP8, syn.KV_MXFP4]
+
+
+# ------------------------------------------------------------------ decode, bit-exact
+
+def _f32_equal(a, b):
+    a = np.asarray(a, np.float32)
+    b = np.asarray(b, np.float32)
+    nan = np.isnan(a) & np.isnan(b)
+    return nan | (a.view(np.uint32) == b.view(np.uint32))
+
+
+@pytest.mark.parametrize("path", [0, 1])
+def test_dequant_fp8_all_codes_bit_exact(mla, orc, dev, path):
+    rng = np.random.default_rng(0)
+    rows = 70
+    codes = rng.integers(0, 256, size=(rows, 576)).astype(np.uint8)
+    codes[0, :256] = np.arange(256, dtype=np.uint8)
+    codes[1, 256:512] = np.arange(256, dtype=np.uint8)
+    codes[2, 320:576] = np.arange(256, dtype=np.uint8)  # covers the RoPE columns too
+    for scale in (1.0, 0.0123456, 7.5):
+        s = np.array([scale], np.float32)
+        got = mla.mla_dequant_debug(torch.from_numpy(codes).to(dev), torch.from_numpy(s).to(dev), 1, path=path)
+        ref = orc.dequant_rows(1, codes, s)
+        ok = _f32_equal(got.cpu().numpy(), ref)
+        assert ok.all(), f"scale {scale} path {path}: {np.argwhere(~ok)[:5]}"
+
+
+@pytest.mark.parametrize("path", [0, 1])
+def test_dequant_mxfp4_all_code_scale_pairs_bit_exact(mla, orc, dev, path):
+    rng = np.random.default_rng(1)
+    rows = 256 + 37
+    nib = rng.integers(0, 16, size=(rows, 576)).astype(np.uint8)
+    nib[:256, 0:16] = np.arange(16, dtype=np.uint8)[None, :]
+    nib[:256, 48:64] = np.arange(16, dtype=np.uint8)[None, ::-1]
+    nib[:256, 560:576] = np.arange(16, dtype=np.uint8)[None, :]
+    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    scales = rng.integers(0, 256, size=(rows, 18)).astype(np.uint8)
+    scales[:256, 0] = np.arange(256, dtype=np.uint8)   # every scale code x every nibble, block 0
+    scales[:256, 1] = np.arange(256, dtype=np.uint8)[::-1]
+    scales[:256, 17] = np.arange(256, dtype=np.uint8)  # RoPE block
+    got = mla.mla_dequant_debug(torch.from_numpy(packed).to(dev), torch.from_numpy(scales).to(dev), 2, path=path)
+    ref = orc.dequant_rows(2, packed, scales)
+    ok = _f32_equal(got.cpu().numpy(), ref)
+    assert ok.all(), f"path {path}: {np.argwhere(~ok)[:5]}"
+
+
+@pytest.mark.parametrize("path", [0, 1])
+def test_dequant_bf16_bit_exact(mla, orc, dev, path):
+    rng = np.random.default_rng(2)
+    bits = rng.integers(0, 65536, size=(45, 576)).astype(np.uint16)
+    kv = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    got = mla.mla_dequant_debug(kv, None, 0, path=path)
+    ref = orc.dequant_rows(0, bits, None)
+    assert _f32_equal(got.cpu().numpy(), ref).all()
+
+
+# ------------------------------------------------------------------ attention parity, small sizes
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+def test_ragged_shuffled_default_plan(mla, orc, dev, kv_dtype):
+    lens = [1, 37, 100, 0, 16, 33, 513, 64]
+    case = syn.make_case(len(lens), lens, kv_dtype, seed=20 + kv_dtype, shuffle=True, extra_rows=11)
+    check(run_gpu(mla, case, dev), oracle_ref(orc, case), "ragged")
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+@pytest.mark.parametrize("splits", [1, 2, 3, 8, 64])
+def test_forced_splits(mla, orc, dev, kv_dtype, splits):
+    lens = [300, 7, 1030]
+    case = syn.make_case(3, lens, kv_dtype, seed=30 + splits, shuffle=True)
+    check(run_gpu(mla, case, dev, flags=mla.flags_for(splits=splits)), oracle_ref(orc, case), f"splits={splits}")
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+@pytest.mark.parametrize("grid", [1, 5, 64, 300])
+def test_persistent_grid(mla, orc, dev, kv_dtype, grid):
+    lens = [300, 0, 7, 1030, 1, 64]
+    case = syn.make_case(len(lens), lens, kv_dtype, seed=40 + grid, shuffle=True)
+    check(run_gpu(mla, case, dev, flags=mla.flags_for(persistent=True, grid=grid)), oracle_ref(orc, case),
+          f"persistent grid={grid}")
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+@pytest.mark.parametrize("L", [1, 15, 16, 17, 31, 32, 33, 63, 65, 127, 129, 1000])
+def test_lengths_single_sequence(mla, orc, dev, kv_dtype, L):
+    case = syn.make_case(1, L, kv_dtype, seed=50 + L, shuffle=True, extra_rows=3)
+    check(run_gpu(mla, case, dev), oracle_ref(orc, case), f"L={L}")
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+def test_long_sequence_several_index_windows(mla, orc, dev, kv_dtype):
+    case = syn.make_case(2, [9000, 4500], kv_dtype, seed=60, shuffle=True)
+    check(run_gpu(mla, case, dev, flags=mla.flags_for(splits=1)), oracle_ref(orc, case), "one split")
+    check(run_gpu(mla, case, dev, flags=mla.flags_for(persistent=True, grid=1)), oracle_ref(orc, case), "grid 1")
+    check(run_gpu(mla, case, dev), oracle_ref(orc, case), "default")
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+def test_all_sequences_empty(mla, orc, dev, kv_dtype):
+    case = syn.make_case(3, [0, 0, 0], kv_dtype, seed=61, extra_rows=4)
+    for flags in (0, mla.flags_for(splits=4), mla.flags_for(persistent=True, grid=3)):
+        o, l = run_gpu(mla, case, dev, flags=flags)
+        assert np.all(o == 0) and np.all(np.isneginf(l))
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+def test_without_lse_and_custom_scale(mla, orc, dev, kv_dtype):
+    case = syn.make_case(3, [40, 200, 5], kv_dtype, seed=62, shuffle=True)
+    got = run_gpu(mla, case, dev, with_lse=False)
+    check(got, (oracle_ref(orc, case)[0], None), "no lse")
+    sc = 1.0 / math.sqrt(512.0)
+    check(run_gpu(mla, case, dev, sm_scale=sc), oracle_ref(orc, case, sm_scale=sc), "sm_scale")
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+def test_one_hot_scores(mla, orc, dev, kv_dtype):
+    """q = 1440 e_col: score 60 for one token, 0 for the others (pins the scale)."""
+    for col in (3, 540):
+        case = syn.make_case(1, 300, kv_dtype, seed=63, shuffle=True)
+        set_one_hot(case, 123, col)
+        case.q[:] = 0
+        case.q[:, :, col] = 0x44B4
+        got = run_gpu(mla, case, dev)
+        ref = oracle_ref(orc, case)
+        check(got, ref, f"one-hot col {col}")
+        assert abs(got[1][0, 0] - 60.0) < 1e-3
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+def test_rope_only_query(mla, orc, dev, kv_dtype):
+    case = syn.make_case(2, [77, 300], kv_dtype, seed=64, shuffle=True)
+    case.q[:, :, :512] = 0
+    check(run_gpu(mla, case, dev), oracle_ref(orc, case), "rope only")
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+def test_deterministic(mla, dev, kv_dtype):
+    case = syn.make_case(4, [1000, 3000, 5, 700], kv_dtype, seed=65, shuffle=True)
+    a = run_gpu(mla, case, dev)
+    b = run_gpu(mla, case, dev, nan_workspace=False)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_large_scores_rescale_path(mla, orc, dev):
+    """Scores that grow along the sequence force the running-max rescale repeatedly."""
+    case = syn.make_case(1, 2000, syn.KV_BF16, seed=66)
+    x = syn.bf16_bits_to_f32(case.kv).copy()
+    x[:, 0] = np.linspace(-4, 4, x.shape[0], dtype=np.float32)
+    case.kv = syn.f32_to_bf16_bits(x)
+    case.q[:, :, 0] = syn.f32_to_bf16_bits(np.full((1, 16), 96.0, np.float32))[0]
+    check(run_gpu(mla, case, dev, flags=mla.flags_for(splits=1)), oracle_ref(orc, case), "rescale")
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled
+
+@pytest.mark.parametrize("name", list(syn.WORKLOADS))
+def test_full_size_workload_sampled(mla, orc, dev, name):
+    """Full-size workloads in the benchmark's launch configuration (default plan);
+    the oracle computes a sample of sequences."""
+    case = syn.make_workload(name)
+    got_o, got_l = run_gpu(mla, case, dev)
+    B = case.batch
+    sample = sorted({0, B - 1, B // 2, (7 * B) // 11})
+    ro, rl = oracle_ref(orc, case, batches=sample)
+    check((got_o[sample], got_l[sample]), (ro, rl), name)

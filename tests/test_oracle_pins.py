@@ -19,6 +19,7 @@ import pytest
 import torch
 
 import synthetic as syn
+from helpers import set_one_hot as _set_one_hot
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -225,24 +226,6 @@ def test_single_token(oracle_mod, kv_dtype):
     q = _q64(case).numpy()[0]
     np.testing.assert_allclose(out[0], np.broadcast_to(x[:512], (16, 512)), rtol=0, atol=0)
     np.testing.assert_allclose(lse[0], (q @ x) / 24.0, rtol=1e-14, atol=1e-14)
-
-
-def _set_one_hot(case, j_star, col):
-    """Make x_j[col] = 1 for token j_star and 0 for every other referenced token."""
-    rows = case.kv_indices
-    if case.kv_dtype == syn.KV_BF16:
-        case.kv[rows, col] = 0
-        case.kv[rows[j_star], col] = 0x3F80  # 1.0
-    elif case.kv_dtype == syn.KV_FP8:
-        case.kv_scales[0] = 1.0
-        case.kv[rows, col] = 0
-        case.kv[rows[j_star], col] = 0x38  # 1.0
-    else:
-        shift = 4 * (col & 1)
-        keep = np.uint8(0xF0 >> shift)
-        case.kv[rows, col // 2] &= keep
-        case.kv[rows[j_star], col // 2] |= np.uint8(0x2 << shift)  # e2m1 1.0
-        case.kv_scales[rows[j_star], col // 32] = 127
 
 
 @pytest.mark.parametrize("kv_dtype", DTYPES)
