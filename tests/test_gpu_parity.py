@@ -2,10 +2,15 @@
 
 Tolerances: every output element within 2e-2 absolute + 2e-2 relative of the
 oracle and every lse within 1e-3 absolute (the stated acceptance band), plus a
-tighter internal gate, max |gpu - oracle| <= 2e-3 on the outputs, because the
-acceptance band alone would miss a wrong softmax scale. The
-error the arithmetic actually allows is bf16 rounding of P and of the output,
-a few 1e-4 for these value ranges.
+tighter internal gate on the outputs, because the acceptance band alone would
+miss a wrong softmax scale. The gate is the worst-case error of the kernel's
+arithmetic: the probabilities enter the P.V product rounded to bf16 (relative
+error <= 2^-8 each) and the output is rounded to bf16 (<= 2^-8 |out|), so
+
+    |gpu - oracle| <= 2^-8 (sum_j p_j |V_j[d]| + |oracle|) + 1e-4
+
+with p_j the exact softmax weights (computed here in fp64 from the decoded rows
+and the oracle's lse) and 1e-4 for the fp32 accumulation.
 Decoding is checked bit-exactly against the oracle's decoders.
 """
 import math
@@ -19,7 +24,9 @@ from helpers import set_one_hot
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-ATOL, RTOL, LSE_TOL, GATE = 2e-2, 2e-2, 1e-3, 2e-3
+ATOL, RTOL, LSE_TOL = 2e-2, 2e-2, 1e-3
+U_BF16 = 2.0 ** -8  # unit roundoff of bf16 (8-bit significand)
+GATE_SLACK = 1e-4
 
 
 @pytest.fixture(scope="module")
@@ -74,12 +81,18 @@ def run_gpu(mla, case, dev, flags=0, sm_scale=0.0, with_lse=True, nan_workspace=
 
 def check(got, ref, name=""):
     go, gl = got
-    ro, rl = ref
+    ro, rl = ref[0], ref[1]
     assert not np.any(np.isnan(go)), f"{name}: NaN in output"
     err = np.abs(go - ro)
     bad = err > ATOL + RTOL * np.abs(ro)
     assert not np.any(bad), f"{name}: {bad.sum()} outputs outside the band, max err {err.max():.3e}"
-    assert err.max() <= GATE, f"{name}: max output error {err.max():.3e} above the internal gate"
+    if len(ref) > 2:
+        allow = U_BF16 * (ref[2] + np.abs(ro)) + GATE_SLACK
+        over = err > allow
+        if np.any(over):
+            i = np.unravel_index(np.argmax(err - allow), err.shape)
+            raise AssertionError(f"{name}: {over.sum()} outputs above the rounding bound; worst at {i}: "
+                                 f"gpu {go[i]:.6f} oracle {ro[i]:.6f} bound {allow[i]:.2e}")
     if gl is not None:
         fin = np.isfinite(rl)
         assert np.array_equal(np.isneginf(gl), np.isneginf(rl)), f"{name}: -inf lse pattern differs"
@@ -89,10 +102,28 @@ def check(got, ref, name=""):
     return float(err.max())
 
 
+def weighted_abs_v(orc, case, batches, lse, sm_scale):
+    """sum_j p_j |V_j[d]| per (sequence, head, column), p_j = exp(s_j - lse) in fp64."""
+    res = np.zeros((len(batches), 16, 512))
+    for i, b in enumerate(batches):
+        s0, s1 = int(case.kv_indptr[b]), int(case.kv_indptr[b + 1])
+        if s1 == s0:
+            continue
+        rows = case.kv_indices[s0:s1]
+        sc = case.kv_scales[rows] if case.kv_dtype == syn.KV_MXFP4 else case.kv_scales
+        x = orc.dequant_rows(case.kv_dtype, case.kv[rows], sc).astype(np.float64)
+        q = syn.bf16_bits_to_f32(case.q[b]).astype(np.float64)
+        p = np.exp((q @ x.T) * sm_scale - lse[i][:, None])
+        res[i] = p @ np.abs(x[:, :512])
+    return res
+
+
 def oracle_ref(orc, case, batches=None, sm_scale=1.0 / 24.0):
+    """Oracle outputs, lse, and the per-element rounding bound term sum_j p_j |V_j[d]|."""
     o, l = orc.mla_decode(case.q, case.kv_dtype, case.kv, case.kv_scales, case.kv_indptr, case.kv_indices,
                           sm_scale=sm_scale, batches=batches)
-    return o, l
+    blist = list(range(case.batch)) if batches is None else list(batches)
+    return o, l, weighted_abs_v(orc, case, blist, l, sm_scale)
 
 
 DTYPES = [syn.KV_BF16, syn.KV_FP8, syn.KV_MXFP4]
@@ -205,7 +236,8 @@ def test_all_sequences_empty(mla, orc, dev, kv_dtype):
 def test_without_lse_and_custom_scale(mla, orc, dev, kv_dtype):
     case = syn.make_case(3, [40, 200, 5], kv_dtype, seed=62, shuffle=True)
     got = run_gpu(mla, case, dev, with_lse=False)
-    check(got, (oracle_ref(orc, case)[0], None), "no lse")
+    ref = oracle_ref(orc, case)
+    check(got, (ref[0], None, ref[2]), "no lse")
     sc = 1.0 / math.sqrt(512.0)
     check(run_gpu(mla, case, dev, sm_scale=sc), oracle_ref(orc, case, sm_scale=sc), "sm_scale")
 
@@ -259,5 +291,4 @@ def test_full_size_workload_sampled(mla, orc, dev, name):
     got_o, got_l = run_gpu(mla, case, dev)
     B = case.batch
     sample = sorted({0, B - 1, B // 2, (7 * B) // 11})
-    ro, rl = oracle_ref(orc, case, batches=sample)
-    check((got_o[sample], got_l[sample]), (ro, rl), name)
+    check((got_o[sample], got_l[sample]), oracle_ref(orc, case, batches=sample), name)
