@@ -58,7 +58,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 16;                // tokens per MFMA tile
-constexpr int kStepTokens = 2 * kTile;   // tokens per wave step
+static_assert(kStepTokens == 2 * kTile, "a step is two MFMA tiles");
 constexpr int kKSteps = kDqk / 32;       // 18 MFMA k-steps over the 576 score dims
 constexpr int kBlocks = kDv / 16;        // 32 output blocks of 16 columns per wave
 constexpr float kRescaleThresh = 8.0f;   // log2 units
@@ -101,8 +101,9 @@ struct Fmt<MLA_KV_BF16> {
     static constexpr int kCodeLoads = 18;
     static constexpr int kTileBytes = 18 * 1024;
     static constexpr int kScaleBytes = 0;
-    static constexpr int kRing = 1;         // steps resident per wave (LDS bound)
-    static constexpr int kOpsPerStep = 36;  // VMEM instructions issued per step
+    static constexpr int kRing = 3;      // steps resident in the workgroup's LDS ring
+    static constexpr int kOps = 36;      // LDS-DMA instructions per step
+    static constexpr int kWgsPerCU = 1;  // LDS bound
 };
 template <>
 struct Fmt<MLA_KV_FP8_E4M3> {
@@ -110,8 +111,9 @@ struct Fmt<MLA_KV_FP8_E4M3> {
     static constexpr int kCodeLoads = 9;
     static constexpr int kTileBytes = 9 * 1024;
     static constexpr int kScaleBytes = 0;
-    static constexpr int kRing = 2;
-    static constexpr int kOpsPerStep = 18;
+    static constexpr int kRing = 3;
+    static constexpr int kOps = 18;
+    static constexpr int kWgsPerCU = 2;
 };
 template <>
 struct Fmt<MLA_KV_MXFP4> {
@@ -119,20 +121,21 @@ struct Fmt<MLA_KV_MXFP4> {
     static constexpr int kCodeLoads = 4;
     static constexpr int kTileBytes = 4 * 1024 + 512;
     static constexpr int kScaleBytes = 18 * kStepTokens * 4;
-    static constexpr int kRing = 3;
-    static constexpr int kOpsPerStep = 2 * (4 + 2) + 9;
+    static constexpr int kRing = 4;
+    static constexpr int kOps = 2 * (4 + 2) + 9;
+    static constexpr int kWgsPerCU = 2;
 };
 
+// LDS of one stage-1 workgroup: the ring of staged steps, the exchange buffer
+// for the four waves' partial scores, and the index window.
 template <int KV>
 struct Layout {
     static constexpr int kStepBytes = 2 * Fmt<KV>::kTileBytes + Fmt<KV>::kScaleBytes;
-    static constexpr int kRingBytes = kWaves * Fmt<KV>::kRing * kStepBytes;
-    static constexpr int kPartialBytes = kWaves * kHeads * kDv * 4;
-    static constexpr int kMainBytes = kRingBytes > kPartialBytes ? kRingBytes : kPartialBytes;
-    static constexpr int kIdxOff = kMainBytes;
-    static constexpr int kStatOff = kIdxOff + kIdxWindow * 4;
-    static constexpr int kBytes = kStatOff + 2 * kWaves * kHeads * 4;
-    static_assert(kBytes <= 160 * 1024, "stage-1 LDS exceeds 160 KiB");
+    static constexpr int kRingBytes = Fmt<KV>::kRing * kStepBytes;
+    static constexpr int kSbufOff = kRingBytes;
+    static constexpr int kIdxOff = kSbufOff + kWaves * 64 * 16;
+    static constexpr int kBytes = kIdxOff + kIdxWindow * 4;
+    static_assert(kBytes * Fmt<KV>::kWgsPerCU <= 160 * 1024, "stage-1 LDS exceeds 160 KiB per CU");
 };
 
 // First score dim of the eight held by lane group G in k-step ks. Q^T is
@@ -187,38 +190,46 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
-// Gather the step starting at window token tok0 into `step`. Tokens at or
-// beyond n re-read the last valid row (always in bounds).
+// LDS-DMA instruction `op` (0 <= op < kOps) of the step starting at window
+// token tok0, written into `step`. Tokens at or beyond n re-read the last
+// valid row (always in bounds). The ops of a step are spread over the waves
+// of the workgroup: wave w issues ops w, w + nw, ...
+//   bf16 / fp8: op = 18t + u (bf16) or 9t + u (fp8): code load u of tile t.
+//   MXFP4: op < 12: 6t + k, code load k < 4 or RoPE dword load k - 4 of tile t;
+//          op >= 12: e8m0 scale load op - 12 (two blocks x 32 tokens each).
 template <int KV>
-__device__ __forceinline__ void issue_step(const Params& P, const int32_t* idx, int tok0, int n, uint8_t* step,
-                                           int lane) {
+__device__ __forceinline__ void issue_op(const Params& P, const int32_t* idx, int tok0, int n, uint8_t* step,
+                                         int lane, int op) {
     constexpr int RB = Fmt<KV>::kRowBytes;
+    constexpr int TB = Fmt<KV>::kTileBytes;
     const int G = lane >> 4, r = lane & 15;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    if constexpr (KV != MLA_KV_MXFP4) {
+        const int t = op / Fmt<KV>::kCodeLoads, u = op % Fmt<KV>::kCodeLoads;
         const int64_t row = idx[min(tok0 + kTile * t + r, n - 1)];
-        const uint8_t* src = P.kv + row * RB + 16 * G;
-        uint8_t* tile = step + t * Fmt<KV>::kTileBytes;
-#pragma unroll
-        for (int u = 0; u < Fmt<KV>::kCodeLoads; ++u) dma16(src + 64 * u, lds_addr(tile + 1024 * u));
-        if constexpr (KV == MLA_KV_MXFP4) {
-#pragma unroll
-            for (int v = 0; v < 2; ++v) {
-                const int s = 64 * v + lane;  // (row s / 8, dword s % 8) of the RoPE block
-                const int64_t row2 = idx[min(tok0 + kTile * t + (s >> 3), n - 1)];
-                dma4(P.kv + row2 * RB + 256 + 4 * (s & 7), lds_addr(tile + 4096 + 256 * v));
-            }
+        dma16(P.kv + row * RB + 64 * u + 16 * G, lds_addr(step + t * TB + 1024 * u));
+    } else if (op < 12) {
+        const int t = op / 6, k = op % 6;
+        if (k < 4) {
+            const int64_t row = idx[min(tok0 + kTile * t + r, n - 1)];
+            dma16(P.kv + row * RB + 64 * k + 16 * G, lds_addr(step + t * TB + 1024 * k));
+        } else {
+            const int v = k - 4, sl = 64 * v + lane;  // (row sl / 8, dword sl % 8) of the RoPE block
+            const int64_t row = idx[min(tok0 + kTile * t + (sl >> 3), n - 1)];
+            dma4(P.kv + row * RB + 256 + 4 * (sl & 7), lds_addr(step + t * TB + 4096 + 256 * v));
         }
-    }
-    if constexpr (KV == MLA_KV_MXFP4) {
+    } else {
+        // dword 64 v + lane of the scale block = (block 2v + lane / 32, token lane % 32)
+        const int v = op - 12;
         const uint8_t* sc = reinterpret_cast<const uint8_t*>(P.kv_scales);
-        const int64_t row3 = idx[min(tok0 + (lane & 31), n - 1)];
-#pragma unroll
-        for (int v = 0; v < 9; ++v) {  // dword 64 v + lane = (block 2v + lane / 32, token lane % 32)
-            dma1(sc + row3 * MLA_MX_SCALES_PER_ROW + 2 * v + (lane >> 5),
-                 lds_addr(step + 2 * Fmt<KV>::kTileBytes + 256 * v));
-        }
+        const int64_t row = idx[min(tok0 + (lane & 31), n - 1)];
+        dma1(sc + row * MLA_MX_SCALES_PER_ROW + 2 * v + (lane >> 5), lds_addr(step + 2 * TB + 256 * v));
     }
+}
+
+template <int KV>
+__device__ __forceinline__ void issue_ops(const Params& P, const int32_t* idx, int tok0, int n, uint8_t* step,
+                                          int lane, int first, int stride) {
+    for (int op = first; op < Fmt<KV>::kOps; op += stride) issue_op<KV>(P, idx, tok0, n, step, lane, op);
 }
 
 // e8m0 code -> fp32 scale operand of the scaled converts (the code is the
@@ -335,28 +346,40 @@ __device__ __forceinline__ void pv_operand_fp4(const uint8_t* step, int b, int l
 // 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+constexpr int kHalfK = kKSteps / 2;            // 9 score k-steps per wave
+constexpr int kWaveBlocks = kBlocks / kWaves;  // 8 output blocks (128 columns) per wave
+
+// Partial scores of one wave: tile t, score k-steps kHalfK * HF .. +kHalfK-1.
+// Result: lane (G, r) holds S^T[token 4G+i of tile t][head r] over those dims.
+template <int KV, int HF>
+__device__ __forceinline__ f32x4 qk_partial(const uint8_t* step, const bf16x8 (&qB)[kHalfK], int t, int lane) {
+    f32x4 e0 = {0.f, 0.f, 0.f, 0.f}, e1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kHalfK; ++j) {
+        const bf16x8 k = qk_operand<KV>(step, t, kHalfK * HF + j, lane);
+        if (j & 1) e1 = mfma32(k, qB[j], e1);
+        else e0 = mfma32(k, qB[j], e0);
+    }
+    return e0 + e1;
+}
+
 struct WaveAcc {
-    f32x4 o[kBlocks];  // o[blk][i]: head 4G+i, column dcol(blk, r)
-    float m;           // running max of head r (log2 units), same in its 4 lanes
-    float l;           // this lane's share of head r's softmax denominator
+    f32x4 o[kWaveBlocks];  // o[j][i]: head 4G+i, column dcol(kWaveBlocks * wave + j, r)
+    float m;               // running max of head r (log2 units), the same in every lane and wave
+    float l;               // this lane's share of head r's softmax denominator
 };
 
+// Online softmax of one step's 32 scores and this wave's share of P . V.
+// s[t]: full scores of tile t (the same in all four waves, so every wave
+// takes the same rescale decisions and keeps the same m and l).
 template <int KV>
-__device__ __forceinline__ void compute_step(const uint8_t* step, const bf16x8 (&qB)[kKSteps], float qk_scale,
-                                             int nvalid, int lane, WaveAcc& a) {
+__device__ __forceinline__ void softmax_pv(const uint8_t* step, const f32x4 (&s)[2], float qk_scale, int nvalid,
+                                           int lane, int wave, WaveAcc& a) {
     const int G = lane >> 4;
-    // Scores of both tiles: S^T[token 4G+i (+16)][head r] in lane (G, r).
-    f32x4 s[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        f32x4 e0 = {0.f, 0.f, 0.f, 0.f}, e1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < kKSteps; ks += 2) {
-            e0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qk_operand<KV>(step, t, ks, lane), qB[ks], e0, 0, 0, 0);
-            e1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qk_operand<KV>(step, t, ks + 1, lane), qB[ks + 1], e1, 0, 0, 0);
-        }
-        s[t] = e0 + e1;
-    }
     float x[8];
     float mx = -INFINITY;
 #pragma unroll
@@ -375,9 +398,9 @@ __device__ __forceinline__ void compute_step(const uint8_t* step, const bf16x8 (
 #pragma unroll
         for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * G + i);
 #pragma unroll
-        for (int blk = 0; blk < kBlocks; ++blk)
+        for (int j = 0; j < kWaveBlocks; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a.o[blk][i] *= al[i];
+            for (int i = 0; i < 4; ++i) a.o[j][i] *= al[i];
     }
     float p[8];
 #pragma unroll
@@ -389,156 +412,143 @@ __device__ __forceinline__ void compute_step(const uint8_t* step, const bf16x8 (
 
     if constexpr (KV == MLA_KV_MXFP4) {
 #pragma unroll
-        for (int b = 0; b < kBlocks / 2; ++b) {
+        for (int j = 0; j < kWaveBlocks / 2; ++j) {
             bf16x8 ev, od;
-            pv_operand_fp4(step, b, lane, ev, od);
-            a.o[2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, ev, a.o[2 * b], 0, 0, 0);
-            a.o[2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, od, a.o[2 * b + 1], 0, 0, 0);
+            pv_operand_fp4(step, (kWaveBlocks / 2) * wave + j, lane, ev, od);
+            a.o[2 * j] = mfma32(pa, ev, a.o[2 * j]);
+            a.o[2 * j + 1] = mfma32(pa, od, a.o[2 * j + 1]);
         }
     } else {
 #pragma unroll
-        for (int c = 0; c < kBlocks; ++c)
-            a.o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, pv_operand<KV>(step, c, lane), a.o[c], 0, 0, 0);
+        for (int j = 0; j < kWaveBlocks; ++j)
+            a.o[j] = mfma32(pa, pv_operand<KV>(step, kWaveBlocks * wave + j, lane), a.o[j]);
     }
 }
 
-// Wait for the step issued `ahead` steps before the most recently issued one.
+// Wait until this wave's own LDS-DMA ops of all but the last `groups` issued
+// steps have landed. Wave w issues ops w, w + 4, ... of every step.
 template <int KV>
-__device__ __forceinline__ void wait_step(int ahead) {
-    constexpr int N = Fmt<KV>::kOpsPerStep;
-    if (ahead <= 0) wait_vmcnt<0>();
-    else if (ahead == 1) wait_vmcnt<N>();
-    else wait_vmcnt<2 * N>();
+__device__ __forceinline__ void wait_own(int groups, int wave) {
+    constexpr int kHi = (Fmt<KV>::kOps + kWaves - 1) / kWaves;
+    constexpr int kLo = Fmt<KV>::kOps / kWaves;
+    const bool hi = wave < Fmt<KV>::kOps % kWaves;
+    if (groups <= 0) wait_vmcnt<0>();
+    else if (groups == 1) { if (hi) wait_vmcnt<kHi>(); else wait_vmcnt<kLo>(); }
+    else { if (hi) wait_vmcnt<2 * kHi>(); else wait_vmcnt<2 * kLo>(); }
 }
 
 // Attend tokens [t0, t1) of sequence b with the whole workgroup and write the
 // result: final bf16 output + lse when `final`, else partial slot `slot`.
+// The four waves work on the same 32-token step: wave w computes the scores of
+// tile w % 2 over score k-steps 9 (w / 2) .. +8, the partial scores are summed
+// through LDS in a fixed order, and every wave then runs the same softmax and
+// accumulates P . V for its own 128 output columns.
 template <int KV>
 __device__ void run_wg(const Params& P, uint8_t* smem, int b, int t0, int t1, bool final, int slot) {
     using L = Layout<KV>;
-    constexpr int D = Fmt<KV>::kRing - 1;  // steps in flight ahead of the one computed
-    static_assert(D <= 2, "wait_step handles at most two steps ahead");
+    constexpr int R = Fmt<KV>::kRing;
+    constexpr int D = R - 1;  // steps issued ahead of the one computed
+    static_assert(D >= 1 && D <= 3, "ring depth");
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, G = lane >> 4, r = lane & 15;
+    const int tile = wave & 1, hf = wave >> 1;
     int32_t* idx = reinterpret_cast<int32_t*>(smem + L::kIdxOff);
-    float* sm_m = reinterpret_cast<float*>(smem + L::kStatOff);
-    float* sm_l = sm_m + kWaves * kHeads;
-    float* sm_o = reinterpret_cast<float*>(smem);  // epilogue: [wave][head][512]
-    uint8_t* ring = smem + wave * Fmt<KV>::kRing * L::kStepBytes;
+    f32x4* sbuf = reinterpret_cast<f32x4*>(smem + L::kSbufOff);
 
     float kv_scale = 1.0f;
     if constexpr (KV == MLA_KV_FP8_E4M3) kv_scale = *reinterpret_cast<const float*>(P.kv_scales);
     const float qk_scale = P.sm_scale * kv_scale * kLog2e;
 
-    bf16x8 qB[kKSteps];
+    // The first index window and this wave's half of Q^T are requested together
+    // so that the workgroup start pays one memory round trip for both.
+    constexpr int kPer = kIdxWindow / kThreads;
+    int32_t iv[kPer];
+    auto load_idx = [&](int w0, int n) {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) iv[k] = (tid + k * kThreads < n) ? P.indices[w0 + tid + k * kThreads] : 0;
+    };
+    load_idx(t0, min(kIdxWindow, t1 - t0));
+    bf16x8 qB[kHalfK];
     {
         const __bf16* qrow = P.q + ((int64_t)b * kHeads + r) * kDqk;
 #pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) qB[ks] = *reinterpret_cast<const bf16x8*>(qrow + dbase<KV>(ks, G));
-        // Consume Q^T here so that the compiler's wait for these loads is placed
-        // before the token loop, not inside it.
-#pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" ::"v"(qB[ks]));
+        for (int j = 0; j < kHalfK; ++j)
+            qB[j] = *reinterpret_cast<const bf16x8*>(qrow + dbase<KV>(kHalfK * hf + j, G));
     }
 
     WaveAcc a;
 #pragma unroll
-    for (int blk = 0; blk < kBlocks; ++blk) a.o[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kWaveBlocks; ++j) a.o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     a.m = -INFINITY;
     a.l = 0.f;
 
     for (int w0 = t0; w0 < t1; w0 += kIdxWindow) {
         const int n = min(kIdxWindow, t1 - w0);
         __syncthreads();  // every wave is done with the previous window / previous range
-        {
-            constexpr int kPer = kIdxWindow / kThreads;
-            int32_t v[kPer];
+        if (w0 != t0) load_idx(w0, n);
 #pragma unroll
-            for (int k = 0; k < kPer; ++k) v[k] = (tid + k * kThreads < n) ? P.indices[w0 + tid + k * kThreads] : 0;
-#pragma unroll
-            for (int k = 0; k < kPer; ++k)
-                if (tid + k * kThreads < n) idx[tid + k * kThreads] = v[k];
-        }
+        for (int k = 0; k < kPer; ++k)
+            if (tid + k * kThreads < n) idx[tid + k * kThreads] = iv[k];
         __syncthreads();
         const int nsteps = (n + kStepTokens - 1) / kStepTokens;
-        const int nj = nsteps > wave ? (nsteps - wave + kWaves - 1) / kWaves : 0;  // steps wave + j*kWaves
 #pragma unroll
         for (int d = 0; d < D; ++d)
-            if (d < nj) issue_step<KV>(P, idx, (wave + d * kWaves) * kStepTokens, n, ring + d * L::kStepBytes, lane);
-        for (int j = 0; j < nj; ++j) {
-            if (j + D < nj)
-                issue_step<KV>(P, idx, (wave + (j + D) * kWaves) * kStepTokens, n,
-                               ring + ((j + D) % Fmt<KV>::kRing) * L::kStepBytes, lane);
-            wait_step<KV>(min(D, nj - 1 - j));
-            const int tok0 = (wave + j * kWaves) * kStepTokens;
-            compute_step<KV>(ring + (j % Fmt<KV>::kRing) * L::kStepBytes, qB, qk_scale, n - tok0, lane, a);
+            if (d < nsteps) issue_ops<KV>(P, idx, d * kStepTokens, n, smem + d * L::kStepBytes, lane, wave, kWaves);
+        if (w0 == t0) {
+            // Consume Q^T here, after the first gathers are in flight, so that the
+            // compiler's wait for these loads is placed before the token loop.
+#pragma unroll
+            for (int j = 0; j < kHalfK; ++j) asm volatile("" ::"v"(qB[j]));
+        }
+        for (int s = 0; s < nsteps; ++s) {
+            wait_own<KV>(min(D - 1, nsteps - 1 - s), wave);
+            __syncthreads();  // step s has landed; every wave is done with step s - 1
+            if (s + D < nsteps)
+                issue_ops<KV>(P, idx, (s + D) * kStepTokens, n, smem + ((s + D) % R) * L::kStepBytes, lane, wave,
+                              kWaves);
+            const uint8_t* st = smem + (s % R) * L::kStepBytes;
+            const f32x4 part = hf ? qk_partial<KV, 1>(st, qB, tile, lane) : qk_partial<KV, 0>(st, qB, tile, lane);
+            sbuf[wave * 64 + lane] = part;
+            __syncthreads();
+            f32x4 sc[2];
+            sc[0] = sbuf[0 * 64 + lane] + sbuf[2 * 64 + lane];
+            sc[1] = sbuf[1 * 64 + lane] + sbuf[3 * 64 + lane];
+            softmax_pv<KV>(st, sc, qk_scale, n - s * kStepTokens, lane, wave, a);
         }
     }
 
-    // ---- merge the four waves: M = max_w m_w, O = sum_w 2^(m_w - M) O_w ----
+    // ---- epilogue: every wave holds the same m and l; it writes its own columns ----
     float lt = a.l;
     lt += __shfl_xor(lt, 16);
     lt += __shfl_xor(lt, 32);
-    __syncthreads();  // all waves done with the ring (aliased by sm_o)
-    if (G == 0) {
-        sm_m[wave * kHeads + r] = a.m;
-        sm_l[wave * kHeads + r] = lt;
-    }
-    __syncthreads();
+    const float inv_r = (lt > 0.f) ? kv_scale / lt : 0.f;  // head r
+    const float lse_r = (lt > 0.f) ? (a.m + log2f(lt)) * kLn2 : -INFINITY;
+    float inv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int h = 4 * G + i;
-        float M = sm_m[h];
+    for (int i = 0; i < 4; ++i) inv[i] = __shfl(inv_r, 4 * G + i);  // head 4G+i lives in lane 4G+i
+    if (final) {
+        __bf16* o = P.out + (int64_t)b * kHeads * kDv;
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w * kHeads + h]);
-        const float mw = sm_m[wave * kHeads + h];
-        const float c = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-        float* dst = sm_o + (wave * kHeads + h) * kDv;
+        for (int j = 0; j < kWaveBlocks; ++j) {
+            const int col = dcol<KV>(kWaveBlocks * wave + j, r);
 #pragma unroll
-        for (int blk = 0; blk < kBlocks; ++blk) dst[dcol<KV>(blk, r)] = a.o[blk][i] * c;
-    }
-    __syncthreads();
-    {
-        const int h = tid >> 4, dc = (tid & 15) * 32;
-        float M = sm_m[h];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w * kHeads + h]);
-        float Lsum = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float mw = sm_m[w * kHeads + h];
-            Lsum += (mw == -INFINITY) ? 0.f : fast_exp2(mw - M) * sm_l[w * kHeads + h];
+            for (int i = 0; i < 4; ++i) o[(4 * G + i) * kDv + col] = (__bf16)(a.o[j][i] * inv[i]);
         }
-        const float inv = (Lsum > 0.f) ? kv_scale / Lsum : 0.f;
-        const float lse_nat = (Lsum > 0.f) ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
-        float v[32];
+        if (wave == 0 && G == 0 && P.lse) P.lse[(int64_t)b * kHeads + r] = lse_r;
+    } else {
+        float* o = P.part_o + (int64_t)slot * kHeads * kDv;
 #pragma unroll
-        for (int e = 0; e < 32; ++e) {
-            const int d = dc + e;
-            v[e] = (((sm_o[(0 * kHeads + h) * kDv + d] + sm_o[(1 * kHeads + h) * kDv + d]) +
-                     sm_o[(2 * kHeads + h) * kDv + d]) + sm_o[(3 * kHeads + h) * kDv + d]) * inv;
+        for (int j = 0; j < kWaveBlocks; ++j) {
+            const int col = dcol<KV>(kWaveBlocks * wave + j, r);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[(4 * G + i) * kDv + col] = a.o[j][i] * inv[i];
         }
-        if (final) {
-            __bf16* o = P.out + ((int64_t)b * kHeads + h) * kDv + dc;
-#pragma unroll
-            for (int e = 0; e < 32; e += 8) {
-                bf16x8 pk;
-#pragma unroll
-                for (int k = 0; k < 8; ++k) pk[k] = (__bf16)v[e + k];
-                *reinterpret_cast<bf16x8*>(o + e) = pk;
-            }
-            if ((tid & 15) == 0 && P.lse) P.lse[(int64_t)b * kHeads + h] = lse_nat;
-        } else {
-            float* o = P.part_o + ((int64_t)slot * kHeads + h) * kDv + dc;
-#pragma unroll
-            for (int e = 0; e < 32; e += 4) *reinterpret_cast<f32x4*>(o + e) = f32x4{v[e], v[e + 1], v[e + 2], v[e + 3]};
-            if ((tid & 15) == 0) P.part_lse[(int64_t)slot * kHeads + h] = lse_nat;
-        }
+        if (wave == 0 && G == 0) P.part_lse[(int64_t)slot * kHeads + r] = lse_r;
     }
 }
 
 template <int KV>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void split_kernel(Params P) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[Layout<KV>::kBytes];
     const int b = blockIdx.x / P.nsplit, s = blockIdx.x % P.nsplit;
@@ -555,7 +565,7 @@ __device__ __forceinline__ int share_of(int64_t t, int64_t T, int64_t G) { retur
 __device__ __forceinline__ int64_t share_start(int64_t p, int64_t T, int64_t G) { return p * T / G; }
 
 template <int KV>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void persistent_kernel(Params P) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[Layout<KV>::kBytes];
     const int64_t T = P.total, Gn = P.grid;
@@ -582,6 +592,9 @@ void persistent_kernel(Params P) {
 // Stage 2: out[b,h] = sum_s w_s O_s / sum_s w_s, w_s = exp(lse_s - max lse),
 // lse = max + ln sum w_s; empty partials (lse = -inf) carry no weight.
 // (Submission 703488, `_reduce_splitk_parallel_*`.)
+// One workgroup per (sequence, head, 128-column chunk); its 256 threads are
+// 32 column quads x 8 partial groups, so the loads of all partials are in
+// flight together; the 8 group sums are added in LDS in a fixed order.
 struct CombineParams {
     const float* part_o;
     const float* part_lse;
@@ -595,54 +608,82 @@ struct CombineParams {
     int total;
 };
 
-__global__ __launch_bounds__(128) void combine_kernel(CombineParams C) {
-    const int h = blockIdx.x & 15, b = blockIdx.x >> 4;
-    const int d = threadIdx.x * 4;
-    int first, last, base;
+constexpr int kCombThreads = 256;
+constexpr int kCombCols = 128;
+constexpr int kCombGroups = kCombThreads / (kCombCols / 4);  // 8
+
+__global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineParams C) {
+    __shared__ f32x4 s_acc[kCombGroups][kCombCols / 4];
+    __shared__ float s_red[kCombThreads / 64];
+    __shared__ float s_w[kCombGroups];
+    const int chunk = blockIdx.x & 3, h = (blockIdx.x >> 2) & 15, b = blockIdx.x >> 6;
+    const int tid = threadIdx.x, quad = tid & 31, grp = tid >> 5;
+    const int d = chunk * kCombCols + quad * 4;
+    // partial k of this sequence lives in slot base + first + k, for k < count
+    int first = 0, count = 0, base = 0;
     if (C.mode == 0) {
-        first = 0;
-        last = C.nsplit - 1;
+        count = C.nsplit;
         base = b * C.nsplit;
     } else {
         const int s = C.indptr[b], e = C.indptr[b + 1];
         if (e > s) {
             first = share_of(s, C.total, C.grid);
-            last = share_of(e - 1, C.total, C.grid);
+            const int last = share_of(e - 1, C.total, C.grid);
             if (first == last) return;  // one workgroup held the whole sequence and wrote it
-        } else {
-            first = 0;
-            last = -1;
+            count = last - first + 1;
         }
         base = b;  // slot of workgroup p for sequence b is p + b
     }
+    auto part_lse = [&](int k) -> float {
+        const int p = first + k;
+        if (C.mode == 1 && share_start(p, C.total, C.grid) == share_start(p + 1, C.total, C.grid))
+            return -INFINITY;  // empty share: wrote nothing
+        return C.part_lse[(int64_t)(base + p) * kHeads + h];
+    };
+    // M = max_k lse_k over the workgroup
     float M = -INFINITY;
-    for (int p = first; p <= last; ++p) {
-        if (C.mode == 1 && share_start(p, C.total, C.grid) == share_start(p + 1, C.total, C.grid)) continue;
-        M = fmaxf(M, C.part_lse[(int64_t)(base + p) * kHeads + h]);
-    }
+    for (int k = tid; k < count; k += kCombThreads) M = fmaxf(M, part_lse(k));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    if ((tid & 63) == 0) s_red[tid >> 6] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    __syncthreads();
+    // per group: sum over its partials k = grp, grp + 8, ... of w_k O_k and w_k
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float W = 0.f;
     if (M != -INFINITY) {
-        for (int p = first; p <= last; ++p) {
-            if (C.mode == 1 && share_start(p, C.total, C.grid) == share_start(p + 1, C.total, C.grid)) continue;
-            const int64_t slot = base + p;
-            const float l = C.part_lse[slot * kHeads + h];
+#pragma unroll 4
+        for (int k = grp; k < count; k += kCombGroups) {
+            const float l = part_lse(k);
             if (l == -INFINITY) continue;
             const float w = __expf(l - M);
             W += w;
-            const f32x4 o = *reinterpret_cast<const f32x4*>(C.part_o + (slot * kHeads + h) * kDv + d);
+            const f32x4 o = *reinterpret_cast<const f32x4*>(C.part_o + ((int64_t)(base + first + k) * kHeads + h) * kDv + d);
             acc += w * o;
         }
     }
-    const float inv = (W > 0.f) ? 1.f / W : 0.f;
-    bf16x4 pk;
+    s_acc[grp][quad] = acc;
+    if (quad == 0) s_w[grp] = W;  // W is the same in every thread of a group
+    __syncthreads();
+    if (grp == 0) {
+        f32x4 t = s_acc[0][quad];
+        float Wt = s_w[0];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(acc[e] * inv);
-    *reinterpret_cast<bf16x4*>(C.out + ((int64_t)b * kHeads + h) * kDv + d) = pk;
-    if (threadIdx.x == 0 && C.lse) C.lse[(int64_t)b * kHeads + h] = (W > 0.f) ? M + logf(W) : -INFINITY;
+        for (int g = 1; g < kCombGroups; ++g) {
+            t += s_acc[g][quad];
+            Wt += s_w[g];
+        }
+        const float inv = (Wt > 0.f) ? 1.f / Wt : 0.f;
+        bf16x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(t[e] * inv);
+        *reinterpret_cast<bf16x4*>(C.out + ((int64_t)b * kHeads + h) * kDv + d) = pk;
+        if (quad == 0 && chunk == 0 && C.lse) C.lse[(int64_t)b * kHeads + h] = (Wt > 0.f) ? M + logf(Wt) : -INFINITY;
+    }
 }
 
-// Decode check: rows -> fp32 through the stage-1 staging (issue_step) and the
+// Decode check: rows -> fp32 through the stage-1 staging (issue_ops) and the
 // two decode routines of the attention kernel. path 0: every column through
 // the score operand (qk_operand); path 1: columns 0..511 through the value
 // operand (pv_operand / pv_operand_fp4), columns 512..575 through path 0.
@@ -656,7 +697,7 @@ __global__ __launch_bounds__(64) void dequant_kernel(Params P, int64_t rows, int
     const int n = (int)min<int64_t>(kStepTokens, rows - row0);
     if (lane < kStepTokens) idx[lane] = (int32_t)(row0 + min(lane, n - 1));
     __syncthreads();
-    issue_step<KV>(P, idx, 0, n, step, lane);
+    issue_ops<KV>(P, idx, 0, n, step, lane, 0, 1);
     wait_vmcnt<0>();
     __syncthreads();
     float mul = 1.0f;
@@ -737,7 +778,7 @@ static int launch(const mla_plan_info& plan, const Params& P, hipStream_t stream
         C.nsplit = plan.num_splits;
         C.grid = plan.grid;
         C.total = P.total;
-        hipLaunchKernelGGL(combine_kernel, dim3(kHeads * P.batch), dim3(128), 0, stream, C);
+        hipLaunchKernelGGL(combine_kernel, dim3(kHeads * 4 * P.batch), dim3(kCombThreads), 0, stream, C);
         if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
     }
     return MLA_OK;

@@ -4,7 +4,7 @@
 // Two grid shapes are planned:
 //   split-K     (splits x batch) workgroups; split s of sequence b covers
 //               tokens [s*chunk, min(L_b, (s+1)*chunk)), chunk = ceil(L_b /
-//               splits) rounded up to the 16-token wave step. One partial
+//               splits) rounded up to the 32-token workgroup step. One partial
 //               slot per (b, s); a combine launch merges them when splits > 1.
 //               (Flash-decoding split-K: the split partial plus log-sum-exp
 //               merge of amd-mixed-mla submission 593653, `_flash_fp8_split_s1`
@@ -36,13 +36,13 @@ size_t partial_lse_offset(int num_partials) {
     return ((o + 255) / 256) * 256;
 }
 
-// Split count for split-K: enough workgroups to give every compute unit one,
-// but never fewer than kMinTokensPerWg tokens per workgroup (the four waves of
-// a workgroup each want at least one 16-token step), and at most kMaxSplits.
-int heuristic_splits(int batch, int64_t total_kv) {
+// Split count for split-K: enough workgroups to fill every compute unit, but
+// never fewer than kMinTokensPerWg tokens per workgroup (each split also costs
+// a 32 KB partial written and read back), and at most kMaxSplits.
+int heuristic_splits(int batch, int64_t total_kv, int kv_dtype) {
     if (batch <= 0) return 1;
     int64_t avg = cdiv(total_kv, batch);
-    int64_t s = cdiv(kNumCUs * kWgsPerCU, batch);
+    int64_t s = cdiv((int64_t)kNumCUs * wgs_per_cu(kv_dtype), batch);
     int64_t by_len = avg / kMinTokensPerWg;
     if (s > by_len) s = by_len;
     if (s > kMaxSplits) s = kMaxSplits;
@@ -52,8 +52,8 @@ int heuristic_splits(int batch, int64_t total_kv) {
 
 // Persistent grid: one workgroup per compute unit, fewer when there are not
 // enough tokens to give each at least kMinTokensPerWg.
-int heuristic_grid(int64_t total_kv) {
-    int64_t g = (int64_t)kNumCUs * kWgsPerCU;
+int heuristic_grid(int64_t total_kv, int kv_dtype) {
+    int64_t g = (int64_t)kNumCUs * wgs_per_cu(kv_dtype);
     int64_t by_len = total_kv / kMinTokensPerWg;
     if (g > by_len) g = by_len;
     if (g < 1) g = 1;
@@ -64,9 +64,9 @@ int heuristic_grid(int64_t total_kv) {
 // split grid lands on a whole number of workgroups per compute unit; the
 // persistent grid for large, uneven shapes where the split grid would leave
 // compute units idle.
-static bool prefer_persistent(int batch, int64_t total_kv) {
+static bool prefer_persistent(int batch, int64_t total_kv, int kv_dtype) {
     if (total_kv < (int64_t)kNumCUs * kPersistentMinTokensPerCU) return false;
-    int s = heuristic_splits(batch, total_kv);
+    int s = heuristic_splits(batch, total_kv, kv_dtype);
     int64_t wgs = (int64_t)s * batch;
     return (wgs % kNumCUs) != 0;
 }
@@ -94,9 +94,9 @@ int make_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_inf
         p->workspace_bytes = 0;
         return MLA_OK;
     }
-    bool persistent = force_pers || (!force_split && forced_splits == 0 && prefer_persistent(batch, total_kv));
+    bool persistent = force_pers || (!force_split && forced_splits == 0 && prefer_persistent(batch, total_kv, kv_dtype));
     if (persistent) {
-        int g = forced_grid ? forced_grid : heuristic_grid(total_kv);
+        int g = forced_grid ? forced_grid : heuristic_grid(total_kv, kv_dtype);
         p->mode = 1;
         p->num_splits = 0;
         p->grid = g;
@@ -104,7 +104,7 @@ int make_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_inf
         p->combine = 1;
         p->workspace_bytes = partial_bytes(p->num_partials);
     } else {
-        int s = forced_splits ? forced_splits : heuristic_splits(batch, total_kv);
+        int s = forced_splits ? forced_splits : heuristic_splits(batch, total_kv, kv_dtype);
         p->mode = 0;
         p->num_splits = s;
         p->grid = s * batch;

@@ -14,16 +14,18 @@ constexpr int kDqk = MLA_QK_DIM;
 constexpr int kDv = MLA_V_DIM;
 
 constexpr int kNumCUs = 256;          // MI355X compute units
-constexpr int kWgsPerCU = 1;          // stage-1 workgroups resident per CU (LDS/VGPR bound)
 constexpr int kWaves = 4;             // waves per stage-1 workgroup
-constexpr int kStep = 16;             // tokens per wave step (MFMA M dimension)
-constexpr int kMinTokensPerWg = kWaves * kStep;
+constexpr int kStepTokens = 32;       // tokens per workgroup step (two 16-token MFMA tiles)
+constexpr int kMinTokensPerWg = 4 * kStepTokens;  // enough steps for the gather pipeline to overlap
 constexpr int kMaxSplits = 64;
 constexpr int kPersistentMinTokensPerCU = 1024;
 
+// Stage-1 workgroups resident per compute unit (bound by the LDS ring size).
+constexpr int wgs_per_cu(int kv_dtype) { return kv_dtype == MLA_KV_BF16 ? 1 : 2; }
+
 int make_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_info* p);
-int heuristic_splits(int batch, int64_t total_kv);
-int heuristic_grid(int64_t total_kv);
+int heuristic_splits(int batch, int64_t total_kv, int kv_dtype);
+int heuristic_grid(int64_t total_kv, int kv_dtype);
 size_t partial_lse_offset(int num_partials);
 
 }  // namespace mla

@@ -76,9 +76,12 @@ def test_heuristic_plan_invariants(mla, B, L, kv_dtype):
 
 
 def test_heuristic_fills_the_chip_for_the_measured_shapes(mla):
-    for B, L in [(32, 1024), (4, 8192), (64, 8192), (32, 8192), (256, 1024)]:
-        p = mla.mla_decode_plan(B, B * L, 1)
-        assert p.grid == 256, (B, L, p)
+    # fp8 and MXFP4 stage-1 workgroups fit two per compute unit, bf16 one: the
+    # grid is a whole number of workgroups per CU, between one and that many.
+    for fmt, per_cu in [(0, 1), (1, 2), (2, 2)]:
+        for B, L in [(32, 1024), (4, 8192), (64, 8192), (32, 8192), (256, 1024)]:
+            p = mla.mla_decode_plan(B, B * L, fmt)
+            assert p.grid % 256 == 0 and 256 <= p.grid <= 256 * per_cu, (fmt, B, L, p)
 
 
 def test_forced_plans(mla):
@@ -89,7 +92,7 @@ def test_forced_plans(mla):
     p = mla.mla_decode_plan(4, 4000, 2, mla.flags_for(persistent=True, grid=37))
     assert (p.mode, p.grid, p.num_partials, p.combine) == (1, 37, 40, 1)
     p = mla.mla_decode_plan(4, 4000, 2, mla.flags_for(persistent=True))
-    assert p.mode == 1 and p.grid == 4000 // 64
+    assert p.mode == 1 and p.grid == 4000 // 128  # at least 128 tokens per workgroup
 
 
 @pytest.mark.parametrize("args", [
