@@ -84,14 +84,20 @@ struct Params {
 };
 
 // ---------------------------------------------------------------------------
-// Cache formats: staging layout of one 16-row tile in LDS.
+// Cache formats: staging layout of one 16-row tile in LDS. The gather of a
+// tile is split in two halves (hi = 0, 1), each issued by one wave; every
+// lane of a half fetches parts of the row of token r = lane % 16, so the
+// issuing wave reads one row index per step.
 //   codes: load u (0 <= u < kCodeLoads) is one 16-byte DMA per lane; lane
 //          (G, r) = (lane / 16, lane % 16) brings bytes 64u + 16G .. +15 of
-//          tile row r to tile + 1024u + 16 lane.
-//   MXFP4: the 32 RoPE bytes of each row (bytes 256..287) are two dword DMAs
-//          into a [16 rows][8 dwords] block at tile + 4096; the step's e8m0
-//          scales are byte DMAs into one dword per (block, token):
-//          step + 2 * kTileBytes + 4 (32 block + token).
+//          tile row r to tile + 1024u + 16 lane. Half hi issues u = hi, hi+2, ...
+//   MXFP4: the 32 RoPE bytes of each row (bytes 256..287) are one 16-byte DMA
+//          on lanes 0..31 (lane (c, r) brings bytes 256 + 16c .. +15 of row r
+//          to tile + kRopeOff + 16 lane); the 18 e8m0 codes of each row are
+//          two-byte DMAs, load v bringing codes 2p, 2p+1, p = 4v + G, of row
+//          r into the low half of the dword at tile + kScaleOff + 256 v + 4 lane
+//          (load 2 on lanes 0..15 only). Half 0 issues codes 0, 2 and scale
+//          loads 0, 2; half 1 codes 1, 3, the RoPE load and scale load 1.
 // ---------------------------------------------------------------------------
 template <int KV>
 struct Fmt;
@@ -100,42 +106,42 @@ struct Fmt<MLA_KV_BF16> {
     static constexpr int kRowBytes = 2 * kDqk;
     static constexpr int kCodeLoads = 18;
     static constexpr int kTileBytes = 18 * 1024;
-    static constexpr int kScaleBytes = 0;
     static constexpr int kRing = 3;      // steps resident in the workgroup's LDS ring
-    static constexpr int kOps = 36;      // LDS-DMA instructions per step
     static constexpr int kWgsPerCU = 1;  // LDS bound
+    static constexpr int ops(int hi) { return 9 + 0 * hi; }  // LDS-DMA instructions of one tile half
 };
 template <>
 struct Fmt<MLA_KV_FP8_E4M3> {
     static constexpr int kRowBytes = kDqk;
     static constexpr int kCodeLoads = 9;
     static constexpr int kTileBytes = 9 * 1024;
-    static constexpr int kScaleBytes = 0;
     static constexpr int kRing = 3;
-    static constexpr int kOps = 18;
     static constexpr int kWgsPerCU = 2;
+    static constexpr int ops(int hi) { return hi ? 4 : 5; }
 };
 template <>
 struct Fmt<MLA_KV_MXFP4> {
     static constexpr int kRowBytes = kDqk / 2;
     static constexpr int kCodeLoads = 4;
-    static constexpr int kTileBytes = 4 * 1024 + 512;
-    static constexpr int kScaleBytes = 18 * kStepTokens * 4;
+    static constexpr int kRopeOff = 4 * 1024;
+    static constexpr int kScaleOff = kRopeOff + 512;
+    static constexpr int kTileBytes = kScaleOff + 3 * 256;
     static constexpr int kRing = 4;
-    static constexpr int kOps = 2 * (4 + 2) + 9;
     static constexpr int kWgsPerCU = 2;
+    static constexpr int ops(int hi) { return 4 + 0 * hi; }
 };
 
 // LDS of one stage-1 workgroup: the ring of staged steps, the exchange buffer
 // for the four waves' partial scores, and the index window.
 template <int KV>
 struct Layout {
-    static constexpr int kStepBytes = 2 * Fmt<KV>::kTileBytes + Fmt<KV>::kScaleBytes;
+    static constexpr int kStepBytes = 2 * Fmt<KV>::kTileBytes;
     static constexpr int kRingBytes = Fmt<KV>::kRing * kStepBytes;
     static constexpr int kSbufOff = kRingBytes;
     static constexpr int kIdxOff = kSbufOff + kWaves * 64 * 16;
     static constexpr int kBytes = kIdxOff + kIdxWindow * 4;
     static_assert(kBytes * Fmt<KV>::kWgsPerCU <= 160 * 1024, "stage-1 LDS exceeds 160 KiB per CU");
+    static_assert(Fmt<KV>::kTileBytes % 16 == 0, "tiles stay 16-byte aligned");
 };
 
 // First score dim of the eight held by lane group G in k-step ks. Q^T is
@@ -160,7 +166,7 @@ __device__ __forceinline__ int tau(int G, int j) { return j < 4 ? 4 * G + j : 16
 
 // LDS-DMA loads: lane L's `size` bytes from its global address g land at LDS
 // byte lds + size * L (size 16), or in the dword at lds + 4 L, zero-extended
-// (sizes 1 and 4). Issued from inline assembly so that the compiler, which
+// (sizes 2 and 4). Issued from inline assembly so that the compiler, which
 // would otherwise drain every outstanding load before each LDS read it cannot
 // prove disjoint, leaves the ordering to the explicit waits below. m0 (the
 // LDS base operand) is restored before the statement ends.
@@ -169,14 +175,9 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
                  : "=&s"(save) : "v"(g), "s"(lds) : "memory");
 }
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+__device__ __forceinline__ void dma2(const void* g, uint32_t lds) {
     uint32_t save;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
-                 : "=&s"(save) : "v"(g), "s"(lds) : "memory");
-}
-__device__ __forceinline__ void dma1(const void* g, uint32_t lds) {
-    uint32_t save;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_ubyte %1, off\n\ts_mov_b32 m0, %0"
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_ushort %1, off\n\ts_mov_b32 m0, %0"
                  : "=&s"(save) : "v"(g), "s"(lds) : "memory");
 }
 // Wave-uniform 32-bit LDS address of a pointer into shared memory.
@@ -190,51 +191,39 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
-// LDS-DMA instruction `op` (0 <= op < kOps) of the step starting at window
-// token tok0, written into `step`. Tokens at or beyond n re-read the last
-// valid row (always in bounds). The ops of a step are spread over the waves
-// of the workgroup: wave w issues ops w, w + nw, ...
-//   bf16 / fp8: op = 18t + u (bf16) or 9t + u (fp8): code load u of tile t.
-//   MXFP4: op < 12: 6t + k, code load k < 4 or RoPE dword load k - 4 of tile t;
-//          op >= 12: e8m0 scale load op - 12 (two blocks x 32 tokens each).
-template <int KV>
-__device__ __forceinline__ void issue_op(const Params& P, const int32_t* idx, int tok0, int n, uint8_t* step,
-                                         int lane, int op) {
+// The LDS-DMA loads of half `hi` of one tile (layout above). `row` is the
+// cache row of token lane % 16 of the tile; `tile` its LDS staging area.
+template <int KV, int HI>
+__device__ __forceinline__ void issue_half(const Params& P, int64_t row, uint8_t* tile, int lane) {
     constexpr int RB = Fmt<KV>::kRowBytes;
-    constexpr int TB = Fmt<KV>::kTileBytes;
-    const int G = lane >> 4, r = lane & 15;
+    const int G = lane >> 4;
+    const uint8_t* src = P.kv + row * RB + 16 * G;
     if constexpr (KV != MLA_KV_MXFP4) {
-        const int t = op / Fmt<KV>::kCodeLoads, u = op % Fmt<KV>::kCodeLoads;
-        const int64_t row = idx[min(tok0 + kTile * t + r, n - 1)];
-        dma16(P.kv + row * RB + 64 * u + 16 * G, lds_addr(step + t * TB + 1024 * u));
-    } else if (op < 12) {
-        const int t = op / 6, k = op % 6;
-        if (k < 4) {
-            const int64_t row = idx[min(tok0 + kTile * t + r, n - 1)];
-            dma16(P.kv + row * RB + 64 * k + 16 * G, lds_addr(step + t * TB + 1024 * k));
-        } else {
-            const int v = k - 4, sl = 64 * v + lane;  // (row sl / 8, dword sl % 8) of the RoPE block
-            const int64_t row = idx[min(tok0 + kTile * t + (sl >> 3), n - 1)];
-            dma4(P.kv + row * RB + 256 + 4 * (sl & 7), lds_addr(step + t * TB + 4096 + 256 * v));
-        }
+#pragma unroll
+        for (int u = HI; u < Fmt<KV>::kCodeLoads; u += 2) dma16(src + 64 * u, lds_addr(tile + 1024 * u));
     } else {
-        // dword 64 v + lane of the scale block = (block 2v + lane / 32, token lane % 32)
-        const int v = op - 12;
-        const uint8_t* sc = reinterpret_cast<const uint8_t*>(P.kv_scales);
-        const int64_t row = idx[min(tok0 + (lane & 31), n - 1)];
-        dma1(sc + row * MLA_MX_SCALES_PER_ROW + 2 * v + (lane >> 5), lds_addr(step + 2 * TB + 256 * v));
+        dma16(src + 64 * HI, lds_addr(tile + 1024 * HI));
+        dma16(src + 64 * (HI + 2), lds_addr(tile + 1024 * (HI + 2)));
+        const uint8_t* sc = reinterpret_cast<const uint8_t*>(P.kv_scales) + row * MLA_MX_SCALES_PER_ROW + 2 * G;
+        if (HI == 0) {
+            dma2(sc, lds_addr(tile + Fmt<KV>::kScaleOff));
+            if (lane < 16) dma2(sc + 16, lds_addr(tile + Fmt<KV>::kScaleOff + 512));
+        } else {
+            if (lane < 32) dma16(P.kv + row * RB + 256 + 16 * G, lds_addr(tile + Fmt<KV>::kRopeOff));
+            dma2(sc + 8, lds_addr(tile + Fmt<KV>::kScaleOff + 256));
+        }
     }
 }
 
 template <int KV>
-__device__ __forceinline__ void issue_ops(const Params& P, const int32_t* idx, int tok0, int n, uint8_t* step,
-                                          int lane, int first, int stride) {
-    for (int op = first; op < Fmt<KV>::kOps; op += stride) issue_op<KV>(P, idx, tok0, n, step, lane, op);
+__device__ __forceinline__ void issue_half(const Params& P, int64_t row, uint8_t* tile, int lane, int hi) {
+    if (hi) issue_half<KV, 1>(P, row, tile, lane);
+    else issue_half<KV, 0>(P, row, tile, lane);
 }
 
-// e8m0 code -> fp32 scale operand of the scaled converts (the code is the
-// exponent field: 2^(code - 127)).
-__device__ __forceinline__ float e8m0_scale(uint32_t code) { return __uint_as_float(code << 23); }
+// e8m0 code in bits sh..sh+7 of w -> fp32 scale operand of the scaled
+// converts (the code is the exponent field: 2^(code - 127)).
+__device__ __forceinline__ float e8m0_scale(uint32_t w, int sh) { return __uint_as_float(((w >> sh) & 0xffu) << 23); }
 
 __device__ __forceinline__ bf16x8 join(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
     bf16x8 o;
@@ -269,17 +258,22 @@ __device__ __forceinline__ bf16x8 qk_operand(const uint8_t* step, int t, int ks,
         const u32x4 w = *reinterpret_cast<const u32x4*>(tile + 1024 * (ks >> 1) + 16 * lane);
         return (ks & 1) ? fp8x8_to_bf16(w[2], w[3]) : fp8x8_to_bf16(w[0], w[1]);
     } else {
+        // e8m0 block k of row r is byte k & 1 of the dword at scale index 16 (k / 2) + r
         const int G = lane >> 4, r = lane & 15;
-        const uint32_t* scl = reinterpret_cast<const uint32_t*>(step + 2 * Fmt<KV>::kTileBytes);
-        uint32_t dw, blk;
-        if (ks < 16) {
+        const uint32_t* scl = reinterpret_cast<const uint32_t*>(tile + Fmt<KV>::kScaleOff);
+        uint32_t dw, sw;
+        int sh;
+        if (ks < 16) {  // dims 128 (ks / 4) + 32 G + 8 (ks % 4) ..: block 4 (ks / 4) + G
             dw = *reinterpret_cast<const uint32_t*>(tile + 1024 * (ks >> 2) + 16 * lane + 4 * (ks & 3));
-            blk = 4 * (ks >> 2) + G;
-        } else {
-            dw = *reinterpret_cast<const uint32_t*>(tile + 4096 + 4 * (8 * r + 2 * G + (ks - 16)));
-            blk = 16 + (G >> 1);
+            sw = scl[16 * (2 * (ks >> 2) + (G >> 1)) + r];
+            sh = 8 * (G & 1);
+        } else {        // RoPE dims 512 + 16 G + 8 (ks - 16) ..: block 16 + G / 2
+            dw = *reinterpret_cast<const uint32_t*>(tile + Fmt<KV>::kRopeOff + 16 * (16 * (G >> 1) + r) +
+                                                    8 * (G & 1) + 4 * (ks - 16));
+            sw = scl[16 * 8 + r];
+            sh = 8 * (G >> 1);
         }
-        return fp4x8_to_bf16(dw, e8m0_scale(scl[32 * blk + kTile * t + r]));
+        return fp4x8_to_bf16(dw, e8m0_scale(sw, sh));
     }
 }
 
@@ -311,12 +305,13 @@ __device__ __forceinline__ bf16x8 pv_operand(const uint8_t* step, int c, int lan
     }
 }
 
-// Byte i of dw (two e2m1 codes of one token) scaled by 2^(sc[i] - 127) -> bf16x2.
-__device__ __forceinline__ void cvt_fp4_bytes(uint32_t dw, u32x4 sc, uint32_t* c) {
-    c[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, e8m0_scale(sc[0]), 0));
-    c[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, e8m0_scale(sc[1]), 1));
-    c[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, e8m0_scale(sc[2]), 2));
-    c[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, e8m0_scale(sc[3]), 3));
+// Byte i of dw (two e2m1 codes of one token) scaled by 2^(e - 127), e = bits
+// sh..sh+7 of sc[i] -> bf16x2.
+__device__ __forceinline__ void cvt_fp4_bytes(uint32_t dw, u32x4 sc, int sh, uint32_t* c) {
+    c[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, e8m0_scale(sc[0], sh), 0));
+    c[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, e8m0_scale(sc[1], sh), 1));
+    c[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, e8m0_scale(sc[2], sh), 2));
+    c[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, e8m0_scale(sc[3], sh), 3));
 }
 
 // Value operands of MXFP4 block b (32 columns): lane (G, n) receives byte n of
@@ -328,11 +323,13 @@ __device__ __forceinline__ void pv_operand_fp4(const uint8_t* step, int b, int l
     const int tk = tau(G, j >> 1);
     const uint8_t* a = step + (tk >> 4) * TB + 1024 * (b >> 2) + 16 * (16 * (b & 3) + (tk & 15)) + 8 * (j & 1);
     const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)a);
-    const u32x4* scl = reinterpret_cast<const u32x4*>(step + 2 * TB + 4 * (32 * b));
-    const u32x4 s0 = scl[G], s1 = scl[4 + G];  // tokens 4G..4G+3 and 16+4G..16+4G+3
+    // scale dwords 16 (b / 2) + 4G .. +3 of each tile: tokens 4G..4G+3, code in byte b & 1
+    const int q4 = 4 * (b >> 1) + G, sh = 8 * (b & 1);
+    const u32x4 s0 = reinterpret_cast<const u32x4*>(step + Fmt<MLA_KV_MXFP4>::kScaleOff)[q4];
+    const u32x4 s1 = reinterpret_cast<const u32x4*>(step + TB + Fmt<MLA_KV_MXFP4>::kScaleOff)[q4];
     uint32_t c[8];
-    cvt_fp4_bytes((uint32_t)w[0], s0, c);
-    cvt_fp4_bytes((uint32_t)w[1], s1, c + 4);
+    cvt_fp4_bytes((uint32_t)w[0], s0, sh, c);
+    cvt_fp4_bytes((uint32_t)w[1], s1, sh, c + 4);
     u32x4 e, o;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -341,6 +338,22 @@ __device__ __forceinline__ void pv_operand_fp4(const uint8_t* step, int b, int l
     }
     even = __builtin_bit_cast(bf16x8, e);
     odd = __builtin_bit_cast(bf16x8, o);
+}
+
+// Max and sum over the four lane groups of column r (lanes r, r+16, r+32, r+48),
+// with the gfx950 lane swaps: permlane32_swap pairs lane l with l ^ 32 and
+// permlane16_swap lane l with l ^ 16, so two swaps cover the group.
+__device__ __forceinline__ float group_max4(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float group_sum4(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
 // 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
@@ -387,8 +400,7 @@ __device__ __forceinline__ void softmax_pv(const uint8_t* step, const f32x4 (&s)
         x[j] = (tau(G, j) < nvalid) ? s[j >> 2][j & 3] * qk_scale : -INFINITY;
         mx = fmaxf(mx, x[j]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = group_max4(mx);
     const float m_new = fmaxf(a.m, mx);
     if (__any(m_new > a.m + kRescaleThresh)) {
         const float alpha = (a.m == -INFINITY) ? 0.f : fast_exp2(a.m - m_new);
@@ -425,24 +437,23 @@ __device__ __forceinline__ void softmax_pv(const uint8_t* step, const f32x4 (&s)
     }
 }
 
-// Wait until this wave's own LDS-DMA ops of all but the last `groups` issued
-// steps have landed. Wave w issues ops w, w + 4, ... of every step.
+// Wait until this wave's own LDS-DMA loads of all but the last `groups` issued
+// steps have landed. The wave issues half `hi` of one tile per step.
 template <int KV>
-__device__ __forceinline__ void wait_own(int groups, int wave) {
-    constexpr int kHi = (Fmt<KV>::kOps + kWaves - 1) / kWaves;
-    constexpr int kLo = Fmt<KV>::kOps / kWaves;
-    const bool hi = wave < Fmt<KV>::kOps % kWaves;
+__device__ __forceinline__ void wait_own(int groups, int hi) {
+    constexpr int k0 = Fmt<KV>::ops(0), k1 = Fmt<KV>::ops(1);
     if (groups <= 0) wait_vmcnt<0>();
-    else if (groups == 1) { if (hi) wait_vmcnt<kHi>(); else wait_vmcnt<kLo>(); }
-    else { if (hi) wait_vmcnt<2 * kHi>(); else wait_vmcnt<2 * kLo>(); }
+    else if (groups == 1) { if (hi) wait_vmcnt<k1>(); else wait_vmcnt<k0>(); }
+    else { if (hi) wait_vmcnt<2 * k1>(); else wait_vmcnt<2 * k0>(); }
 }
 
 // Attend tokens [t0, t1) of sequence b with the whole workgroup and write the
 // result: final bf16 output + lse when `final`, else partial slot `slot`.
-// The four waves work on the same 32-token step: wave w computes the scores of
-// tile w % 2 over score k-steps 9 (w / 2) .. +8, the partial scores are summed
-// through LDS in a fixed order, and every wave then runs the same softmax and
-// accumulates P . V for its own 128 output columns.
+// The four waves work on the same 32-token step: wave w gathers half w / 2 of
+// tile w % 2 and computes the scores of tile w % 2 over score k-steps
+// 9 (w / 2) .. +8, the partial scores are summed through LDS in a fixed order,
+// and every wave then runs the same softmax and accumulates P . V for its own
+// 128 output columns.
 template <int KV>
 __device__ void run_wg(const Params& P, uint8_t* smem, int b, int t0, int t1, bool final, int slot) {
     using L = Layout<KV>;
@@ -450,7 +461,7 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int t0, int t1, bo
     constexpr int D = R - 1;  // steps issued ahead of the one computed
     static_assert(D >= 1 && D <= 3, "ring depth");
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, G = lane >> 4, r = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, G = lane >> 4, r = lane & 15;
     const int tile = wave & 1, hf = wave >> 1;
     int32_t* idx = reinterpret_cast<int32_t*>(smem + L::kIdxOff);
     f32x4* sbuf = reinterpret_cast<f32x4*>(smem + L::kSbufOff);
@@ -475,6 +486,12 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int t0, int t1, bo
         for (int j = 0; j < kHalfK; ++j)
             qB[j] = *reinterpret_cast<const bf16x8*>(qrow + dbase<KV>(kHalfK * hf + j, G));
     }
+    // Consume Q^T and the scale here: the compiler's wait for these loads must
+    // not land inside the token loop, where the count it waits for would also
+    // drain the gathers in flight (it does not see the LDS-DMA loads).
+#pragma unroll
+    for (int j = 0; j < kHalfK; ++j) asm volatile("" ::"v"(qB[j]));
+    asm volatile("" ::"v"(qk_scale), "v"(kv_scale));
 
     WaveAcc a;
 #pragma unroll
@@ -491,21 +508,19 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int t0, int t1, bo
             if (tid + k * kThreads < n) idx[tid + k * kThreads] = iv[k];
         __syncthreads();
         const int nsteps = (n + kStepTokens - 1) / kStepTokens;
+        // This wave's half of tile `tile` of step i into ring slot i % R; tokens
+        // at or beyond n re-read the last valid row (always in bounds).
+        auto issue_step = [&](int i) {
+            const int64_t row = idx[min(i * kStepTokens + kTile * tile + r, n - 1)];
+            issue_half<KV>(P, row, smem + (i % R) * L::kStepBytes + tile * Fmt<KV>::kTileBytes, lane, hf);
+        };
 #pragma unroll
         for (int d = 0; d < D; ++d)
-            if (d < nsteps) issue_ops<KV>(P, idx, d * kStepTokens, n, smem + d * L::kStepBytes, lane, wave, kWaves);
-        if (w0 == t0) {
-            // Consume Q^T here, after the first gathers are in flight, so that the
-            // compiler's wait for these loads is placed before the token loop.
-#pragma unroll
-            for (int j = 0; j < kHalfK; ++j) asm volatile("" ::"v"(qB[j]));
-        }
+            if (d < nsteps) issue_step(d);
         for (int s = 0; s < nsteps; ++s) {
-            wait_own<KV>(min(D - 1, nsteps - 1 - s), wave);
+            wait_own<KV>(min(D - 1, nsteps - 1 - s), hf);
             __syncthreads();  // step s has landed; every wave is done with step s - 1
-            if (s + D < nsteps)
-                issue_ops<KV>(P, idx, (s + D) * kStepTokens, n, smem + ((s + D) % R) * L::kStepBytes, lane, wave,
-                              kWaves);
+            if (s + D < nsteps) issue_step(s + D);
             const uint8_t* st = smem + (s % R) * L::kStepBytes;
             const f32x4 part = hf ? qk_partial<KV, 1>(st, qB, tile, lane) : qk_partial<KV, 0>(st, qB, tile, lane);
             sbuf[wave * 64 + lane] = part;
@@ -518,9 +533,7 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int t0, int t1, bo
     }
 
     // ---- epilogue: every wave holds the same m and l; it writes its own columns ----
-    float lt = a.l;
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = group_sum4(a.l);
     const float inv_r = (lt > 0.f) ? kv_scale / lt : 0.f;  // head r
     const float lse_r = (lt > 0.f) ? (a.m + log2f(lt)) * kLn2 : -INFINITY;
     float inv[4];
@@ -548,7 +561,7 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int t0, int t1, bo
 }
 
 template <int KV>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Fmt<KV>::kWgsPerCU, Fmt<KV>::kWgsPerCU)))
 void split_kernel(Params P) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[Layout<KV>::kBytes];
     const int b = blockIdx.x / P.nsplit, s = blockIdx.x % P.nsplit;
@@ -565,7 +578,7 @@ __device__ __forceinline__ int share_of(int64_t t, int64_t T, int64_t G) { retur
 __device__ __forceinline__ int64_t share_start(int64_t p, int64_t T, int64_t G) { return p * T / G; }
 
 template <int KV>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Fmt<KV>::kWgsPerCU, Fmt<KV>::kWgsPerCU)))
 void persistent_kernel(Params P) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[Layout<KV>::kBytes];
     const int64_t T = P.total, Gn = P.grid;
@@ -593,8 +606,12 @@ void persistent_kernel(Params P) {
 // lse = max + ln sum w_s; empty partials (lse = -inf) carry no weight.
 // (Submission 703488, `_reduce_splitk_parallel_*`.)
 // One workgroup per (sequence, head, 128-column chunk); its 256 threads are
-// 32 column quads x 8 partial groups, so the loads of all partials are in
-// flight together; the 8 group sums are added in LDS in a fixed order.
+// 32 column quads x 8 partial groups. Group g merges partials g, g + 8, ...
+// against its own running max, with the lse and O loads of up to kCombBatch
+// partials in flight at once (one memory round trip for up to 32 partials);
+// the 8 group results (m_g, W_g, A_g) are then merged in LDS in a fixed order:
+// M = max m_g, out = sum e^(m_g - M) A_g / sum e^(m_g - M) W_g. This is the
+// same weighted mean with the sum regrouped.
 struct CombineParams {
     const float* part_o;
     const float* part_lse;
@@ -611,10 +628,11 @@ struct CombineParams {
 constexpr int kCombThreads = 256;
 constexpr int kCombCols = 128;
 constexpr int kCombGroups = kCombThreads / (kCombCols / 4);  // 8
+constexpr int kCombBatch = 4;                                 // partials per group per round trip
 
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineParams C) {
     __shared__ f32x4 s_acc[kCombGroups][kCombCols / 4];
-    __shared__ float s_red[kCombThreads / 64];
+    __shared__ float s_m[kCombGroups];
     __shared__ float s_w[kCombGroups];
     const int chunk = blockIdx.x & 3, h = (blockIdx.x >> 2) & 15, b = blockIdx.x >> 6;
     const int tid = threadIdx.x, quad = tid & 31, grp = tid >> 5;
@@ -634,45 +652,63 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineParams C) 
         }
         base = b;  // slot of workgroup p for sequence b is p + b
     }
-    auto part_lse = [&](int k) -> float {
-        const int p = first + k;
-        if (C.mode == 1 && share_start(p, C.total, C.grid) == share_start(p + 1, C.total, C.grid))
-            return -INFINITY;  // empty share: wrote nothing
-        return C.part_lse[(int64_t)(base + p) * kHeads + h];
-    };
-    // M = max_k lse_k over the workgroup
-    float M = -INFINITY;
-    for (int k = tid; k < count; k += kCombThreads) M = fmaxf(M, part_lse(k));
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    if ((tid & 63) == 0) s_red[tid >> 6] = M;
-    __syncthreads();
-    M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    __syncthreads();
-    // per group: sum over its partials k = grp, grp + 8, ... of w_k O_k and w_k
+    float m = -INFINITY, W = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float W = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll 4
-        for (int k = grp; k < count; k += kCombGroups) {
-            const float l = part_lse(k);
-            if (l == -INFINITY) continue;
-            const float w = __expf(l - M);
-            W += w;
-            const f32x4 o = *reinterpret_cast<const f32x4*>(C.part_o + ((int64_t)(base + first + k) * kHeads + h) * kDv + d);
-            acc += w * o;
+    for (int k0 = grp; k0 < count; k0 += kCombGroups * kCombBatch) {
+        float l[kCombBatch];
+        f32x4 o[kCombBatch];
+#pragma unroll
+        for (int u = 0; u < kCombBatch; ++u) {
+            const int k = k0 + kCombGroups * u, p = first + k;
+            l[u] = -INFINITY;
+            o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (k < count) {
+                // an empty persistent share wrote nothing: its slot holds no partial
+                const bool empty = C.mode == 1 && share_start(p, C.total, C.grid) == share_start(p + 1, C.total, C.grid);
+                if (!empty) {
+                    const int64_t slot = base + p;
+                    l[u] = C.part_lse[slot * kHeads + h];
+                    o[u] = *reinterpret_cast<const f32x4*>(C.part_o + (slot * kHeads + h) * kDv + d);
+                }
+            }
         }
+        float mb = l[0];
+#pragma unroll
+        for (int u = 1; u < kCombBatch; ++u) mb = fmaxf(mb, l[u]);
+        if (mb == -INFINITY) continue;
+        const float mn = fmaxf(m, mb);
+        const float sc = __expf(m - mn);  // m = -inf: 0
+        W *= sc;
+        acc *= sc;
+#pragma unroll
+        for (int u = 0; u < kCombBatch; ++u) {
+            if (l[u] == -INFINITY) continue;  // skipped, never multiplied: the slot may hold anything
+            const float w = __expf(l[u] - mn);
+            W += w;
+            acc += w * o[u];
+        }
+        m = mn;
     }
     s_acc[grp][quad] = acc;
-    if (quad == 0) s_w[grp] = W;  // W is the same in every thread of a group
+    if (quad == 0) {  // m and W are the same in every thread of a group
+        s_m[grp] = m;
+        s_w[grp] = W;
+    }
     __syncthreads();
     if (grp == 0) {
-        f32x4 t = s_acc[0][quad];
-        float Wt = s_w[0];
+        float M = s_m[0];
 #pragma unroll
-        for (int g = 1; g < kCombGroups; ++g) {
-            t += s_acc[g][quad];
-            Wt += s_w[g];
+        for (int g = 1; g < kCombGroups; ++g) M = fmaxf(M, s_m[g]);
+        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+        float Wt = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int g = 0; g < kCombGroups; ++g) {
+                if (s_m[g] == -INFINITY) continue;
+                const float e = __expf(s_m[g] - M);
+                t += e * s_acc[g][quad];
+                Wt += e * s_w[g];
+            }
         }
         const float inv = (Wt > 0.f) ? 1.f / Wt : 0.f;
         bf16x4 pk;
@@ -683,7 +719,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineParams C) 
     }
 }
 
-// Decode check: rows -> fp32 through the stage-1 staging (issue_ops) and the
+// Decode check: rows -> fp32 through the stage-1 staging (issue_half) and the
 // two decode routines of the attention kernel. path 0: every column through
 // the score operand (qk_operand); path 1: columns 0..511 through the value
 // operand (pv_operand / pv_operand_fp4), columns 512..575 through path 0.
@@ -691,13 +727,15 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineParams C) 
 template <int KV>
 __global__ __launch_bounds__(64) void dequant_kernel(Params P, int64_t rows, int path, float* out) {
     __shared__ __attribute__((aligned(16))) uint8_t step[Layout<KV>::kStepBytes];
-    __shared__ int32_t idx[kStepTokens];
     const int lane = threadIdx.x, G = lane >> 4, r = lane & 15;
     const int64_t row0 = (int64_t)blockIdx.x * kStepTokens;
     const int n = (int)min<int64_t>(kStepTokens, rows - row0);
-    if (lane < kStepTokens) idx[lane] = (int32_t)(row0 + min(lane, n - 1));
-    __syncthreads();
-    issue_ops<KV>(P, idx, 0, n, step, lane, 0, 1);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int64_t row = row0 + min(kTile * t + r, n - 1);
+        issue_half<KV, 0>(P, row, step + t * Fmt<KV>::kTileBytes, lane);
+        issue_half<KV, 1>(P, row, step + t * Fmt<KV>::kTileBytes, lane);
+    }
     wait_vmcnt<0>();
     __syncthreads();
     float mul = 1.0f;
