@@ -62,7 +62,6 @@ static_assert(kStepTokens == 2 * kTile, "a step is two MFMA tiles");
 constexpr int kKSteps = kDqk / 32;       // 18 MFMA k-steps over the 576 score dims
 constexpr int kBlocks = kDv / 16;        // 32 output blocks of 16 columns per wave
 constexpr float kRescaleThresh = 8.0f;   // log2 units
-constexpr int kIdxWindow = 2048;         // tokens whose indices are staged in LDS at a time
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -106,8 +105,9 @@ struct Fmt<MLA_KV_BF16> {
     static constexpr int kRowBytes = 2 * kDqk;
     static constexpr int kCodeLoads = 18;
     static constexpr int kTileBytes = 18 * 1024;
-    static constexpr int kRing = 3;      // steps resident in the workgroup's LDS ring
-    static constexpr int kWgsPerCU = 1;  // LDS bound
+    static constexpr int kRing = 4;         // steps resident in the workgroup's LDS ring
+    static constexpr int kIdxWindow = 2048;  // tokens whose indices are staged in LDS at a time
+    static constexpr int kWgsPerCU = 1;     // LDS bound
     static constexpr int ops(int hi) { return 9 + 0 * hi; }  // LDS-DMA instructions of one tile half
 };
 template <>
@@ -116,6 +116,7 @@ struct Fmt<MLA_KV_FP8_E4M3> {
     static constexpr int kCodeLoads = 9;
     static constexpr int kTileBytes = 9 * 1024;
     static constexpr int kRing = 3;
+    static constexpr int kIdxWindow = 2048;
     static constexpr int kWgsPerCU = 2;
     static constexpr int ops(int hi) { return hi ? 4 : 5; }
 };
@@ -126,8 +127,9 @@ struct Fmt<MLA_KV_MXFP4> {
     static constexpr int kRopeOff = 4 * 1024;
     static constexpr int kScaleOff = kRopeOff + 512;
     static constexpr int kTileBytes = kScaleOff + 3 * 256;
-    static constexpr int kRing = 4;
-    static constexpr int kWgsPerCU = 2;
+    static constexpr int kRing = 3;
+    static constexpr int kIdxWindow = 1024;
+    static constexpr int kWgsPerCU = 3;
     static constexpr int ops(int hi) { return 4 + 0 * hi; }
 };
 
@@ -138,9 +140,11 @@ struct Layout {
     static constexpr int kStepBytes = 2 * Fmt<KV>::kTileBytes;
     static constexpr int kRingBytes = Fmt<KV>::kRing * kStepBytes;
     static constexpr int kSbufOff = kRingBytes;
-    static constexpr int kIdxOff = kSbufOff + kWaves * 64 * 16;
-    static constexpr int kBytes = kIdxOff + kIdxWindow * 4;
+    static constexpr int kSbufBytes = kWaves * 64 * 16;  // one step's partial scores; double-buffered
+    static constexpr int kIdxOff = kSbufOff + 2 * kSbufBytes;
+    static constexpr int kBytes = kIdxOff + Fmt<KV>::kIdxWindow * 4;
     static_assert(kBytes * Fmt<KV>::kWgsPerCU <= 160 * 1024, "stage-1 LDS exceeds 160 KiB per CU");
+    static_assert(Fmt<KV>::kIdxWindow % kThreads == 0, "index window is loaded by whole workgroups");
     static_assert(Fmt<KV>::kTileBytes % 16 == 0, "tiles stay 16-byte aligned");
 };
 
@@ -393,14 +397,16 @@ template <int KV>
 __device__ __forceinline__ void softmax_pv(const uint8_t* step, const f32x4 (&s)[2], float qk_scale, int nvalid,
                                            int lane, int wave, WaveAcc& a) {
     const int G = lane >> 4;
-    float x[8];
-    float mx = -INFINITY;
+    float x[8];  // raw scores; scaled below inside the exponent
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        x[j] = (tau(G, j) < nvalid) ? s[j >> 2][j & 3] * qk_scale : -INFINITY;
-        mx = fmaxf(mx, x[j]);
+    for (int j = 0; j < 8; ++j) x[j] = s[j >> 2][j & 3];
+    if (nvalid < kStepTokens) {  // a partial last step: padded tokens carry no weight
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (tau(G, j) >= nvalid) x[j] = -INFINITY;
     }
-    mx = group_max4(mx);
+    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    mx = group_max4(mx) * qk_scale;  // qk_scale > 0, so this is the max of the scaled scores
     const float m_new = fmaxf(a.m, mx);
     if (__any(m_new > a.m + kRescaleThresh)) {
         const float alpha = (a.m == -INFINITY) ? 0.f : fast_exp2(a.m - m_new);
@@ -416,7 +422,7 @@ __device__ __forceinline__ void softmax_pv(const uint8_t* step, const f32x4 (&s)
     }
     float p[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = fast_exp2(x[j] - a.m);
+    for (int j = 0; j < 8; ++j) p[j] = fast_exp2(fmaf(x[j], qk_scale, -a.m));
     a.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     bf16x8 pa;
 #pragma unroll
@@ -459,7 +465,7 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int t0, int t1, bo
     using L = Layout<KV>;
     constexpr int R = Fmt<KV>::kRing;
     constexpr int D = R - 1;  // steps issued ahead of the one computed
-    static_assert(D >= 1 && D <= 3, "ring depth");
+    static_assert(D >= 2 && D <= 3, "ring depth: the pipeline needs the next step landed (wait_own covers up to two younger steps)");
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, G = lane >> 4, r = lane & 15;
     const int tile = wave & 1, hf = wave >> 1;
@@ -472,6 +478,7 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int t0, int t1, bo
 
     // The first index window and this wave's half of Q^T are requested together
     // so that the workgroup start pays one memory round trip for both.
+    constexpr int kIdxWindow = Fmt<KV>::kIdxWindow;
     constexpr int kPer = kIdxWindow / kThreads;
     int32_t iv[kPer];
     auto load_idx = [&](int w0, int n) {
@@ -514,21 +521,35 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int t0, int t1, bo
             const int64_t row = idx[min(i * kStepTokens + kTile * tile + r, n - 1)];
             issue_half<KV>(P, row, smem + (i % R) * L::kStepBytes + tile * Fmt<KV>::kTileBytes, lane, hf);
         };
+        // This wave's partial scores of step i, written to exchange buffer i % 2.
+        auto scores = [&](int i) {
+            const uint8_t* st = smem + (i % R) * L::kStepBytes;
+            const f32x4 part = hf ? qk_partial<KV, 1>(st, qB, tile, lane) : qk_partial<KV, 0>(st, qB, tile, lane);
+            sbuf[(i & 1) * (kWaves * 64) + wave * 64 + lane] = part;
+        };
 #pragma unroll
         for (int d = 0; d < D; ++d)
             if (d < nsteps) issue_step(d);
+        wait_own<KV>(min(D - 1, nsteps - 1), hf);
+        __syncthreads();  // step 0 has landed
+        scores(0);
+        // Software pipeline: iteration s computes the scores of step s + 1
+        // while it runs the softmax and P . V of step s, so the score MFMAs
+        // overlap the softmax arithmetic. One barrier per step:
+        //   - every wave's partial scores of step s are in buffer s % 2;
+        //   - step s + 1 has landed (each wave waited for its own loads);
+        //   - every wave is done with step s - 1 (its ring slot and buffer
+        //     (s - 1) % 2, which this iteration refills).
         for (int s = 0; s < nsteps; ++s) {
-            wait_own<KV>(min(D - 1, nsteps - 1 - s), hf);
-            __syncthreads();  // step s has landed; every wave is done with step s - 1
-            if (s + D < nsteps) issue_step(s + D);
-            const uint8_t* st = smem + (s % R) * L::kStepBytes;
-            const f32x4 part = hf ? qk_partial<KV, 1>(st, qB, tile, lane) : qk_partial<KV, 0>(st, qB, tile, lane);
-            sbuf[wave * 64 + lane] = part;
+            if (s + 1 < nsteps) wait_own<KV>(min(D - 2, nsteps - 2 - s), hf);
             __syncthreads();
+            if (s + D < nsteps) issue_step(s + D);  // into the slot of step s - 1
+            const f32x4* sb = sbuf + (s & 1) * (kWaves * 64);
             f32x4 sc[2];
-            sc[0] = sbuf[0 * 64 + lane] + sbuf[2 * 64 + lane];
-            sc[1] = sbuf[1 * 64 + lane] + sbuf[3 * 64 + lane];
-            softmax_pv<KV>(st, sc, qk_scale, n - s * kStepTokens, lane, wave, a);
+            sc[0] = sb[0 * 64 + lane] + sb[2 * 64 + lane];
+            sc[1] = sb[1 * 64 + lane] + sb[3 * 64 + lane];
+            if (s + 1 < nsteps) scores(s + 1);
+            softmax_pv<KV>(smem + (s % R) * L::kStepBytes, sc, qk_scale, n - s * kStepTokens, lane, wave, a);
         }
     }
 
@@ -560,11 +581,20 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int t0, int t1, bo
     }
 }
 
+// Workgroups are handed to the eight XCDs round-robin (workgroup x to XCD
+// x % 8), and each XCD has its own L2. Renumbering the work items so that
+// consecutive ones share an XCD keeps the splits of one sequence, which all
+// read the same Q row and whose partials one combine workgroup reads back,
+// behind one L2. A bijection on [0, n) when n is a multiple of 8, else the
+// identity; correctness never depends on where a workgroup runs.
+__device__ __forceinline__ int xcd_order(int x, int n) { return (n & 7) ? x : (x & 7) * (n >> 3) + (x >> 3); }
+
 template <int KV>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Fmt<KV>::kWgsPerCU, Fmt<KV>::kWgsPerCU)))
 void split_kernel(Params P) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[Layout<KV>::kBytes];
-    const int b = blockIdx.x / P.nsplit, s = blockIdx.x % P.nsplit;
+    const int item = xcd_order(blockIdx.x, gridDim.x);
+    const int b = item / P.nsplit, s = item % P.nsplit;
     const int start = P.indptr[b], end = P.indptr[b + 1];
     const int L = end - start;
     const int chunk = ((L + P.nsplit - 1) / P.nsplit + kStepTokens - 1) / kStepTokens * kStepTokens;
@@ -582,7 +612,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Fmt<KV
 void persistent_kernel(Params P) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[Layout<KV>::kBytes];
     const int64_t T = P.total, Gn = P.grid;
-    const int p = blockIdx.x;
+    const int p = xcd_order(blockIdx.x, gridDim.x);
     const int64_t g0 = share_start(p, T, Gn), g1 = share_start(p + 1, T, Gn);
     if (g0 >= g1) return;
     // first sequence b with indptr[b] <= g0 < indptr[b+1]
@@ -634,7 +664,8 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineParams C) 
     __shared__ f32x4 s_acc[kCombGroups][kCombCols / 4];
     __shared__ float s_m[kCombGroups];
     __shared__ float s_w[kCombGroups];
-    const int chunk = blockIdx.x & 3, h = (blockIdx.x >> 2) & 15, b = blockIdx.x >> 6;
+    const int item = xcd_order(blockIdx.x, gridDim.x);
+    const int chunk = item & 3, h = (item >> 2) & 15, b = item >> 6;
     const int tid = threadIdx.x, quad = tid & 31, grp = tid >> 5;
     const int d = chunk * kCombCols + quad * 4;
     // partial k of this sequence lives in slot base + first + k, for k < count
