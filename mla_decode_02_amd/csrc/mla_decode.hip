@@ -127,9 +127,9 @@ struct Fmt<MLA_KV_MXFP4> {
     static constexpr int kRopeOff = 4 * 1024;
     static constexpr int kScaleOff = kRopeOff + 512;
     static constexpr int kTileBytes = kScaleOff + 3 * 256;
-    static constexpr int kRing = 3;
+    static constexpr int kRing = 4;
     static constexpr int kIdxWindow = 1024;
-    static constexpr int kWgsPerCU = 3;
+    static constexpr int kWgsPerCU = 2;
     static constexpr int ops(int hi) { return 4 + 0 * hi; }
 };
 
@@ -141,7 +141,10 @@ struct Layout {
     static constexpr int kRingBytes = Fmt<KV>::kRing * kStepBytes;
     static constexpr int kSbufOff = kRingBytes;
     static constexpr int kSbufBytes = kWaves * 64 * 16;  // one step's partial scores; double-buffered
-    static constexpr int kIdxOff = kSbufOff + 2 * kSbufBytes;
+    // MXFP4: the step's value-block scales as fp32, [tile][block 0..15][token], double-buffered
+    static constexpr int kFsBytes = KV == MLA_KV_MXFP4 ? 2 * 16 * kTile * 4 : 0;
+    static constexpr int kFsOff = kSbufOff + 2 * kSbufBytes;
+    static constexpr int kIdxOff = kFsOff + 2 * kFsBytes;
     static constexpr int kBytes = kIdxOff + Fmt<KV>::kIdxWindow * 4;
     static_assert(kBytes * Fmt<KV>::kWgsPerCU <= 160 * 1024, "stage-1 LDS exceeds 160 KiB per CU");
     static_assert(Fmt<KV>::kIdxWindow % kThreads == 0, "index window is loaded by whole workgroups");
@@ -281,67 +284,23 @@ __device__ __forceinline__ bf16x8 qk_operand(const uint8_t* step, int t, int ks,
     }
 }
 
-// Value operand of 16-column block c (bf16 / fp8): lane (G, n) receives column
-// 16c + n of the eight tokens tau(G, 0..7).
-template <int KV>
-__device__ __forceinline__ bf16x8 pv_operand(const uint8_t* step, int c, int lane) {
-    const int G = lane >> 4, j = lane & 15;
-    if constexpr (KV == MLA_KV_FP8_E4M3) {
-        // Row i of the transposed 8x16-byte block is token tau(G, i); lanes
-        // 2i and 2i+1 supply its bytes 0-7 and 8-15.
-        const int tk = tau(G, j >> 1);
-        const uint8_t* a = step + (tk >> 4) * Fmt<KV>::kTileBytes + 1024 * (c >> 2) +
-                           16 * (16 * (c & 3) + (tk & 15)) + 8 * (j & 1);
-        const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)a);
-        return fp8x8_to_bf16((uint32_t)w[0], (uint32_t)w[1]);
-    } else {
-        // Row i of each transposed 4x16-element block is token tau(G, i) (first
-        // read) or tau(G, 4 + i) (second read); lanes 4i..4i+3 supply its 32 bytes.
-        const int i = j >> 2, q = j & 3;
-        const int g0 = 2 * (c & 1) + (q >> 1);
-        const int t0 = tau(G, i), t1 = tau(G, 4 + i);
-        const uint8_t* base = step + 1024 * (c >> 1) + 16 * (16 * g0) + 8 * (q & 1);
-        const uint8_t* a0 = base + (t0 >> 4) * Fmt<KV>::kTileBytes + 16 * (t0 & 15);
-        const uint8_t* a1 = base + (t1 >> 4) * Fmt<KV>::kTileBytes + 16 * (t1 & 15);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a1);
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
+// Byte i of dw (two e2m1 codes of one token) scaled by sc[i] -> bf16x2.
+__device__ __forceinline__ void cvt_fp4_bytes(uint32_t dw, f32x4 sc, uint32_t* c) {
+    c[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc[0], 0));
+    c[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc[1], 1));
+    c[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc[2], 2));
+    c[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc[3], 3));
 }
 
-// Byte i of dw (two e2m1 codes of one token) scaled by 2^(e - 127), e = bits
-// sh..sh+7 of sc[i] -> bf16x2.
-__device__ __forceinline__ void cvt_fp4_bytes(uint32_t dw, u32x4 sc, int sh, uint32_t* c) {
-    c[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, e8m0_scale(sc[0], sh), 0));
-    c[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, e8m0_scale(sc[1], sh), 1));
-    c[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, e8m0_scale(sc[2], sh), 2));
-    c[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, e8m0_scale(sc[3], sh), 3));
-}
-
-// Value operands of MXFP4 block b (32 columns): lane (G, n) receives byte n of
-// the block for tokens tau(G, 0..7), i.e. columns 32b + 2n (even) and
-// 32b + 2n + 1 (odd), each token scaled by its own e8m0 code.
-__device__ __forceinline__ void pv_operand_fp4(const uint8_t* step, int b, int lane, bf16x8& even, bf16x8& odd) {
+// The value-block scales of one staged MXFP4 step as fp32: fs[t][b][r] =
+// 2^(e - 127) for block b (< 16) of token r of tile t. Thread i (of 256)
+// converts the dword of tile i / 128, block pair (i / 16) % 8, token i % 16.
+__device__ __forceinline__ void convert_scales(const uint8_t* step, float* fs, int i) {
     constexpr int TB = Fmt<MLA_KV_MXFP4>::kTileBytes;
-    const int G = lane >> 4, j = lane & 15;
-    const int tk = tau(G, j >> 1);
-    const uint8_t* a = step + (tk >> 4) * TB + 1024 * (b >> 2) + 16 * (16 * (b & 3) + (tk & 15)) + 8 * (j & 1);
-    const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)a);
-    // scale dwords 16 (b / 2) + 4G .. +3 of each tile: tokens 4G..4G+3, code in byte b & 1
-    const int q4 = 4 * (b >> 1) + G, sh = 8 * (b & 1);
-    const u32x4 s0 = reinterpret_cast<const u32x4*>(step + Fmt<MLA_KV_MXFP4>::kScaleOff)[q4];
-    const u32x4 s1 = reinterpret_cast<const u32x4*>(step + TB + Fmt<MLA_KV_MXFP4>::kScaleOff)[q4];
-    uint32_t c[8];
-    cvt_fp4_bytes((uint32_t)w[0], s0, sh, c);
-    cvt_fp4_bytes((uint32_t)w[1], s1, sh, c + 4);
-    u32x4 e, o;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        e[k] = __builtin_amdgcn_perm(c[2 * k + 1], c[2 * k], 0x05040100u);  // low halves
-        o[k] = __builtin_amdgcn_perm(c[2 * k + 1], c[2 * k], 0x07060302u);  // high halves
-    }
-    even = __builtin_bit_cast(bf16x8, e);
-    odd = __builtin_bit_cast(bf16x8, o);
+    const int t = i >> 7, p = (i >> 4) & 7, r = i & 15;
+    const uint32_t dw = *reinterpret_cast<const uint32_t*>(step + t * TB + Fmt<MLA_KV_MXFP4>::kScaleOff + 4 * (16 * p + r));
+    fs[(16 * t + 2 * p) * kTile + r] = e8m0_scale(dw, 0);
+    fs[(16 * t + 2 * p + 1) * kTile + r] = e8m0_scale(dw, 8);
 }
 
 // Max and sum over the four lane groups of column r (lanes r, r+16, r+32, r+48),
@@ -390,12 +349,132 @@ struct WaveAcc {
     float l;               // this lane's share of head r's softmax denominator
 };
 
-// Online softmax of one step's 32 scores and this wave's share of P . V.
-// s[t]: full scores of tile t (the same in all four waves, so every wave
-// takes the same rescale decisions and keeps the same m and l).
+// This wave's value-operand data of one staged step, read from LDS ahead of
+// the softmax so that the read latency overlaps it (converted afterwards).
 template <int KV>
-__device__ __forceinline__ void softmax_pv(const uint8_t* step, const f32x4 (&s)[2], float qk_scale, int nvalid,
-                                           int lane, int wave, WaveAcc& a) {
+struct PvRaw;
+template <>
+struct PvRaw<MLA_KV_BF16> {
+    i16x4 lo[kWaveBlocks], hi[kWaveBlocks];
+};
+template <>
+struct PvRaw<MLA_KV_FP8_E4M3> {
+    i32x2 w[kWaveBlocks];
+};
+template <>
+struct PvRaw<MLA_KV_MXFP4> {
+    i32x2 w[kWaveBlocks / 2];
+    f32x4 s0[kWaveBlocks / 2], s1[kWaveBlocks / 2];
+};
+
+// Per-lane byte offset (within a staged step) of this wave's value reads; the
+// per-block part is a compile-time constant added in pv_load, so the LDS reads
+// take it as an immediate offset.
+//   fp8 / MXFP4 (ds_read_b64_tr_b8): row i of the transposed 8 x 16-byte block
+//     is token tau(G, i); lanes 2i and 2i+1 supply its bytes 0-7 and 8-15.
+//     Block c's 16 (fp8) or 32 (MXFP4, two codes a byte) columns are bytes
+//     16 (c % 4) .. +15 of code load c / 4.
+//   bf16 (ds_read_b64_tr_b16, two reads): row i of each transposed 4 x 16
+//     block is token tau(G, i) (first read) or tau(G, 4 + i) (second read);
+//     lanes 4i..4i+3 supply its 32 bytes.
+template <int KV>
+__device__ __forceinline__ int pv_lane_offset(int lane, int wave) {
+    const int G = lane >> 4, j = lane & 15;
+    if constexpr (KV == MLA_KV_FP8_E4M3) {
+        const int tk = tau(G, j >> 1);
+        return (tk >> 4) * Fmt<KV>::kTileBytes + 16 * (tk & 15) + 8 * (j & 1) + 2048 * wave;
+    } else if constexpr (KV == MLA_KV_BF16) {
+        const int i = j >> 2, q = j & 3;
+        const int t0 = tau(G, i);
+        return (t0 >> 4) * Fmt<KV>::kTileBytes + 16 * (t0 & 15) + 256 * (q >> 1) + 8 * (q & 1) + 4096 * wave;
+    } else {
+        const int tk = tau(G, j >> 1);
+        return (tk >> 4) * Fmt<KV>::kTileBytes + 16 * (tk & 15) + 8 * (j & 1) + 1024 * wave;
+    }
+}
+
+template <int KV>
+__device__ __forceinline__ void pv_load(const uint8_t* step, const float* fs, int lane_off, int lane, int wave,
+                                        PvRaw<KV>& v) {
+    const uint8_t* vb = step + lane_off;
+    if constexpr (KV == MLA_KV_FP8_E4M3) {
+        // block 8 wave + j: + 1024 (j / 4) + 256 (j % 4)
+#pragma unroll
+        for (int j = 0; j < kWaveBlocks; ++j)
+            v.w[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vb + 1024 * (j >> 2) + 256 * (j & 3)));
+    } else if constexpr (KV == MLA_KV_BF16) {
+        // block 8 wave + j: + 1024 (j / 2) + 512 (j % 2); the second read covers tokens tau(G, 4 + i),
+        // 16 tokens (one tile) or 12 rows further on
+        const int G = lane >> 4, i = (lane & 15) >> 2;
+        const int t0 = tau(G, i), t1 = tau(G, 4 + i);
+        const int d1 = ((t1 >> 4) - (t0 >> 4)) * Fmt<KV>::kTileBytes + 16 * ((t1 & 15) - (t0 & 15));
+#pragma unroll
+        for (int j = 0; j < kWaveBlocks; ++j) {
+            const uint8_t* a0 = vb + 1024 * (j >> 1) + 512 * (j & 1);
+            v.lo[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0);
+            v.hi[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + d1));
+        }
+    } else {
+        // MX block b = 4 wave + j: codes + 256 j; scales fs[t][b][4G..4G+3] (as f32x4: 4 (16 t + b) + G)
+        const int G = lane >> 4;
+        const f32x4* f = reinterpret_cast<const f32x4*>(fs) + 16 * wave + G;
+#pragma unroll
+        for (int j = 0; j < kWaveBlocks / 2; ++j) {
+            v.w[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vb + 256 * j));
+            v.s0[j] = f[4 * j];
+            v.s1[j] = f[64 + 4 * j];
+        }
+    }
+}
+
+// Value operand of block kWaveBlocks * wave + j (bf16 / fp8): lane (G, n)
+// holds column 16 (kWaveBlocks * wave + j) + n of the tokens tau(G, 0..7).
+template <int KV>
+__device__ __forceinline__ bf16x8 pv_convert(const PvRaw<KV>& v, int j) {
+    if constexpr (KV == MLA_KV_FP8_E4M3) return fp8x8_to_bf16((uint32_t)v.w[j][0], (uint32_t)v.w[j][1]);
+    else return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v.lo[j], v.hi[j], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Value operands of MX block b = (kWaveBlocks / 2) * wave + j: lane (G, n) holds
+// byte n of the block for tokens tau(G, 0..7), i.e. columns 32b + 2n (even)
+// and 32b + 2n + 1 (odd), each token scaled by its own e8m0 code.
+__device__ __forceinline__ void pv_convert_fp4(const PvRaw<MLA_KV_MXFP4>& v, int j, bf16x8& even, bf16x8& odd) {
+    uint32_t c[8];
+    cvt_fp4_bytes((uint32_t)v.w[j][0], v.s0[j], c);
+    cvt_fp4_bytes((uint32_t)v.w[j][1], v.s1[j], c + 4);
+    u32x4 e, o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        e[k] = __builtin_amdgcn_perm(c[2 * k + 1], c[2 * k], 0x05040100u);  // low halves: even columns
+        o[k] = __builtin_amdgcn_perm(c[2 * k + 1], c[2 * k], 0x07060302u);  // high halves: odd columns
+    }
+    even = __builtin_bit_cast(bf16x8, e);
+    odd = __builtin_bit_cast(bf16x8, o);
+}
+
+// O += P . V for this wave's blocks from the raw operand data.
+template <int KV>
+__device__ __forceinline__ void pv_mma(const PvRaw<KV>& v, bf16x8 pa, WaveAcc& a) {
+    if constexpr (KV == MLA_KV_MXFP4) {
+#pragma unroll
+        for (int j = 0; j < kWaveBlocks / 2; ++j) {
+            bf16x8 ev, od;
+            pv_convert_fp4(v, j, ev, od);
+            a.o[2 * j] = mfma32(pa, ev, a.o[2 * j]);
+            a.o[2 * j + 1] = mfma32(pa, od, a.o[2 * j + 1]);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kWaveBlocks; ++j) a.o[j] = mfma32(pa, pv_convert<KV>(v, j), a.o[j]);
+    }
+}
+
+// Online softmax of one step's 32 scores; returns P (bf16) in the A-operand
+// layout of the P . V product. s[t]: full scores of tile t (the same in all
+// four waves, so every wave takes the same rescale decisions and keeps the
+// same m and l).
+__device__ __forceinline__ bf16x8 softmax_step(const f32x4 (&s)[2], float qk_scale, int nvalid, int lane,
+                                               WaveAcc& a) {
     const int G = lane >> 4;
     float x[8];  // raw scores; scaled below inside the exponent
 #pragma unroll
@@ -427,30 +506,23 @@ __device__ __forceinline__ void softmax_pv(const uint8_t* step, const f32x4 (&s)
     bf16x8 pa;
 #pragma unroll
     for (int j = 0; j < 8; ++j) pa[j] = (__bf16)p[j];
-
-    if constexpr (KV == MLA_KV_MXFP4) {
-#pragma unroll
-        for (int j = 0; j < kWaveBlocks / 2; ++j) {
-            bf16x8 ev, od;
-            pv_operand_fp4(step, (kWaveBlocks / 2) * wave + j, lane, ev, od);
-            a.o[2 * j] = mfma32(pa, ev, a.o[2 * j]);
-            a.o[2 * j + 1] = mfma32(pa, od, a.o[2 * j + 1]);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < kWaveBlocks; ++j)
-            a.o[j] = mfma32(pa, pv_operand<KV>(step, kWaveBlocks * wave + j, lane), a.o[j]);
-    }
+    return pa;
 }
 
 // Wait until this wave's own LDS-DMA loads of all but the last `groups` issued
 // steps have landed. The wave issues half `hi` of one tile per step.
-template <int KV>
+template <int KV, int N = 0>
 __device__ __forceinline__ void wait_own(int groups, int hi) {
     constexpr int k0 = Fmt<KV>::ops(0), k1 = Fmt<KV>::ops(1);
-    if (groups <= 0) wait_vmcnt<0>();
-    else if (groups == 1) { if (hi) wait_vmcnt<k1>(); else wait_vmcnt<k0>(); }
-    else { if (hi) wait_vmcnt<2 * k1>(); else wait_vmcnt<2 * k0>(); }
+    static_assert(N * k0 <= 63 && N * k1 <= 63, "vmcnt holds at most 63");
+    if constexpr (N < Fmt<KV>::kRing - 2) {
+        if (groups > N) {
+            wait_own<KV, N + 1>(groups, hi);
+            return;
+        }
+    }
+    if (hi) wait_vmcnt<N * k1>();
+    else wait_vmcnt<N * k0>();
 }
 
 // Attend tokens [t0, t1) of sequence b with the whole workgroup and write the
@@ -465,12 +537,14 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int t0, int t1, bo
     using L = Layout<KV>;
     constexpr int R = Fmt<KV>::kRing;
     constexpr int D = R - 1;  // steps issued ahead of the one computed
-    static_assert(D >= 2 && D <= 3, "ring depth: the pipeline needs the next step landed (wait_own covers up to two younger steps)");
+    static_assert(D >= 2, "ring depth: the pipeline needs the next step landed while one more is in flight");
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, G = lane >> 4, r = lane & 15;
     const int tile = wave & 1, hf = wave >> 1;
     int32_t* idx = reinterpret_cast<int32_t*>(smem + L::kIdxOff);
     f32x4* sbuf = reinterpret_cast<f32x4*>(smem + L::kSbufOff);
+    float* fs_buf = reinterpret_cast<float*>(smem + L::kFsOff);
+    const int pv_off = pv_lane_offset<KV>(lane, wave);
 
     float kv_scale = 1.0f;
     if constexpr (KV == MLA_KV_FP8_E4M3) kv_scale = *reinterpret_cast<const float*>(P.kv_scales);
@@ -521,18 +595,20 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int t0, int t1, bo
             const int64_t row = idx[min(i * kStepTokens + kTile * tile + r, n - 1)];
             issue_half<KV>(P, row, smem + (i % R) * L::kStepBytes + tile * Fmt<KV>::kTileBytes, lane, hf);
         };
-        // This wave's partial scores of step i, written to exchange buffer i % 2.
-        auto scores = [&](int i) {
+        // This wave's partial scores of step i, for exchange buffer i % 2.
+        // (MXFP4: also converts the step's value-block scales into buffer i % 2.)
+        auto scores = [&](int i) -> f32x4 {
             const uint8_t* st = smem + (i % R) * L::kStepBytes;
-            const f32x4 part = hf ? qk_partial<KV, 1>(st, qB, tile, lane) : qk_partial<KV, 0>(st, qB, tile, lane);
-            sbuf[(i & 1) * (kWaves * 64) + wave * 64 + lane] = part;
+            if constexpr (KV == MLA_KV_MXFP4) convert_scales(st, fs_buf + (i & 1) * (L::kFsBytes / 4), tid);
+            return hf ? qk_partial<KV, 1>(st, qB, tile, lane) : qk_partial<KV, 0>(st, qB, tile, lane);
         };
+        auto put_scores = [&](int i, f32x4 part) { sbuf[(i & 1) * (kWaves * 64) + wave * 64 + lane] = part; };
 #pragma unroll
         for (int d = 0; d < D; ++d)
             if (d < nsteps) issue_step(d);
         wait_own<KV>(min(D - 1, nsteps - 1), hf);
         __syncthreads();  // step 0 has landed
-        scores(0);
+        put_scores(0, scores(0));
         // Software pipeline: iteration s computes the scores of step s + 1
         // while it runs the softmax and P . V of step s, so the score MFMAs
         // overlap the softmax arithmetic. One barrier per step:
@@ -548,8 +624,16 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int t0, int t1, bo
             f32x4 sc[2];
             sc[0] = sb[0 * 64 + lane] + sb[2 * 64 + lane];
             sc[1] = sb[1 * 64 + lane] + sb[3 * 64 + lane];
-            if (s + 1 < nsteps) scores(s + 1);
-            softmax_pv<KV>(smem + (s % R) * L::kStepBytes, sc, qk_scale, n - s * kStepTokens, lane, wave, a);
+            // Program order keeps every long latency behind independent work:
+            // the value reads of step s and the score MFMAs of step s + 1 are
+            // issued before the softmax, and the scores are stored after P . V.
+            PvRaw<KV> v;
+            pv_load<KV>(smem + (s % R) * L::kStepBytes, fs_buf + (s & 1) * (L::kFsBytes / 4), pv_off, lane, wave, v);
+            f32x4 next = {0.f, 0.f, 0.f, 0.f};
+            if (s + 1 < nsteps) next = scores(s + 1);
+            const bf16x8 pa = softmax_step(sc, qk_scale, n - s * kStepTokens, lane, a);
+            pv_mma<KV>(v, pa, a);
+            if (s + 1 < nsteps) put_scores(s + 1, next);
         }
     }
 
@@ -753,7 +837,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineParams C) 
 // Decode check: rows -> fp32 through the stage-1 staging (issue_half) and the
 // two decode routines of the attention kernel. path 0: every column through
 // the score operand (qk_operand); path 1: columns 0..511 through the value
-// operand (pv_operand / pv_operand_fp4), columns 512..575 through path 0.
+// operand (pv_load, pv_convert / pv_convert_fp4), columns 512..575 through path 0.
 // One wave per 32 rows; fp8 values are multiplied by kv_scale in fp32.
 template <int KV>
 __global__ __launch_bounds__(64) void dequant_kernel(Params P, int64_t rows, int path, float* out) {
@@ -769,6 +853,12 @@ __global__ __launch_bounds__(64) void dequant_kernel(Params P, int64_t rows, int
     }
     wait_vmcnt<0>();
     __syncthreads();
+    __shared__ float fs[KV == MLA_KV_MXFP4 ? 2 * 16 * kTile : 1];
+    if constexpr (KV == MLA_KV_MXFP4) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) convert_scales(step, fs, 64 * k + lane);
+        __syncthreads();
+    }
     float mul = 1.0f;
     if constexpr (KV == MLA_KV_FP8_E4M3) mul = *reinterpret_cast<const float*>(P.kv_scales);
 #pragma unroll
@@ -785,22 +875,28 @@ __global__ __launch_bounds__(64) void dequant_kernel(Params P, int64_t rows, int
         }
     }
     if (path == 1) {
-        // lane (G, n) holds column n of block c for tokens tau(G, 0..7)
+        // The value reads of each of the four attention waves (pv_load, pv_convert):
+        // lane (G, n) holds column n of block c for tokens tau(G, 0..7).
+        for (int w = 0; w < kWaves; ++w) {
+            PvRaw<KV> v;
+            pv_load<KV>(step, fs, pv_lane_offset<KV>(lane, w), lane, w, v);
 #pragma unroll
-        for (int c = 0; c < (KV == MLA_KV_MXFP4 ? kBlocks / 2 : kBlocks); ++c) {
-            bf16x8 v0, v1;
-            if constexpr (KV == MLA_KV_MXFP4) pv_operand_fp4(step, c, lane, v0, v1);
-            else v0 = pv_operand<KV>(step, c, lane);
+            for (int j = 0; j < (KV == MLA_KV_MXFP4 ? kWaveBlocks / 2 : kWaveBlocks); ++j) {
+                const int c = (KV == MLA_KV_MXFP4 ? kWaveBlocks / 2 : kWaveBlocks) * w + j;
+                bf16x8 v0, v1;
+                if constexpr (KV == MLA_KV_MXFP4) pv_convert_fp4(v, j, v0, v1);
+                else v0 = pv_convert<KV>(v, j);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int tk = tau(G, e);
-                if (tk >= n) continue;
-                float* o = out + (row0 + tk) * kDqk;
-                if constexpr (KV == MLA_KV_MXFP4) {
-                    o[32 * c + 2 * r] = (float)v0[e];
-                    o[32 * c + 2 * r + 1] = (float)v1[e];
-                } else {
-                    o[16 * c + r] = (float)v0[e] * mul;
+                for (int e = 0; e < 8; ++e) {
+                    const int tk = tau(G, e);
+                    if (tk >= n) continue;
+                    float* o = out + (row0 + tk) * kDqk;
+                    if constexpr (KV == MLA_KV_MXFP4) {
+                        o[32 * c + 2 * r] = (float)v0[e];
+                        o[32 * c + 2 * r + 1] = (float)v1[e];
+                    } else {
+                        o[16 * c + r] = (float)v0[e] * mul;
+                    }
                 }
             }
         }

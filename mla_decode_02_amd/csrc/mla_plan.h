@@ -21,8 +21,8 @@ constexpr int kMaxSplits = 64;
 constexpr int kPersistentMinTokensPerCU = 1024;
 
 // Stage-1 workgroups resident per compute unit (bound by the LDS ring size:
-// bf16 one, fp8 two, MXFP4 three).
-constexpr int wgs_per_cu(int kv_dtype) { return kv_dtype == MLA_KV_BF16 ? 1 : kv_dtype == MLA_KV_FP8_E4M3 ? 2 : 3; }
+// bf16 one, fp8 and MXFP4 two).
+constexpr int wgs_per_cu(int kv_dtype) { return kv_dtype == MLA_KV_BF16 ? 1 : 2; }
 
 int make_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_info* p);
 int heuristic_splits(int batch, int64_t total_kv, int kv_dtype);
