@@ -718,14 +718,17 @@ void persistent_kernel(Params P) {
 
 // Stage 2: out[b,h] = sum_s w_s O_s / sum_s w_s, w_s = exp(lse_s - max lse),
 // lse = max + ln sum w_s; empty partials (lse = -inf) carry no weight.
-// (Submission 703488, `_reduce_splitk_parallel_*`.)
-// One workgroup per (sequence, head, 128-column chunk); its 256 threads are
-// 32 column quads x 8 partial groups. Group g merges partials g, g + 8, ...
-// against its own running max, with the lse and O loads of up to kCombBatch
-// partials in flight at once (one memory round trip for up to 32 partials);
-// the 8 group results (m_g, W_g, A_g) are then merged in LDS in a fixed order:
-// M = max m_g, out = sum e^(m_g - M) A_g / sum e^(m_g - M) W_g. This is the
-// same weighted mean with the sum regrouped.
+// (Submission 703488, `_reduce_splitk_parallel_*`; submission 593653,
+// `_flash_fp8_split_s2`.)
+// A sequence has 64 items (head, 128-column chunk). One workgroup takes
+// `items` consecutive items of one sequence (a power of two <= 8, chosen so
+// that no thread needs more than 8 partial loads); its 256 threads are 32
+// column quads x 8 groups, 8 / items groups per item. Group g' of an item
+// merges partials g', g' + 8 / items, ... against its own running max, with
+// the lse and O loads of up to kCombBatch partials in flight at once; the
+// group results (m_g, W_g, A_g) of an item are merged in LDS in a fixed
+// order: M = max m_g, out = sum e^(m_g - M) A_g / sum e^(m_g - M) W_g (the
+// same weighted mean with the sum regrouped).
 struct CombineParams {
     const float* part_o;
     const float* part_lse;
@@ -737,20 +740,36 @@ struct CombineParams {
     int nsplit;  // split-K
     int grid;    // persistent
     int total;
+    int items;   // items per workgroup
 };
 
 constexpr int kCombThreads = 256;
 constexpr int kCombCols = 128;
-constexpr int kCombGroups = kCombThreads / (kCombCols / 4);  // 8
-constexpr int kCombBatch = 4;                                 // partials per group per round trip
+constexpr int kCombQuads = kCombCols / 4;                 // 32
+constexpr int kCombGroups = kCombThreads / kCombQuads;    // 8
+constexpr int kCombBatch = 8;                             // partials in flight per thread
+
+// Items per combine workgroup: as many as keep each thread at <= 8 partial
+// loads (one round trip). The persistent plan's per-sequence partial counts
+// vary, so it takes one item per workgroup.
+static int combine_items(int mode, int nsplit) {
+    if (mode != 0) return 1;
+    int i = 8;
+    while (i > 1 && (nsplit * i + kCombGroups - 1) / kCombGroups > kCombBatch) i /= 2;
+    return i;
+}
 
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineParams C) {
-    __shared__ f32x4 s_acc[kCombGroups][kCombCols / 4];
+    __shared__ f32x4 s_acc[kCombGroups][kCombQuads];
     __shared__ float s_m[kCombGroups];
     __shared__ float s_w[kCombGroups];
-    const int item = xcd_order(blockIdx.x, gridDim.x);
-    const int chunk = item & 3, h = (item >> 2) & 15, b = item >> 6;
-    const int tid = threadIdx.x, quad = tid & 31, grp = tid >> 5;
+    const int I = C.items, gpi = kCombGroups / I;  // items per workgroup, groups per item
+    const int wpb = 4 * kHeads / I;                // workgroups per sequence
+    const int L = xcd_order(blockIdx.x, gridDim.x);
+    const int b = L / wpb, it0 = (L % wpb) * I;
+    const int tid = threadIdx.x, quad = tid & (kCombQuads - 1), gi = tid / kCombQuads;
+    const int u = gi / gpi, gq = gi % gpi;         // this thread's item and its group within the item
+    const int it = it0 + u, h = it >> 2, chunk = it & 3;
     const int d = chunk * kCombCols + quad * 4;
     // partial k of this sequence lives in slot base + first + k, for k < count
     int first = 0, count = 0, base = 0;
@@ -769,60 +788,59 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineParams C) 
     }
     float m = -INFINITY, W = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = grp; k0 < count; k0 += kCombGroups * kCombBatch) {
+    for (int k0 = gq; k0 < count; k0 += gpi * kCombBatch) {
         float l[kCombBatch];
         f32x4 o[kCombBatch];
 #pragma unroll
-        for (int u = 0; u < kCombBatch; ++u) {
-            const int k = k0 + kCombGroups * u, p = first + k;
-            l[u] = -INFINITY;
-            o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int v = 0; v < kCombBatch; ++v) {
+            const int k = k0 + gpi * v, p = first + k;
+            l[v] = -INFINITY;
+            o[v] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (k < count) {
                 // an empty persistent share wrote nothing: its slot holds no partial
                 const bool empty = C.mode == 1 && share_start(p, C.total, C.grid) == share_start(p + 1, C.total, C.grid);
                 if (!empty) {
                     const int64_t slot = base + p;
-                    l[u] = C.part_lse[slot * kHeads + h];
-                    o[u] = *reinterpret_cast<const f32x4*>(C.part_o + (slot * kHeads + h) * kDv + d);
+                    l[v] = C.part_lse[slot * kHeads + h];
+                    o[v] = *reinterpret_cast<const f32x4*>(C.part_o + (slot * kHeads + h) * kDv + d);
                 }
             }
         }
         float mb = l[0];
 #pragma unroll
-        for (int u = 1; u < kCombBatch; ++u) mb = fmaxf(mb, l[u]);
+        for (int v = 1; v < kCombBatch; ++v) mb = fmaxf(mb, l[v]);
         if (mb == -INFINITY) continue;
         const float mn = fmaxf(m, mb);
         const float sc = __expf(m - mn);  // m = -inf: 0
         W *= sc;
         acc *= sc;
 #pragma unroll
-        for (int u = 0; u < kCombBatch; ++u) {
-            if (l[u] == -INFINITY) continue;  // skipped, never multiplied: the slot may hold anything
-            const float w = __expf(l[u] - mn);
+        for (int v = 0; v < kCombBatch; ++v) {
+            if (l[v] == -INFINITY) continue;  // skipped, never multiplied: the slot may hold anything
+            const float w = __expf(l[v] - mn);
             W += w;
-            acc += w * o[u];
+            acc += w * o[v];
         }
         m = mn;
     }
-    s_acc[grp][quad] = acc;
+    s_acc[gi][quad] = acc;
     if (quad == 0) {  // m and W are the same in every thread of a group
-        s_m[grp] = m;
-        s_w[grp] = W;
+        s_m[gi] = m;
+        s_w[gi] = W;
     }
     __syncthreads();
-    if (grp == 0) {
-        float M = s_m[0];
-#pragma unroll
-        for (int g = 1; g < kCombGroups; ++g) M = fmaxf(M, s_m[g]);
+    if (gq == 0) {
+        const int g0 = u * gpi;
+        float M = s_m[g0];
+        for (int g = 1; g < gpi; ++g) M = fmaxf(M, s_m[g0 + g]);
         f32x4 t = {0.f, 0.f, 0.f, 0.f};
         float Wt = 0.f;
         if (M != -INFINITY) {
-#pragma unroll
-            for (int g = 0; g < kCombGroups; ++g) {
-                if (s_m[g] == -INFINITY) continue;
-                const float e = __expf(s_m[g] - M);
-                t += e * s_acc[g][quad];
-                Wt += e * s_w[g];
+            for (int g = 0; g < gpi; ++g) {
+                if (s_m[g0 + g] == -INFINITY) continue;
+                const float e = __expf(s_m[g0 + g] - M);
+                t += e * s_acc[g0 + g][quad];
+                Wt += e * s_w[g0 + g];
             }
         }
         const float inv = (Wt > 0.f) ? 1.f / Wt : 0.f;
@@ -943,7 +961,8 @@ static int launch(const mla_plan_info& plan, const Params& P, hipStream_t stream
         C.nsplit = plan.num_splits;
         C.grid = plan.grid;
         C.total = P.total;
-        hipLaunchKernelGGL(combine_kernel, dim3(kHeads * 4 * P.batch), dim3(kCombThreads), 0, stream, C);
+        C.items = combine_items(plan.mode, plan.num_splits);
+        hipLaunchKernelGGL(combine_kernel, dim3(kHeads * 4 * P.batch / C.items), dim3(kCombThreads), 0, stream, C);
         if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
     }
     return MLA_OK;

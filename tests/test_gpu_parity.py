@@ -62,17 +62,25 @@ def to_dev(case, dev):
                 kv_indices=torch.from_numpy(case.kv_indices).to(dev))
 
 
-def run_gpu(mla, case, dev, flags=0, sm_scale=0.0, with_lse=True, nan_workspace=True):
+def new_workspace(mla, case, dev, flags=0, nan_fill=True):
+    """Workspace for one plan; by default NaN-filled so that an unwritten partial
+    surfaces as NaN (the contents need no initialisation)."""
+    plan = mla.mla_decode_plan(case.batch, case.total_kv, case.kv_dtype, flags)
+    if not plan.workspace_bytes:
+        return None
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    if nan_fill:
+        ws.view(torch.float32).fill_(float("nan"))
+    return ws
+
+
+def run_gpu(mla, case, dev, flags=0, sm_scale=0.0, with_lse=True, nan_workspace=True, ws=None):
     t = to_dev(case, dev)
     B = case.batch
     out = torch.full((B, 16, 512), float("nan"), dtype=torch.bfloat16, device=dev)
     lse = torch.full((B, 16), float("nan"), dtype=torch.float32, device=dev) if with_lse else None
-    need = mla.mla_decode_workspace_size(B, case.total_kv, case.kv_dtype, flags)
-    ws = None
-    if need:
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
-        if nan_workspace:  # unwritten partials would surface as NaN
-            ws.view(torch.float32)[: need // 4].fill_(float("nan"))
+    if ws is None:
+        ws = new_workspace(mla, case, dev, flags, nan_fill=nan_workspace)
     mla.mla_decode(t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], t["kv_indices"], out, lse,
                    total_kv=case.total_kv, kv_dtype=case.kv_dtype, sm_scale=sm_scale, workspace=ws, flags=flags)
     torch.cuda.synchronize()
@@ -269,6 +277,24 @@ def test_deterministic(mla, dev, kv_dtype):
     a = run_gpu(mla, case, dev)
     b = run_gpu(mla, case, dev, nan_workspace=False)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+def test_workspace_reused_across_calls_and_plans(mla, orc, dev, kv_dtype):
+    """One workspace, NaN-filled once, serves a run of calls with different split
+    counts, persistent grids and batch sizes in a row (stale partials of an earlier
+    call are never read)."""
+    big = syn.make_case(5, [900, 40, 2500, 0, 333], kv_dtype, seed=66, shuffle=True)
+    small = syn.make_case(2, [129, 64], kv_dtype, seed=67, shuffle=True)
+    plans = [(big, mla.flags_for(splits=8)), (big, mla.flags_for(splits=3)), (small, 0),
+             (big, mla.flags_for(persistent=True, grid=64)), (small, mla.flags_for(splits=64)), (big, 0),
+             (big, mla.flags_for(splits=8))]
+    need = max(mla.mla_decode_workspace_size(c.batch, c.total_kv, c.kv_dtype, f) for c, f in plans)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws.view(torch.float32)[: need // 4].fill_(float("nan"))
+    refs = {id(big): oracle_ref(orc, big), id(small): oracle_ref(orc, small)}
+    for i, (c, f) in enumerate(plans):
+        check(run_gpu(mla, c, dev, flags=f, ws=ws), refs[id(c)], f"call {i} flags={f:#x}")
 
 
 def test_large_scores_rescale_path(mla, orc, dev):
