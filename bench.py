@@ -56,6 +56,8 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--only-gpu-loop", type=int, default=0,
                     help="skip measurement; run this many back-to-back calls of --workload (for profilers)")
+    ap.add_argument("--cold", action="store_true",
+                    help="with --only-gpu-loop: read-flush the caches before every call")
     return ap.parse_args()
 
 
@@ -223,7 +225,10 @@ def main():
         lse = torch.empty((case.batch, 16), dtype=torch.float32, device=dev)
         call = mla.prepare_decode(q, kv, sc, indptr, indices, out, lse, total_kv=case.total_kv,
                                   kv_dtype=case.kv_dtype, flags=args.flags)
+        flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev) if args.cold else None
         for _ in range(args.only_gpu_loop):
+            if flush is not None:
+                flush_read(flush)
             call()
         torch.cuda.synchronize()
         print(json.dumps({"workload": args.workload, "calls": args.only_gpu_loop}), flush=True)
