@@ -49,9 +49,11 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=HEADLINE, choices=sorted(syn.WORKLOADS))
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(set(syn.WORKLOADS) | set(syn.SWEEP)))
     ap.add_argument("--flags", type=int, default=0, help="MLA_FLAG_* word (0 = library heuristic)")
     ap.add_argument("--no-grid", action="store_true", help="time only the headline workload")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the full batch {4,32,64,256} x kv_len {1k,8k} x format grid (reported under 'sweep')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--only-gpu-loop", type=int, default=0,
@@ -247,6 +249,17 @@ def main():
     case = head.pop("_case")
     for r in results.values():
         r.pop("_case", None)
+    sweep = None
+    if args.sweep:
+        sweep = {}
+        for n in syn.SWEEP:
+            r = dict(results[n]) if n in results else measure(n, args, dev, flush)
+            r.pop("_case", None)
+            sweep[n] = r
+            print(f"# sweep {n}: cold {r['cold_us_median']:.2f} us, warm {r['warm_us']:.2f} us, "
+                  f"{r['effective_kv_GBps']:.0f} GB/s KV ({r['pct_hbm_peak_kv']:.1f}% of 8 TB/s), plan {r['plan']}",
+                  file=sys.stderr, flush=True)
+            torch.cuda.empty_cache()
 
     achieved = head["algorithmic_bytes"] / (head["cold_us_mean"] * 1e-6) / 1e9
     traffic = load_traffic(args.workload)
@@ -284,6 +297,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "grid": results,
+        "sweep": sweep,
         "kernel_source_hash": source_hash(),
         "host": platform.node(),
     }

@@ -131,12 +131,16 @@ class Case:
 
 
 def make_case(batch: int, kv_lens, kv_dtype: int, seed: int, shuffle: bool = False,
-              extra_rows: int = 0) -> Case:
+              extra_rows: int = 0, pool_rows: int = 0) -> Case:
     """Build a seeded workload.
 
     kv_lens: an int (uniform length) or a sequence of per-batch lengths.
     shuffle: use a seeded permutation of the physical rows as kv_indices.
     extra_rows: physical rows beyond the ones referenced (never read).
+    pool_rows: if > 0 and smaller than the cache, draw and quantise that many
+        rows and repeat them to fill the cache (physical rows stay distinct
+        in memory; used for the largest shapes, where drawing every row on the
+        host would take minutes).
     """
     if np.isscalar(kv_lens):
         lens = np.full(batch, int(kv_lens), dtype=np.int64)
@@ -149,7 +153,8 @@ def make_case(batch: int, kv_lens, kv_dtype: int, seed: int, shuffle: bool = Fal
     rows = T + int(extra_rows)
     rng = np.random.default_rng(seed)
     q = f32_to_bf16_bits(rng.standard_normal((batch, NUM_HEADS, DQK), dtype=np.float32))
-    kv_f32 = rng.standard_normal((rows, DQK), dtype=np.float32)
+    drawn = min(rows, pool_rows) if pool_rows > 0 else rows
+    kv_f32 = rng.standard_normal((drawn, DQK), dtype=np.float32)
     kv_bits = f32_to_bf16_bits(kv_f32)
     del kv_f32
     if kv_dtype == KV_BF16:
@@ -160,6 +165,11 @@ def make_case(batch: int, kv_lens, kv_dtype: int, seed: int, shuffle: bool = Fal
         kv, scales = quantize_mxfp4(bf16_bits_to_f32(kv_bits))
     else:
         raise ValueError(f"unknown kv dtype {kv_dtype}")
+    if drawn < rows:  # repeat the pool: row r holds pool row r % drawn
+        reps = -(-rows // drawn)
+        kv = np.ascontiguousarray(np.tile(kv, (reps, 1))[:rows])
+        if kv_dtype == KV_MXFP4:
+            scales = np.ascontiguousarray(np.tile(scales, (reps, 1))[:rows])
     if shuffle:
         indices = rng.permutation(rows)[:T].astype(np.int32)
     else:
@@ -178,7 +188,20 @@ WORKLOADS = {
 }
 
 
+# The pages' full benchmark grid: batch {4, 32, 64, 256} x kv_len {1024, 8192}
+# x each KV format (timed by `bench.py --sweep`; caches beyond 64K rows repeat a
+# 64K-row seeded pool).
+SWEEP_POOL_ROWS = 65536
+SWEEP = {
+    f"{KV_NAMES[fmt]}_b{b}_kv{L}": dict(batch=b, kv_lens=L, kv_dtype=fmt, seed=100 + 10 * fmt + i,
+                                          pool_rows=SWEEP_POOL_ROWS)
+    for fmt in (KV_BF16, KV_FP8, KV_MXFP4)
+    for i, (b, L) in enumerate((b, L) for b in (4, 32, 64, 256) for L in (1024, 8192))
+}
+
+
 def make_workload(name: str) -> Case:
-    c = make_case(**WORKLOADS[name])
+    spec = WORKLOADS[name] if name in WORKLOADS else SWEEP[name]
+    c = make_case(**spec)
     c.meta["workload"] = name
     return c

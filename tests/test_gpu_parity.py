@@ -318,3 +318,19 @@ def test_full_size_workload_sampled(mla, orc, dev, name):
     B = case.batch
     sample = sorted({0, B - 1, B // 2, (7 * B) // 11})
     check((got_o[sample], got_l[sample]), oracle_ref(orc, case, batches=sample), name)
+
+
+# The rest of the pages' shape grid (batch x kv_len x format), at full size and in the
+# default plan; caches beyond 64K rows repeat a seeded 64K-row pool. The oracle computes
+# a sample of sequences.
+SWEEP_SAMPLE = ["bf16_b256_kv8192", "fp8_b256_kv8192", "mxfp4_b256_kv1024", "mxfp4_b4_kv8192",
+                "bf16_b32_kv8192", "fp8_b256_kv1024"]
+
+
+@pytest.mark.parametrize("name", SWEEP_SAMPLE)
+def test_sweep_shape_sampled(mla, orc, dev, name):
+    case = syn.make_workload(name)
+    got_o, got_l = run_gpu(mla, case, dev, nan_workspace=False)
+    B = case.batch
+    sample = sorted({0, 1, B - 1, B // 2, (5 * B) // 7})
+    check((got_o[sample], got_l[sample]), oracle_ref(orc, case, batches=sample), name)
