@@ -84,6 +84,17 @@ def test_heuristic_fills_the_chip_for_the_measured_shapes(mla):
             assert p.grid % 256 == 0 and 256 <= p.grid <= 256 * per_cu, (fmt, B, L, p)
 
 
+def test_short_sequences_take_one_step_per_workgroup(mla):
+    # 4 x 1k: one workgroup per compute unit with one 32-token step each beats
+    # fewer, longer workgroups (the fill rule alone gives 8 splits)
+    for fmt in (0, 1, 2):
+        p = mla.mla_decode_plan(4, 4 * 1024, fmt)
+        assert (p.mode, p.num_splits, p.grid) == (0, 32, 128), (fmt, p)
+    # long sequences keep the fill rule
+    assert mla.mla_decode_plan(64, 64 * 8192, 1).num_splits == 8
+    assert mla.mla_decode_plan(32, 32 * 8192, 2).num_splits == 16
+
+
 def test_forced_plans(mla):
     p = mla.mla_decode_plan(4, 4000, 1, mla.flags_for(splits=7))
     assert (p.mode, p.num_splits, p.grid, p.num_partials) == (0, 7, 28, 28)
