@@ -49,7 +49,7 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=HEADLINE, choices=sorted(set(syn.WORKLOADS) | set(syn.SWEEP)))
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(set(syn.WORKLOADS) | set(syn.SWEEP) | set(syn.PAGED)))
     ap.add_argument("--flags", type=int, default=0, help="MLA_FLAG_* word (0 = library heuristic)")
     ap.add_argument("--no-grid", action="store_true", help="time only the headline workload")
     ap.add_argument("--sweep", action="store_true",
@@ -89,6 +89,20 @@ def upload(case, dev):
     return q, kv, sc, torch.from_numpy(case.kv_indptr).to(dev), torch.from_numpy(case.kv_indices).to(dev)
 
 
+def prepare(mla, case, q, kv, sc, indptr, indices, out, lse, flags, dev):
+    """The pre-marshalled decode call: mla_decode, or mla_decode_paged for a paged workload."""
+    import torch
+
+    paged = case.meta.get("paged")
+    if paged is None:
+        return mla.prepare_decode(q, kv, sc, indptr, indices, out, lse, total_kv=case.total_kv,
+                                  kv_dtype=case.kv_dtype, flags=flags)
+    t = {k: torch.from_numpy(paged[k]).to(dev) for k in ("kv_indptr", "kv_indices", "kv_last_page_len")}
+    return mla.prepare_decode_paged(q, kv, sc, t["kv_indptr"], t["kv_indices"], t["kv_last_page_len"], out, lse,
+                                    page_size=paged["page_size"], total_kv=case.total_kv, kv_dtype=case.kv_dtype,
+                                    flags=flags)
+
+
 def measure(name, args, dev, flush):
     import torch
 
@@ -100,9 +114,10 @@ def measure(name, args, dev, flush):
     B = case.batch
     out = torch.empty((B, 16, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, 16), dtype=torch.float32, device=dev)
-    call = mla.prepare_decode(q, kv, sc, indptr, indices, out, lse, total_kv=case.total_kv,
-                              kv_dtype=case.kv_dtype, flags=args.flags)
-    plan = mla.mla_decode_plan(B, case.total_kv, case.kv_dtype, args.flags)
+    call = prepare(mla, case, q, kv, sc, indptr, indices, out, lse, args.flags, dev)
+    paged = case.meta.get("paged")
+    plan_flags = args.flags | (mla.FLAG_FORCE_SPLIT if paged and paged["page_size"] > 1 else 0)
+    plan = mla.mla_decode_plan(B, case.total_kv, case.kv_dtype, plan_flags)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -135,6 +150,7 @@ def measure(name, args, dev, flush):
     return {
         "workload": name,
         "kv_format": syn.KV_NAMES[case.kv_dtype],
+        "page_size": case.meta.get("paged", {}).get("page_size", 1),
         "batch": B,
         "kv_len": int(case.kv_indptr[1] - case.kv_indptr[0]),
         "plan": {"mode": "split" if plan.mode == 0 else "persistent", "splits": plan.num_splits,
@@ -225,8 +241,7 @@ def main():
         q, kv, sc, indptr, indices = upload(case, dev)
         out = torch.empty((case.batch, 16, 512), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((case.batch, 16), dtype=torch.float32, device=dev)
-        call = mla.prepare_decode(q, kv, sc, indptr, indices, out, lse, total_kv=case.total_kv,
-                                  kv_dtype=case.kv_dtype, flags=args.flags)
+        call = prepare(mla, case, q, kv, sc, indptr, indices, out, lse, args.flags, dev)
         flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev) if args.cold else None
         for _ in range(args.only_gpu_loop):
             if flush is not None:
@@ -252,7 +267,7 @@ def main():
     sweep = None
     if args.sweep:
         sweep = {}
-        for n in syn.SWEEP:
+        for n in list(syn.SWEEP) + list(syn.PAGED):
             r = dict(results[n]) if n in results else measure(n, args, dev, flush)
             r.pop("_case", None)
             sweep[n] = r

@@ -136,6 +136,37 @@ int mla_decode(const void* q, const void* kv, const void* kv_scales, const int32
                void* stream);
 
 /*
+ * mla_decode_paged: mla_decode over a paged cache (page_size rows per page),
+ * the layout the pages' a16w8 path uses with 8-row pages for kv >= 8192
+ * (submission 616673, `_run_a16w8`: the fp8 cache viewed as
+ * [num_pages, page_size, 1, 576], page indptr = token indptr / page_size,
+ * kv_last_page_lens; the paged kv_indptr / kv_indices / kv_last_page_len
+ * convention of `mla_decode_fwd` in submission 593653).
+ *   kv                cache rows grouped in pages: page p is rows
+ *                     p * page_size .. p * page_size + page_size - 1
+ *   kv_indptr         device int32 [batch + 1] into kv_indices (pages)
+ *   kv_indices        device int32 page ids; sequence b uses pages
+ *                     kv_indices[kv_indptr[b] .. kv_indptr[b+1] - 1] in order
+ *   kv_last_page_len  device int32 [batch]: tokens in the last page of each
+ *                     non-empty sequence (1..page_size); ignored when
+ *                     page_size = 1 (may be NULL then)
+ *   page_size         1..65536; 1 gives exactly mla_decode
+ *   total_kv          host copy of the total number of tokens over the batch
+ *                     (sum of (pages_b - 1) * page_size + kv_last_page_len[b])
+ * Token j of sequence b is row kv_indices[kv_indptr[b] + j / page_size] *
+ * page_size + j % page_size; all other arguments, the outputs and the
+ * workspace are as for mla_decode. With page_size > 1 the plan is always
+ * split-K (size the workspace with MLA_FLAG_FORCE_SPLIT set) and
+ * MLA_FLAG_FORCE_PERSISTENT is rejected with MLA_ERR_INVALID_ARG.
+ * Returns as mla_decode; MLA_ERR_INVALID_ARG also for page_size out of range
+ * or a NULL / misaligned kv_last_page_len when page_size > 1.
+ */
+int mla_decode_paged(const void* q, const void* kv, const void* kv_scales, const int32_t* kv_indptr,
+                     const int32_t* kv_indices, const int32_t* kv_last_page_len, int page_size, void* out,
+                     float* lse, int batch, int64_t total_kv, int kv_dtype, float sm_scale, void* workspace,
+                     size_t workspace_bytes, int flags, void* stream);
+
+/*
  * mla_dequant_debug: decode `rows` physical cache rows to fp32 [rows, 576]
  * through the attention kernel's own staging and decode routines (test aid
  * for the bit-exact decoder check). For fp8 the value written is the binary32

@@ -22,9 +22,11 @@ from ._lib import (  # noqa: F401
     PlanInfo,
     flags_for,
     mla_decode,
+    mla_decode_paged,
     mla_decode_plan,
     mla_decode_workspace_size,
     mla_dequant_debug,
     mla_status_string,
     prepare_decode,
+    prepare_decode_paged,
 )

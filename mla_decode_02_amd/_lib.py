@@ -21,8 +21,8 @@ KV_BF16, KV_FP8_E4M3, KV_MXFP4 = 0, 1, 2
 FLAG_FORCE_SPLIT, FLAG_FORCE_PERSISTENT = 0x1, 0x2
 FLAG_SPLITS_SHIFT, FLAG_GRID_SHIFT = 8, 16
 
-_EXPORTS = ("mla_decode", "mla_decode_plan", "mla_decode_workspace_size", "mla_dequant_debug",
-            "mla_status_string")
+_EXPORTS = ("mla_decode", "mla_decode_paged", "mla_decode_plan", "mla_decode_workspace_size",
+            "mla_dequant_debug", "mla_status_string")
 
 
 class MlaError(RuntimeError):
@@ -59,6 +59,9 @@ def _load():
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
     lib.mla_decode.restype = i32
     lib.mla_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, ctypes.c_float, vp, sz, i32, vp]
+    lib.mla_decode_paged.restype = i32
+    lib.mla_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i64, i32, ctypes.c_float, vp, sz, i32,
+                                     vp]
     lib.mla_decode_plan.restype = i32
     lib.mla_decode_plan.argtypes = [i32, i64, i32, i32, ctypes.POINTER(_Plan)]
     lib.mla_decode_workspace_size.restype = sz
@@ -166,6 +169,47 @@ def mla_decode(q, kv, kv_scales, kv_indptr, kv_indices, out, lse=None, *, total_
     return workspace
 
 
+def mla_decode_paged(q, kv, kv_scales, kv_indptr, kv_indices, kv_last_page_len, out, lse=None, *, page_size: int,
+                     total_kv: int, kv_dtype: int, sm_scale: float = 0.0, workspace=None, flags: int = 0):
+    """Enqueue MLA decode over a paged cache (see include/mla_decode.h, mla_decode_paged).
+
+    kv rows grouped in pages of page_size rows ([pages * page_size, ...] as for
+    mla_decode); kv_indptr [B+1] int32 into kv_indices (page ids);
+    kv_last_page_len [B] int32 (tokens in each sequence's last page);
+    total_kv is the host total token count. Returns the workspace used.
+    """
+    B = int(kv_indptr.shape[0]) - 1
+    _need(q.is_cuda and q.dtype == torch.bfloat16 and q.is_contiguous() and tuple(q.shape) == (B, NUM_HEADS, QK_DIM),
+          "q must be contiguous bf16 [batch, 16, 576]")
+    _check_kv(kv, kv_scales, kv_dtype)
+    _need(kv.shape[0] % max(int(page_size), 1) == 0, "kv rows must be a whole number of pages")
+    _need(kv_indptr.is_cuda and kv_indptr.dtype == torch.int32 and kv_indptr.is_contiguous(),
+          "kv_indptr must be a contiguous device int32 tensor")
+    _need(kv_indices.is_cuda and kv_indices.dtype == torch.int32 and kv_indices.is_contiguous(),
+          "kv_indices must be a contiguous device int32 tensor")
+    if page_size > 1:
+        _need(kv_last_page_len is not None and kv_last_page_len.is_cuda and kv_last_page_len.dtype == torch.int32
+              and kv_last_page_len.is_contiguous() and kv_last_page_len.numel() == B,
+              "kv_last_page_len must be a contiguous device int32 tensor [batch]")
+    _need(out.is_cuda and out.dtype == torch.bfloat16 and out.is_contiguous() and tuple(out.shape) == (B, NUM_HEADS, V_DIM),
+          "out must be contiguous bf16 [batch, 16, 512]")
+    if lse is not None:
+        _need(lse.is_cuda and lse.dtype == torch.float32 and lse.is_contiguous() and tuple(lse.shape) == (B, NUM_HEADS),
+              "lse must be contiguous fp32 [batch, 16]")
+    plan_flags = flags | (FLAG_FORCE_SPLIT if page_size > 1 else 0)
+    need = mla_decode_workspace_size(B, total_kv, kv_dtype, plan_flags)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = _lib.mla_decode_paged(_ptr(q), _ptr(kv), _ptr(kv_scales), _ptr(kv_indptr), _ptr(kv_indices),
+                               _ptr(kv_last_page_len), int(page_size), _ptr(out), _ptr(lse), B, int(total_kv),
+                               int(kv_dtype), float(sm_scale), _ptr(workspace), ws_bytes, int(flags),
+                               _stream(q.device))
+    if rc != 0:
+        raise MlaError(rc, "mla_decode_paged")
+    return workspace
+
+
 def prepare_decode(q, kv, kv_scales, kv_indptr, kv_indices, out, lse=None, *, total_kv: int, kv_dtype: int,
                    sm_scale: float = 0.0, workspace=None, flags: int = 0):
     """Check and marshal the arguments once; return a zero-argument callable that
@@ -185,6 +229,30 @@ def prepare_decode(q, kv, kv_scales, kv_indptr, kv_indices, out, lse=None, *, to
         rc = fn(*args)
         if rc != 0:
             raise MlaError(rc, "mla_decode")
+        return keep
+
+    return call
+
+
+def prepare_decode_paged(q, kv, kv_scales, kv_indptr, kv_indices, kv_last_page_len, out, lse=None, *,
+                         page_size: int, total_kv: int, kv_dtype: int, sm_scale: float = 0.0, workspace=None,
+                         flags: int = 0):
+    """prepare_decode for mla_decode_paged: checks once (one checked call),
+    then returns a zero-argument callable that enqueues the same call."""
+    ws = mla_decode_paged(q, kv, kv_scales, kv_indptr, kv_indices, kv_last_page_len, out, lse, page_size=page_size,
+                          total_kv=total_kv, kv_dtype=kv_dtype, sm_scale=sm_scale, workspace=workspace, flags=flags)
+    B = int(kv_indptr.shape[0]) - 1
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    args = (_ptr(q), _ptr(kv), _ptr(kv_scales), _ptr(kv_indptr), _ptr(kv_indices), _ptr(kv_last_page_len),
+            int(page_size), _ptr(out), _ptr(lse), B, int(total_kv), int(kv_dtype), float(sm_scale), _ptr(ws),
+            ws_bytes, int(flags), _stream(q.device))
+    fn = _lib.mla_decode_paged
+    keep = (q, kv, kv_scales, kv_indptr, kv_indices, kv_last_page_len, out, lse, ws)
+
+    def call():
+        rc = fn(*args)
+        if rc != 0:
+            raise MlaError(rc, "mla_decode_paged")
         return keep
 
     return call

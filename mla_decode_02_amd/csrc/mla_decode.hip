@@ -69,8 +69,10 @@ struct Params {
     const __bf16* q;
     const uint8_t* kv;
     const void* kv_scales;
-    const int32_t* indptr;
-    const int32_t* indices;
+    const int32_t* indptr;     // [batch + 1] into indices (pages when page_size > 1)
+    const int32_t* indices;    // row (page_size 1) or page id of each entry
+    const int32_t* last_page;  // [batch] tokens in the last page (page_size > 1)
+    int page_size;             // rows per page (1: indices are rows)
     __bf16* out;
     float* lse;
     float* part_o;
@@ -525,15 +527,18 @@ __device__ __forceinline__ void wait_own(int groups, int hi) {
     else wait_vmcnt<N * k0>();
 }
 
-// Attend tokens [t0, t1) of sequence b with the whole workgroup and write the
-// result: final bf16 output + lse when `final`, else partial slot `slot`.
+// Attend tokens [t0, t1) (positions within sequence b, whose kv_indices
+// entries start at `base`) with the whole workgroup and write the result:
+// final bf16 output + lse when `final`, else partial slot `slot`. Token j of
+// the sequence is cache row indices[base + j] (page size 1), or row
+// indices[base + j / page_size] * page_size + j % page_size.
 // The four waves work on the same 32-token step: wave w gathers half w / 2 of
 // tile w % 2 and computes the scores of tile w % 2 over score k-steps
 // 9 (w / 2) .. +8, the partial scores are summed through LDS in a fixed order,
 // and every wave then runs the same softmax and accumulates P . V for its own
 // 128 output columns.
 template <int KV>
-__device__ void run_wg(const Params& P, uint8_t* smem, int b, int t0, int t1, bool final, int slot) {
+__device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, int t1, bool final, int slot) {
     using L = Layout<KV>;
     constexpr int R = Fmt<KV>::kRing;
     constexpr int D = R - 1;  // steps issued ahead of the one computed
@@ -556,8 +561,20 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int t0, int t1, bo
     constexpr int kPer = kIdxWindow / kThreads;
     int32_t iv[kPer];
     auto load_idx = [&](int w0, int n) {
+        const int ps = P.page_size;
 #pragma unroll
-        for (int k = 0; k < kPer; ++k) iv[k] = (tid + k * kThreads < n) ? P.indices[w0 + tid + k * kThreads] : 0;
+        for (int k = 0; k < kPer; ++k) {
+            const int j = w0 + tid + k * kThreads;
+            iv[k] = 0;
+            if (tid + k * kThreads < n) {
+                if (ps == 1) {
+                    iv[k] = P.indices[base + j];
+                } else {
+                    const int pg = j / ps;
+                    iv[k] = P.indices[base + pg] * ps + (j - pg * ps);
+                }
+            }
+        }
     };
     load_idx(t0, min(kIdxWindow, t1 - t0));
     bf16x8 qB[kHalfK];
@@ -679,12 +696,13 @@ void split_kernel(Params P) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[Layout<KV>::kBytes];
     const int item = xcd_order(blockIdx.x, gridDim.x);
     const int b = item / P.nsplit, s = item % P.nsplit;
-    const int start = P.indptr[b], end = P.indptr[b + 1];
-    const int L = end - start;
+    const int base = P.indptr[b], entries = P.indptr[b + 1] - base;
+    // tokens of the sequence: its entries, or (pages - 1) full pages plus the last page's tokens
+    const int L = P.page_size == 1 ? entries : entries > 0 ? (entries - 1) * P.page_size + P.last_page[b] : 0;
     const int chunk = ((L + P.nsplit - 1) / P.nsplit + kStepTokens - 1) / kStepTokens * kStepTokens;
-    const int t0 = min(end, start + s * chunk);
-    const int t1 = min(end, t0 + chunk);
-    run_wg<KV>(P, smem, b, t0, t1, P.nsplit == 1, b * P.nsplit + s);
+    const int t0 = min(L, s * chunk);
+    const int t1 = min(L, t0 + chunk);
+    run_wg<KV>(P, smem, b, base, t0, t1, P.nsplit == 1, b * P.nsplit + s);
 }
 
 // Largest p whose share [floor(p T / G), floor((p+1) T / G)) starts at or before t.
@@ -712,7 +730,7 @@ void persistent_kernel(Params P) {
         if (t0 >= t1) continue;
         const bool whole = (s >= g0) && (e <= g1);
         __syncthreads();  // the previous sequence's epilogue has finished reading LDS
-        run_wg<KV>(P, smem, b, t0, t1, whole, p + b);
+        run_wg<KV>(P, smem, b, s, t0 - s, t1 - s, whole, p + b);  // page size 1: entries are tokens
     }
 }
 
@@ -970,11 +988,13 @@ static int launch(const mla_plan_info& plan, const Params& P, hipStream_t stream
 
 }  // namespace mla
 
-extern "C" int mla_decode(const void* q, const void* kv, const void* kv_scales, const int32_t* kv_indptr,
-                          const int32_t* kv_indices, void* out, float* lse, int batch, int64_t total_kv,
-                          int kv_dtype, float sm_scale, void* workspace, size_t workspace_bytes, int flags,
-                          void* stream) {
-    using namespace mla;
+namespace mla {
+
+// Shared body of mla_decode (page size 1) and mla_decode_paged.
+static int decode_impl(const void* q, const void* kv, const void* kv_scales, const int32_t* kv_indptr,
+                       const int32_t* kv_indices, const int32_t* kv_last_page_len, int page_size, void* out,
+                       float* lse, int batch, int64_t total_kv, int kv_dtype, float sm_scale, void* workspace,
+                       size_t workspace_bytes, int flags, void* stream) {
     mla_plan_info plan;
     int rc = make_plan(batch, total_kv, kv_dtype, flags, &plan);
     if (rc != MLA_OK) return rc;
@@ -982,6 +1002,7 @@ extern "C" int mla_decode(const void* q, const void* kv, const void* kv_scales, 
     if (!q || !kv || !kv_indptr || !out) return MLA_ERR_INVALID_ARG;
     if (total_kv > 0 && !kv_indices) return MLA_ERR_INVALID_ARG;
     if (kv_dtype != MLA_KV_BF16 && !kv_scales) return MLA_ERR_INVALID_ARG;
+    if (page_size > 1 && (!kv_last_page_len || !aligned(kv_last_page_len, 4))) return MLA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 16) || !aligned(kv_indptr, 4) ||
         (kv_indices && !aligned(kv_indices, 4)) || (lse && !aligned(lse, 4)) ||
         (kv_dtype == MLA_KV_FP8_E4M3 && !aligned(kv_scales, 4)))
@@ -999,6 +1020,8 @@ extern "C" int mla_decode(const void* q, const void* kv, const void* kv_scales, 
     P.kv_scales = kv_scales;
     P.indptr = kv_indptr;
     P.indices = kv_indices;
+    P.last_page = kv_last_page_len;
+    P.page_size = page_size;
     P.out = reinterpret_cast<__bf16*>(out);
     P.lse = lse;
     P.part_o = reinterpret_cast<float*>(workspace);
@@ -1017,6 +1040,31 @@ extern "C" int mla_decode(const void* q, const void* kv, const void* kv_scales, 
         case MLA_KV_FP8_E4M3: return launch<MLA_KV_FP8_E4M3>(plan, P, s);
         default: return launch<MLA_KV_MXFP4>(plan, P, s);
     }
+}
+
+}  // namespace mla
+
+extern "C" int mla_decode(const void* q, const void* kv, const void* kv_scales, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, void* out, float* lse, int batch, int64_t total_kv,
+                          int kv_dtype, float sm_scale, void* workspace, size_t workspace_bytes, int flags,
+                          void* stream) {
+    return mla::decode_impl(q, kv, kv_scales, kv_indptr, kv_indices, nullptr, 1, out, lse, batch, total_kv, kv_dtype,
+                            sm_scale, workspace, workspace_bytes, flags, stream);
+}
+
+extern "C" int mla_decode_paged(const void* q, const void* kv, const void* kv_scales, const int32_t* kv_indptr,
+                                const int32_t* kv_indices, const int32_t* kv_last_page_len, int page_size, void* out,
+                                float* lse, int batch, int64_t total_kv, int kv_dtype, float sm_scale,
+                                void* workspace, size_t workspace_bytes, int flags, void* stream) {
+    if (page_size < 1 || page_size > (1 << 16)) return MLA_ERR_INVALID_ARG;
+    if (page_size > 1) {
+        // the persistent partition needs token offsets of every sequence, which
+        // paged caches do not carry: paged calls always plan split-K
+        if (flags & MLA_FLAG_FORCE_PERSISTENT) return MLA_ERR_INVALID_ARG;
+        flags |= MLA_FLAG_FORCE_SPLIT;
+    }
+    return mla::decode_impl(q, kv, kv_scales, kv_indptr, kv_indices, kv_last_page_len, page_size, out, lse, batch,
+                            total_kv, kv_dtype, sm_scale, workspace, workspace_bytes, flags, stream);
 }
 
 extern "C" int mla_dequant_debug(int kv_dtype, const void* kv, const void* kv_scales, int64_t rows, int path,

@@ -178,6 +178,43 @@ def make_case(batch: int, kv_lens, kv_dtype: int, seed: int, shuffle: bool = Fal
                 meta={"batch": batch, "seed": seed, "shuffle": shuffle, "kv_dtype": KV_NAMES[kv_dtype]})
 
 
+def make_paged_case(batch: int, kv_lens, kv_dtype: int, page_size: int, seed: int, shuffle: bool = True,
+                    extra_pages: int = 0):
+    """A seeded workload over a paged cache: each sequence's tokens fill whole
+    pages of `page_size` rows except the last one; physical pages are a
+    seeded permutation (or the identity). Returns (case, paged), where `case`
+    is the same workload with one kv_indices entry per token (token j of
+    sequence b at row page * page_size + j % page_size) and `paged` holds the
+    page-level kv_indptr, kv_indices (page ids) and kv_last_page_len."""
+    if np.isscalar(kv_lens):
+        lens = np.full(batch, int(kv_lens), dtype=np.int64)
+    else:
+        lens = np.asarray(kv_lens, dtype=np.int64)
+        assert lens.shape == (batch,)
+    npages = (lens + page_size - 1) // page_size
+    page_indptr = np.zeros(batch + 1, dtype=np.int64)
+    page_indptr[1:] = np.cumsum(npages)
+    total_pages = int(page_indptr[-1])
+    phys_pages = total_pages + int(extra_pages)
+    base = make_case(batch, 0, kv_dtype, seed, extra_rows=phys_pages * page_size)  # q and every physical row
+    rng = np.random.default_rng(seed + 7919)
+    page_ids = (rng.permutation(phys_pages)[:total_pages] if shuffle else np.arange(total_pages)).astype(np.int64)
+    tok_indptr = np.zeros(batch + 1, dtype=np.int64)
+    tok_indptr[1:] = np.cumsum(lens)
+    rows = []
+    for b in range(batch):
+        j = np.arange(lens[b])
+        rows.append(page_ids[page_indptr[b] + j // page_size] * page_size + j % page_size)
+    tok_indices = np.concatenate(rows) if rows else np.zeros(0, dtype=np.int64)
+    last = np.where(npages > 0, lens - (npages - 1) * page_size, 0)
+    case = Case(kv_dtype, base.q, base.kv, base.kv_scales, tok_indptr.astype(np.int32),
+                tok_indices.astype(np.int32),
+                meta={"batch": batch, "seed": seed, "page_size": page_size, "kv_dtype": KV_NAMES[kv_dtype]})
+    paged = {"page_size": page_size, "kv_indptr": page_indptr.astype(np.int32),
+             "kv_indices": page_ids.astype(np.int32), "kv_last_page_len": last.astype(np.int32)}
+    return case, paged
+
+
 # The five measured workloads (batch x kv_len, KV format, seed).
 WORKLOADS = {
     "bf16_b4_kv1024": dict(batch=4, kv_lens=1024, kv_dtype=KV_BF16, seed=0),
@@ -200,8 +237,19 @@ SWEEP = {
 }
 
 
+# Paged caches in the pages' configuration for kv >= 8192 (8-row pages).
+PAGED = {
+    "fp8_b64_kv8192_page8": dict(batch=64, kv_lens=8192, kv_dtype=KV_FP8, page_size=8, seed=3),
+    "mxfp4_b32_kv8192_page8": dict(batch=32, kv_lens=8192, kv_dtype=KV_MXFP4, page_size=8, seed=4),
+}
+
+
 def make_workload(name: str) -> Case:
-    spec = WORKLOADS[name] if name in WORKLOADS else SWEEP[name]
-    c = make_case(**spec)
+    """A named workload; for the paged ones the page-level arrays are in meta['paged']."""
+    if name in PAGED:
+        c, paged = make_paged_case(**PAGED[name])
+        c.meta["paged"] = paged
+    else:
+        c = make_case(**(WORKLOADS[name] if name in WORKLOADS else SWEEP[name]))
     c.meta["workload"] = name
     return c

@@ -166,6 +166,27 @@ def test_workspace_too_small(raw_lib, mla):
     assert _call(raw_lib, q=A, kv=A, sc=A, indptr=A, indices=A, out=A, ws=A + 4, ws_bytes=need, flags=f) == -1
 
 
+def _call_paged(raw_lib, last=A, page_size=8, flags=0, batch=2, total=64):
+    f = raw_lib.mla_decode_paged
+    f.restype = ctypes.c_int
+    vp = ctypes.c_void_p
+    f.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                  ctypes.c_float, vp, ctypes.c_size_t, ctypes.c_int, vp]
+    return f(A, A, A, A, A, last, page_size, A, None, batch, total, 1, 0.0, None, 0, flags, None)
+
+
+def test_paged_validation(raw_lib, mla):
+    assert _call_paged(raw_lib, page_size=0) == -1
+    assert _call_paged(raw_lib, page_size=-3) == -1
+    assert _call_paged(raw_lib, page_size=(1 << 16) + 1) == -1
+    assert _call_paged(raw_lib, last=None) == -1                    # page_size > 1 needs last-page lengths
+    assert _call_paged(raw_lib, last=A + 2) == -1                   # misaligned
+    assert _call_paged(raw_lib, flags=mla.flags_for(persistent=True)) == -1
+    # paged calls plan split-K: without a workspace a multi-split plan reports it
+    assert _call_paged(raw_lib, flags=mla.flags_for(splits=4)) == -3
+    assert _call_paged(raw_lib, batch=0, total=0) == 0
+
+
 def test_batch_zero_is_a_noop(raw_lib):
     assert _call(raw_lib, q=None, kv=None, sc=None, indptr=None, indices=None, out=None, batch=0, total=0) == 0
 

@@ -334,3 +334,62 @@ def test_sweep_shape_sampled(mla, orc, dev, name):
     B = case.batch
     sample = sorted({0, 1, B - 1, B // 2, (5 * B) // 7})
     check((got_o[sample], got_l[sample]), oracle_ref(orc, case, batches=sample), name)
+
+
+# ------------------------------------------------------------------ paged cache
+
+def run_gpu_paged(mla, case, paged, dev, flags=0):
+    t = to_dev(case, dev)
+    B = case.batch
+    out = torch.full((B, 16, 512), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((B, 16), float("nan"), dtype=torch.float32, device=dev)
+    ps = paged["page_size"]
+    plan_flags = flags | (mla.FLAG_FORCE_SPLIT if ps > 1 else 0)
+    need = mla.mla_decode_workspace_size(B, case.total_kv, case.kv_dtype, plan_flags)
+    ws = None
+    if need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws.view(torch.float32)[: need // 4].fill_(float("nan"))
+    mla.mla_decode_paged(t["q"], t["kv"], t["kv_scales"], torch.from_numpy(paged["kv_indptr"]).to(dev),
+                         torch.from_numpy(paged["kv_indices"]).to(dev),
+                         torch.from_numpy(paged["kv_last_page_len"]).to(dev), out, lse, page_size=ps,
+                         total_kv=case.total_kv, kv_dtype=case.kv_dtype, workspace=ws, flags=flags)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+@pytest.mark.parametrize("page_size", [2, 3, 8, 16, 64])
+def test_paged_cache(mla, orc, dev, kv_dtype, page_size):
+    """Ragged lengths with partial last pages, an empty sequence, shuffled physical pages."""
+    lens = [1, 0, page_size, 3 * page_size + 1, 333, 1030]
+    case, paged = syn.make_paged_case(len(lens), lens, kv_dtype, page_size, seed=70 + page_size, extra_pages=5)
+    check(run_gpu_paged(mla, case, paged, dev), oracle_ref(orc, case), f"page_size={page_size}")
+
+
+@pytest.mark.parametrize("splits", [1, 5])
+def test_paged_cache_forced_splits(mla, orc, dev, splits):
+    lens = [300, 7, 1030]
+    case, paged = syn.make_paged_case(3, lens, syn.KV_FP8, 8, seed=80 + splits)
+    check(run_gpu_paged(mla, case, paged, dev, flags=mla.flags_for(splits=splits)), oracle_ref(orc, case),
+          f"splits={splits}")
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+def test_page_size_one_is_mla_decode(mla, dev, kv_dtype):
+    """Page size 1 through mla_decode_paged gives bitwise the result of mla_decode."""
+    case = syn.make_case(4, [1000, 3, 700, 0], kv_dtype, seed=85, shuffle=True)
+    paged = {"page_size": 1, "kv_indptr": case.kv_indptr, "kv_indices": case.kv_indices,
+             "kv_last_page_len": np.zeros(case.batch, np.int32)}
+    a = run_gpu(mla, case, dev)
+    b = run_gpu_paged(mla, case, paged, dev)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("kv_dtype,batch", [(syn.KV_FP8, 64), (syn.KV_MXFP4, 32)])
+def test_paged_full_size_page8_sampled(mla, orc, dev, kv_dtype, batch):
+    """The pages' paged configuration for kv >= 8192: 8-row pages, full size, default split plan."""
+    case, paged = syn.make_paged_case(batch, 8192, kv_dtype, 8, seed=90 + kv_dtype)
+    got_o, got_l = run_gpu_paged(mla, case, paged, dev)
+    sample = sorted({0, batch - 1, batch // 2})
+    check((got_o[sample], got_l[sample]), oracle_ref(orc, case, batches=sample), f"paged {batch}x8192")
