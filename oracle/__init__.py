@@ -76,6 +76,17 @@ def _load():
         ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
     ]
+    lib.oracle_mla_decode_q8.restype = ctypes.c_int
+    lib.oracle_mla_decode_q8.argtypes = [
+        ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+    ]
+    lib.oracle_e4m3fn_encode.restype = ctypes.c_uint8
+    lib.oracle_e4m3fn_encode.argtypes = [ctypes.c_float]
+    lib.oracle_quantize_q_fp8.restype = ctypes.c_int
+    lib.oracle_quantize_q_fp8.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                          ctypes.c_void_p]
     lib.oracle_max_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -145,6 +156,60 @@ def mla_decode(q_bits: np.ndarray, kv_dtype: int, kv: np.ndarray, scales: np.nda
     if rc != 0:
         raise ValueError("oracle_mla_decode: invalid argument")
     return out, lse
+
+
+def mla_decode_q8(q_codes: np.ndarray, q_scale: float, kv_dtype: int, kv: np.ndarray, scales: np.ndarray | None,
+                  kv_indptr: np.ndarray, kv_indices: np.ndarray, sm_scale: float = SM_SCALE, batches=None,
+                  route: int = ROUTE_MAIN, nsplit: int = 1, form: int = 0, nthreads: int = 0):
+    """Reference MLA decode with an fp8 query: e4m3fn codes [B,16,576] and one
+    fp32 scale (query element = binary32 code value * q_scale). Returns
+    (out [n,16,512] f64, lse [n,16] f64) as mla_decode."""
+    q_codes = np.ascontiguousarray(q_codes, dtype=np.uint8)
+    kv = np.ascontiguousarray(kv)
+    scales = None if scales is None else np.ascontiguousarray(scales)
+    kv_indptr = np.ascontiguousarray(kv_indptr, dtype=np.int32)
+    kv_indices = np.ascontiguousarray(kv_indices, dtype=np.int32)
+    batch = kv_indptr.shape[0] - 1
+    if batches is None:
+        blist = None
+        n = batch
+    else:
+        blist = np.ascontiguousarray(np.asarray(batches, dtype=np.int32))
+        n = blist.shape[0]
+    out = np.zeros((n, NUM_HEADS, DV), dtype=np.float64)
+    lse = np.zeros((n, NUM_HEADS), dtype=np.float64)
+    rc = _load().oracle_mla_decode_q8(
+        _ptr(q_codes), float(np.float32(q_scale)), kv_dtype, _ptr(kv), _ptr(scales), _ptr(kv_indptr),
+        _ptr(kv_indices) if kv_indices.size else None, batch, float(sm_scale),
+        _ptr(blist), n, route, nsplit, form, nthreads, _ptr(out), _ptr(lse),
+    )
+    if rc != 0:
+        raise ValueError("oracle_mla_decode_q8: invalid argument")
+    return out, lse
+
+
+Q_SCALE_STATIC = 0
+Q_SCALE_DYNAMIC = 1
+
+
+def e4m3fn_encode(x: float) -> int:
+    """Nearest e4m3fn code of a binary32 value (ties to even)."""
+    return int(_load().oracle_e4m3fn_encode(float(np.float32(x))))
+
+
+def quantize_q_fp8(q_bits: np.ndarray, scale: float | None = None):
+    """Per-tensor fp8 quantisation of a bf16 query (bits, any shape).
+
+    scale None: dynamic, scale = max(absmax, 1e-12) / 448 in fp32. Otherwise the
+    static fp32 scale. Returns (codes uint8 of q's shape, scale float32 [1])."""
+    q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    codes = np.empty(q_bits.shape, dtype=np.uint8)
+    sc = np.array([0.0 if scale is None else scale], dtype=np.float32)
+    mode = Q_SCALE_DYNAMIC if scale is None else Q_SCALE_STATIC
+    rc = _load().oracle_quantize_q_fp8(_ptr(q_bits), q_bits.size, mode, _ptr(sc), _ptr(codes))
+    if rc != 0:
+        raise ValueError("oracle_quantize_q_fp8: invalid argument")
+    return codes, sc
 
 
 def max_threads() -> int:

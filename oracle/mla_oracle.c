@@ -27,6 +27,9 @@
  *    odd one; scale column = element index / 32.
  *  - Submission 754939, `quantize_fp8`: one per-tensor fp32 scale, codes in
  *    the fp8 e4m3 format whose finite maximum is 448 (e4m3fn).
+ *  - Submission 593653, `_quantize_q_dynamic_into` / `_quantize_q_static_into`
+ *    (the fp8-Q path): the query itself quantised to fp8 with one per-tensor
+ *    scale; the attention then uses the decoded query (oracle_mla_decode_q8).
  *
  * Readings where the pages leave a step open (each is listed in the design doc):
  *  - fp8 decoded value = binary32 product (code value) * kv_scale, one RNE
@@ -162,12 +165,31 @@ static double* gather_sequence(int kv_dtype, const void* kv, const void* scales,
     return x;
 }
 
-/* Scaled score of query row qh (576 bf16 values) against cache row xj. */
-static double score(const uint16_t* qh, const double* xj, double sm_scale) {
+/* Scaled score of query row qh (576 decoded values) against cache row xj. */
+static double score(const double* qh, const double* xj, double sm_scale) {
     double acc = 0.0;
     int d;
-    for (d = 0; d < OR_DQK; ++d) acc += (double)oracle_bf16_value(qh[d]) * xj[d];
+    for (d = 0; d < OR_DQK; ++d) acc += qh[d] * xj[d];
     return sm_scale * acc;
+}
+
+/*
+ * Query formats: 0 = bf16 bits [.., 576] (the value itself); 1 = e4m3fn codes
+ * with one fp32 scale, decoded like the fp8 cache: the binary32 product
+ * (code value) * q_scale, widened to binary64.
+ */
+static void decode_query(int q_fmt, const void* q, float q_scale, int64_t row, double* qh) {
+    int d;
+    if (q_fmt == 0) {
+        const uint16_t* p = (const uint16_t*)q + row * OR_DQK;
+        for (d = 0; d < OR_DQK; ++d) qh[d] = (double)oracle_bf16_value(p[d]);
+    } else {
+        const uint8_t* p = (const uint8_t*)q + row * OR_DQK;
+        for (d = 0; d < OR_DQK; ++d) {
+            float v = oracle_e4m3fn_value(p[d]) * q_scale; /* one binary32 multiply */
+            qh[d] = (double)v;
+        }
+    }
 }
 
 /*
@@ -177,7 +199,7 @@ static double score(const uint16_t* qh, const double* xj, double sm_scale) {
  *   out = sum_j exp(s_j - M) x_j[0:512] / Z,  lse = M + ln Z.
  * Empty range: out = 0, lse = -inf.
  */
-static void attend_head(const uint16_t* qh, const double* x, int64_t j0, int64_t j1, double sm_scale,
+static void attend_head(const double* qh, const double* x, int64_t j0, int64_t j1, double sm_scale,
                         double* out, double* lse) {
     int64_t j;
     int d;
@@ -208,7 +230,7 @@ static void attend_head(const uint16_t* qh, const double* x, int64_t j0, int64_t
  * exp(s_j) / sum_k exp(s_k) (no max subtraction), then the output is the
  * probability-weighted sum of V rows. Used only to cross-check attend_head.
  */
-static void attend_head_brute(const uint16_t* qh, const double* x, int64_t L, double sm_scale,
+static void attend_head_brute(const double* qh, const double* x, int64_t L, double sm_scale,
                               double* out, double* lse) {
     int64_t j, k;
     int d;
@@ -301,7 +323,7 @@ static void combine(int S, const double* po, const double* plse, const double* p
 }
 
 /* Max scaled score of one head over tokens [j0, j1) (-inf when empty). */
-static double range_max(const uint16_t* qh, const double* x, int64_t j0, int64_t j1, double sm_scale) {
+static double range_max(const double* qh, const double* x, int64_t j0, int64_t j1, double sm_scale) {
     double M = -INFINITY;
     int64_t j;
     for (j = j0; j < j1; ++j) {
@@ -312,8 +334,9 @@ static double range_max(const uint16_t* qh, const double* x, int64_t j0, int64_t
 }
 
 /*
- * Public entry.
- *   q          bf16 bits [batch, 16, 576]
+ * Shared body of the public entries (query format q_fmt as decode_query).
+ *   q          bf16 bits [batch, 16, 576] (oracle_mla_decode) or e4m3fn codes
+ *              with q_scale (oracle_mla_decode_q8)
  *   kv, scales cache codes and scales (layouts as decode_row)
  *   kv_indptr  [batch + 1], kv_indices [kv_indptr[batch]]
  *   batches    list of n_list batch ids to compute (NULL: all, n_list = batch)
@@ -324,7 +347,7 @@ static double range_max(const uint16_t* qh, const double* x, int64_t j0, int64_t
  *   nthreads   OpenMP threads (<= 0: library default)
  * Returns 0, or -1 on an invalid argument.
  */
-int oracle_mla_decode(const uint16_t* q, int kv_dtype, const void* kv, const void* scales,
+static int decode_any(int q_fmt, const void* q, float q_scale, int kv_dtype, const void* kv, const void* scales,
                       const int32_t* kv_indptr, const int32_t* kv_indices, int batch, double sm_scale,
                       const int32_t* batches, int n_list, int route, int nsplit, int form, int nthreads,
                       double* out, double* lse) {
@@ -352,9 +375,10 @@ int oracle_mla_decode(const uint16_t* q, int kv_dtype, const void* kv, const voi
         if (!x) return -1;
 #pragma omp parallel for schedule(dynamic, 1)
         for (h = 0; h < OR_HEADS; ++h) {
-            const uint16_t* qh = q + ((int64_t)b * OR_HEADS + h) * OR_DQK;
+            double qh[OR_DQK];
             double* o = out + ((int64_t)i * OR_HEADS + h) * OR_DV;
             double* l = lse + (int64_t)i * OR_HEADS + h;
+            decode_query(q_fmt, q, q_scale, (int64_t)b * OR_HEADS + h, qh);
             if (route == 0) {
                 attend_head(qh, x, 0, L, sm_scale, o, l);
             } else if (route == 1) {
@@ -376,6 +400,85 @@ int oracle_mla_decode(const uint16_t* q, int kv_dtype, const void* kv, const voi
             }
         }
         free(x);
+    }
+    return 0;
+}
+
+int oracle_mla_decode(const uint16_t* q, int kv_dtype, const void* kv, const void* scales,
+                      const int32_t* kv_indptr, const int32_t* kv_indices, int batch, double sm_scale,
+                      const int32_t* batches, int n_list, int route, int nsplit, int form, int nthreads,
+                      double* out, double* lse) {
+    return decode_any(0, q, 1.0f, kv_dtype, kv, scales, kv_indptr, kv_indices, batch, sm_scale, batches, n_list,
+                      route, nsplit, form, nthreads, out, lse);
+}
+
+/*
+ * The same with an fp8 query: q_codes e4m3fn [batch, 16, 576] and one fp32
+ * q_scale; query element = binary32 (code value) * q_scale.
+ */
+int oracle_mla_decode_q8(const uint8_t* q_codes, float q_scale, int kv_dtype, const void* kv, const void* scales,
+                         const int32_t* kv_indptr, const int32_t* kv_indices, int batch, double sm_scale,
+                         const int32_t* batches, int n_list, int route, int nsplit, int form, int nthreads,
+                         double* out, double* lse) {
+    return decode_any(1, q_codes, q_scale, kv_dtype, kv, scales, kv_indptr, kv_indices, batch, sm_scale, batches,
+                      n_list, route, nsplit, form, nthreads, out, lse);
+}
+
+/*
+ * Nearest e4m3fn code to a binary32 value, ties to the code with an even
+ * mantissa (round to nearest even), by search over the 127 non-negative finite
+ * codes. |x| above 448 saturates to 448 (the quantiser clamps before it
+ * encodes, so saturation never decides a value there). The sign bit follows
+ * the sign of x, so -0 and negative values that round to zero give 0x80.
+ * NaN gives 0x7F.
+ */
+uint8_t oracle_e4m3fn_encode(float x) {
+    double a = fabs((double)x), best_err = INFINITY;
+    int c, best = 0;
+    if (isnan(x)) return 0x7F;
+    for (c = 0; c <= 0x7E; ++c) {
+        double err = fabs((double)oracle_e4m3fn_value((uint8_t)c) - a);
+        if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+            best_err = err;
+            best = c;
+        }
+    }
+    return (uint8_t)(signbit(x) ? (best | 0x80) : best);
+}
+
+/*
+ * Per-tensor fp8 quantisation of a bf16 query of n elements (submission
+ * 593653, `_quantize_q_static_into` and `_quantize_q_dynamic_into`):
+ *   dynamic (mode 1): scale = max(max_i |q_i|, 1e-12) / 448, written to *scale;
+ *   static  (mode 0): scale = *scale as given (must be finite and > 0);
+ *   code_i = e4m3fn(clamp(q_i / scale, -448, 448)).
+ * Every step is one binary32 operation (the bf16 value widened exactly, one
+ * division, one comparison-based clamp, one round to nearest even).
+ * Returns 0, or -1 for a bad mode or scale.
+ */
+int oracle_quantize_q_fp8(const uint16_t* q, int64_t n, int mode, float* scale, uint8_t* codes) {
+    int64_t i;
+    float s;
+    if (mode == 1) {
+        float amax = 0.0f;
+        for (i = 0; i < n; ++i) {
+            float a = fabsf(oracle_bf16_value(q[i]));
+            if (a > amax) amax = a;
+        }
+        if (amax < 1e-12f) amax = 1e-12f;
+        s = amax / 448.0f;
+        *scale = s;
+    } else if (mode == 0) {
+        s = *scale;
+        if (!(s > 0.0f) || isinf(s)) return -1;
+    } else {
+        return -1;
+    }
+    for (i = 0; i < n; ++i) {
+        float y = oracle_bf16_value(q[i]) / s;
+        if (y > 448.0f) y = 448.0f;
+        if (y < -448.0f) y = -448.0f;
+        codes[i] = oracle_e4m3fn_encode(y);
     }
     return 0;
 }

@@ -27,6 +27,11 @@ MUTANTS = {
     "gather_ignores_start": ("kv_indices[start + j]", "kv_indices[j]"),
     "combine_weight_sign": ("w = exp(plse[s] - M);", "w = exp(M - plse[s]);"),
     "fp8_scale_dropped": ("x[d] = c * s; /*", "x[d] = c; (void)s; /*"),
+    "q8_scale_dropped": ("oracle_e4m3fn_value(p[d]) * q_scale;", "oracle_e4m3fn_value(p[d]); (void)q_scale;"),
+    "encode_ties_odd": ("(c & 1) == 0 && (best & 1) == 1", "(c & 1) == 1 && (best & 1) == 0"),
+    "encode_drops_sign": ("signbit(x) ? (best | 0x80) : best", "best"),
+    "quant_scale_inverted": ("s = amax / 448.0f;", "s = 448.0f / amax;"),
+    "quant_multiplies": ("oracle_bf16_value(q[i]) / s;", "oracle_bf16_value(q[i]) * s;"),
 }
 
 

@@ -140,9 +140,9 @@ def _q64(case):
     return torch.from_numpy(case.q.view(np.int16)).view(torch.bfloat16).to(torch.float64)
 
 
-def _sdpa_ref(case, oracle_mod, sm_scale=1.0 / 24.0):
+def _sdpa_ref(case, oracle_mod, sm_scale=1.0 / 24.0, q=None):
     x = _decoded_torch(case, oracle_mod)
-    q = _q64(case)
+    q = _q64(case) if q is None else q
     outs, lses = [], []
     for b in range(case.batch):
         s, e = int(case.kv_indptr[b]), int(case.kv_indptr[b + 1])
@@ -305,3 +305,102 @@ def test_batch_subset_matches_full(oracle_mod):
                                 batches=[4, 1])
     np.testing.assert_array_equal(sub[0], full[0][[4, 1]])
     np.testing.assert_array_equal(sub[1], full[1][[4, 1]])
+
+
+# --------------------------------------------------------------------------- fp8 query
+
+def _q8_decoded_torch(codes, scale):
+    """fp8 query decoded with torch: e4m3fn -> fp32, one fp32 multiply by the scale, widened to fp64."""
+    c = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32)
+    return (c * torch.tensor(np.float32(scale), dtype=torch.float32)).to(torch.float64)
+
+
+def _torch_quant(q_bits, scale):
+    """(q / scale).clamp(-448, 448) cast to e4m3fn, all in torch fp32 (its CPU cast rounds to nearest even)."""
+    q = torch.from_numpy(np.ascontiguousarray(q_bits).view(np.int16)).view(torch.bfloat16).to(torch.float32)
+    y = (q / torch.tensor(np.float32(scale), dtype=torch.float32)).clamp(-448.0, 448.0)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _all_finite_bf16():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = syn.bf16_bits_to_f32(bits)
+    return bits[np.isfinite(v)]
+
+
+def test_e4m3fn_encode_exhaustive_bf16_vs_torch(oracle_mod):
+    """Every finite bf16 value (all e4m3 midpoints are among them, so every tie is hit) through the
+    quantiser with scale 1: codes equal torch's clamped cast bit for bit."""
+    bits = _all_finite_bf16()
+    codes, _ = oracle_mod.quantize_q_fp8(bits, scale=1.0)
+    np.testing.assert_array_equal(codes, _torch_quant(bits, 1.0))
+
+
+def test_e4m3fn_encode_ties_and_points(oracle_mod):
+    assert oracle_mod.e4m3fn_encode(1.0) == 0x38
+    assert oracle_mod.e4m3fn_encode(1.0625) == 0x38          # midpoint of 1 and 1.125 -> even mantissa
+    assert oracle_mod.e4m3fn_encode(1.1875) == 0x3A          # midpoint of 1.125 and 1.25 -> even mantissa
+    assert oracle_mod.e4m3fn_encode(-448.0) == 0xFE
+    assert oracle_mod.e4m3fn_encode(2.0 ** -10) == 0x00      # half the smallest subnormal 2^-9 -> zero (even)
+    assert oracle_mod.e4m3fn_encode(3 * 2.0 ** -10) == 0x02  # between 1 and 2 subnormal steps -> even
+    assert oracle_mod.e4m3fn_encode(-0.0) == 0x80
+
+
+@pytest.mark.parametrize("scale", [0.0133928571, 6.0 / 448.0, 0.5])
+def test_quantize_static_vs_torch(oracle_mod, scale):
+    case = syn.make_case(3, [2, 3, 4], syn.KV_BF16, seed=35)
+    codes, sc = oracle_mod.quantize_q_fp8(case.q, scale=scale)
+    assert sc[0] == np.float32(scale)
+    np.testing.assert_array_equal(codes, _torch_quant(case.q, scale))
+
+
+def test_quantize_dynamic_scale(oracle_mod):
+    case = syn.make_case(4, [2, 3, 4, 5], syn.KV_BF16, seed=36)
+    codes, sc = oracle_mod.quantize_q_fp8(case.q)
+    q = syn.bf16_bits_to_f32(case.q)
+    assert sc[0] == np.float32(np.abs(q).max()) / np.float32(448.0)
+    np.testing.assert_array_equal(codes, _torch_quant(case.q, sc[0]))
+    # the largest magnitude maps to the top of the range
+    assert (codes & 0x7F).max() == 0x7E
+
+
+def test_quantize_dynamic_zero_query(oracle_mod):
+    codes, sc = oracle_mod.quantize_q_fp8(np.zeros((2, 16, 576), dtype=np.uint16))
+    assert sc[0] == np.float32(1e-12) / np.float32(448.0)
+    assert not codes.any()
+
+
+def test_quantize_rejects_bad_static_scale(oracle_mod):
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        with pytest.raises(ValueError):
+            oracle_mod.quantize_q_fp8(np.zeros(4, dtype=np.uint16), scale=bad)
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+def test_q8_vs_torch_sdpa(oracle_mod, kv_dtype):
+    """fp8 query with a scale that is not a power of two, so the fp32 rounding of code * scale matters."""
+    case = syn.make_case(3, [1, 23, 40], kv_dtype, seed=31, shuffle=True, extra_rows=5)
+    codes, scale = oracle_mod.quantize_q_fp8(case.q)
+    assert float(scale[0]) != 2.0 ** round(math.log2(float(scale[0])))
+    out, lse = oracle_mod.mla_decode_q8(codes, float(scale[0]), kv_dtype, case.kv, case.kv_scales,
+                                        case.kv_indptr, case.kv_indices)
+    ref_o, ref_l = _sdpa_ref(case, oracle_mod, q=_q8_decoded_torch(codes, scale[0]))
+    np.testing.assert_allclose(out, ref_o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, ref_l, rtol=1e-13, atol=1e-12)
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+def test_q8_exact_scale_equals_bf16_query(oracle_mod, kv_dtype):
+    """With a power-of-two scale every decoded query element (3 mantissa bits) is a bf16 value, so the
+    fp8-query route must reproduce the bf16-query route on those bf16 bits exactly."""
+    case = syn.make_case(2, [17, 6], kv_dtype, seed=32)
+    rng = np.random.default_rng(33)
+    codes = rng.integers(0, 256, size=case.q.shape, dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3C                       # no NaN codes
+    scale = 2.0 ** -5
+    qf = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32) * scale
+    qbits = qf.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert torch.equal(torch.from_numpy(qbits.view(np.int16)).view(torch.bfloat16).to(torch.float32), qf)
+    a = oracle_mod.mla_decode_q8(codes, scale, kv_dtype, case.kv, case.kv_scales, case.kv_indptr, case.kv_indices)
+    b = oracle_mod.mla_decode(qbits, kv_dtype, case.kv, case.kv_scales, case.kv_indptr, case.kv_indices)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
