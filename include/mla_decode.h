@@ -166,6 +166,60 @@ int mla_decode_paged(const void* q, const void* kv, const void* kv_scales, const
                      float* lse, int batch, int64_t total_kv, int kv_dtype, float sm_scale, void* workspace,
                      size_t workspace_bytes, int flags, void* stream);
 
+/* Query scale modes of mla_decode_q8. */
+#define MLA_Q_SCALE_STATIC 0  /* *q_scale is read: the caller's per-tensor scale (finite, > 0) */
+#define MLA_Q_SCALE_DYNAMIC 1 /* *q_scale is written: max(max |q|, 1e-12) / 448 over the query */
+
+/*
+ * mla_decode_q8: the decode attention with an fp8 query (the a8w8 path of
+ * submission 593653: `_quantize_q_static_into` / `_quantize_q_dynamic_into`
+ * before the attention; submission 754939, `quantize_fp8`). The bf16 query
+ * is quantised with one per-tensor fp32 scale,
+ *     code[b,h,d] = e4m3fn(clamp(q[b,h,d] / scale, -448, 448))
+ * (IEEE binary32 division, round to nearest even), and the attention defined
+ * at the top of this file runs with the decoded query code * scale in place
+ * of q. The quantisation runs inside the attention kernels; the dynamic scale
+ * adds one small reduction launch before them.
+ *   q             device bf16 [batch, 16, 576] (as mla_decode)
+ *   q_scale       device fp32 [1], 4-byte aligned: read (static) or written
+ *                 (dynamic, before the call's kernels finish)
+ *   q_scale_mode  MLA_Q_SCALE_STATIC or MLA_Q_SCALE_DYNAMIC
+ *   kv .. page_size, out, lse, batch, total_kv, kv_dtype, sm_scale, flags,
+ *   stream        as mla_decode_paged (page_size 1 is the layout of
+ *                 mla_decode; kv_last_page_len may then be NULL)
+ *   workspace     at least mla_decode_q8_workspace_size(...) bytes, 16-byte
+ *                 aligned (NULL allowed when that size is 0)
+ * Returns as mla_decode_paged; MLA_ERR_INVALID_ARG also for a bad
+ * q_scale_mode or a NULL / misaligned q_scale.
+ */
+int mla_decode_q8(const void* q, float* q_scale, int q_scale_mode, const void* kv, const void* kv_scales,
+                  const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                  int page_size, void* out, float* lse, int batch, int64_t total_kv, int kv_dtype, float sm_scale,
+                  void* workspace, size_t workspace_bytes, int flags, void* stream);
+
+/*
+ * mla_decode_q8_workspace_size: bytes of workspace mla_decode_q8 needs: the
+ * split partials of mla_decode_workspace_size(batch, total_kv, kv_dtype,
+ * flags), plus 1 KiB of partial maxima for the dynamic scale. For a paged
+ * call (page_size > 1) pass flags with MLA_FLAG_FORCE_SPLIT set. Returns 0
+ * for invalid arguments (mla_decode_q8 reports them).
+ */
+size_t mla_decode_q8_workspace_size(int batch, int64_t total_kv, int kv_dtype, int flags, int q_scale_mode);
+
+/*
+ * mla_quantize_q8_debug: the query quantisation of mla_decode_q8 on its own,
+ * through the same scale reduction and code routine (test aid for the
+ * bit-exact code check).
+ *   q          device bf16 [batch, 16, 576], 16-byte aligned
+ *   q_scale    device fp32 [1]: read (static) or written (dynamic)
+ *   codes      device uint8 [batch, 16, 576], 8-byte aligned: the e4m3fn codes
+ *   workspace  dynamic mode: at least 1 KiB, 16-byte aligned; else unused
+ * Returns MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_WORKSPACE_TOO_SMALL,
+ * MLA_ERR_UNSUPPORTED or MLA_ERR_HIP.
+ */
+int mla_quantize_q8_debug(const void* q, int batch, float* q_scale, int q_scale_mode, uint8_t* codes,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * mla_dequant_debug: decode `rows` physical cache rows to fp32 [rows, 576]
  * through the attention kernel's own staging and decode routines (test aid

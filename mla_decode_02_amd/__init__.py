@@ -19,14 +19,20 @@ from ._lib import (  # noqa: F401
     QK_DIM,
     V_DIM,
     MlaError,
+    Q_SCALE_DYNAMIC,
+    Q_SCALE_STATIC,
     PlanInfo,
     flags_for,
     mla_decode,
     mla_decode_paged,
     mla_decode_plan,
+    mla_decode_q8,
+    mla_decode_q8_workspace_size,
     mla_decode_workspace_size,
     mla_dequant_debug,
+    mla_quantize_q8_debug,
     mla_status_string,
     prepare_decode,
     prepare_decode_paged,
+    prepare_decode_q8,
 )

@@ -20,9 +20,10 @@ NUM_HEADS, QK_DIM, V_DIM = 16, 576, 512
 KV_BF16, KV_FP8_E4M3, KV_MXFP4 = 0, 1, 2
 FLAG_FORCE_SPLIT, FLAG_FORCE_PERSISTENT = 0x1, 0x2
 FLAG_SPLITS_SHIFT, FLAG_GRID_SHIFT = 8, 16
+Q_SCALE_STATIC, Q_SCALE_DYNAMIC = 0, 1
 
-_EXPORTS = ("mla_decode", "mla_decode_paged", "mla_decode_plan", "mla_decode_workspace_size",
-            "mla_dequant_debug", "mla_status_string")
+_EXPORTS = ("mla_decode", "mla_decode_paged", "mla_decode_q8", "mla_decode_plan", "mla_decode_workspace_size",
+            "mla_decode_q8_workspace_size", "mla_quantize_q8_debug", "mla_dequant_debug", "mla_status_string")
 
 
 class MlaError(RuntimeError):
@@ -62,6 +63,13 @@ def _load():
     lib.mla_decode_paged.restype = i32
     lib.mla_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i64, i32, ctypes.c_float, vp, sz, i32,
                                      vp]
+    lib.mla_decode_q8.restype = i32
+    lib.mla_decode_q8.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, i32, i64, i32, ctypes.c_float, vp, sz,
+                                  i32, vp]
+    lib.mla_decode_q8_workspace_size.restype = sz
+    lib.mla_decode_q8_workspace_size.argtypes = [i32, i64, i32, i32, i32]
+    lib.mla_quantize_q8_debug.restype = i32
+    lib.mla_quantize_q8_debug.argtypes = [vp, i32, vp, i32, vp, vp, sz, vp]
     lib.mla_decode_plan.restype = i32
     lib.mla_decode_plan.argtypes = [i32, i64, i32, i32, ctypes.POINTER(_Plan)]
     lib.mla_decode_workspace_size.restype = sz
@@ -102,6 +110,12 @@ def mla_decode_plan(batch: int, total_kv: int, kv_dtype: int, flags: int = 0) ->
 
 def mla_decode_workspace_size(batch: int, total_kv: int, kv_dtype: int, flags: int = 0) -> int:
     return int(_lib.mla_decode_workspace_size(int(batch), int(total_kv), int(kv_dtype), int(flags)))
+
+
+def mla_decode_q8_workspace_size(batch: int, total_kv: int, kv_dtype: int, flags: int = 0,
+                                 q_scale_mode: int = Q_SCALE_DYNAMIC) -> int:
+    return int(_lib.mla_decode_q8_workspace_size(int(batch), int(total_kv), int(kv_dtype), int(flags),
+                                                 int(q_scale_mode)))
 
 
 def _ptr(t):
@@ -275,3 +289,99 @@ def mla_dequant_debug(kv, kv_scales, kv_dtype: int, path: int = 0, out=None):
     if rc != 0:
         raise MlaError(rc, "mla_dequant_debug")
     return out
+
+
+def _check_q_scale(q_scale, q_scale_mode):
+    _need(q_scale_mode in (Q_SCALE_STATIC, Q_SCALE_DYNAMIC), f"unknown q_scale_mode {q_scale_mode}")
+    _need(q_scale is not None and q_scale.is_cuda and q_scale.dtype == torch.float32 and q_scale.numel() >= 1,
+          "q_scale must be a device fp32 tensor of >= 1 element")
+
+
+def mla_decode_q8(q, q_scale, kv, kv_scales, kv_indptr, kv_indices, out, lse=None, *, q_scale_mode: int,
+                  total_kv: int, kv_dtype: int, kv_last_page_len=None, page_size: int = 1, sm_scale: float = 0.0,
+                  workspace=None, flags: int = 0):
+    """Enqueue MLA decode with an fp8-quantised query (see include/mla_decode.h, mla_decode_q8).
+
+    q [B,16,576] bf16 (quantised inside the call); q_scale device fp32 [1]: read
+    (Q_SCALE_STATIC) or written (Q_SCALE_DYNAMIC). The cache arguments are those
+    of mla_decode_paged (page_size 1: those of mla_decode). Returns the workspace.
+    """
+    B = int(kv_indptr.shape[0]) - 1
+    _need(q.is_cuda and q.dtype == torch.bfloat16 and q.is_contiguous() and tuple(q.shape) == (B, NUM_HEADS, QK_DIM),
+          "q must be contiguous bf16 [batch, 16, 576]")
+    _check_q_scale(q_scale, q_scale_mode)
+    _check_kv(kv, kv_scales, kv_dtype)
+    _need(kv.shape[0] % max(int(page_size), 1) == 0, "kv rows must be a whole number of pages")
+    _need(kv_indptr.is_cuda and kv_indptr.dtype == torch.int32 and kv_indptr.is_contiguous(),
+          "kv_indptr must be a contiguous device int32 tensor")
+    _need(kv_indices.is_cuda and kv_indices.dtype == torch.int32 and kv_indices.is_contiguous(),
+          "kv_indices must be a contiguous device int32 tensor")
+    if page_size > 1:
+        _need(kv_last_page_len is not None and kv_last_page_len.is_cuda and kv_last_page_len.dtype == torch.int32
+              and kv_last_page_len.is_contiguous() and kv_last_page_len.numel() == B,
+              "kv_last_page_len must be a contiguous device int32 tensor [batch]")
+    else:
+        _need(kv_indices.numel() >= total_kv, "kv_indices must hold >= total_kv entries")
+    _need(out.is_cuda and out.dtype == torch.bfloat16 and out.is_contiguous() and tuple(out.shape) == (B, NUM_HEADS, V_DIM),
+          "out must be contiguous bf16 [batch, 16, 512]")
+    if lse is not None:
+        _need(lse.is_cuda and lse.dtype == torch.float32 and lse.is_contiguous() and tuple(lse.shape) == (B, NUM_HEADS),
+              "lse must be contiguous fp32 [batch, 16]")
+    plan_flags = flags | (FLAG_FORCE_SPLIT if page_size > 1 else 0)
+    need = mla_decode_q8_workspace_size(B, total_kv, kv_dtype, plan_flags, q_scale_mode)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = _lib.mla_decode_q8(_ptr(q), _ptr(q_scale), int(q_scale_mode), _ptr(kv), _ptr(kv_scales), _ptr(kv_indptr),
+                            _ptr(kv_indices), _ptr(kv_last_page_len), int(page_size), _ptr(out), _ptr(lse), B,
+                            int(total_kv), int(kv_dtype), float(sm_scale), _ptr(workspace), ws_bytes, int(flags),
+                            _stream(q.device))
+    if rc != 0:
+        raise MlaError(rc, "mla_decode_q8")
+    return workspace
+
+
+def prepare_decode_q8(q, q_scale, kv, kv_scales, kv_indptr, kv_indices, out, lse=None, *, q_scale_mode: int,
+                      total_kv: int, kv_dtype: int, kv_last_page_len=None, page_size: int = 1,
+                      sm_scale: float = 0.0, workspace=None, flags: int = 0):
+    """prepare_decode for mla_decode_q8: checks once (one checked call), then
+    returns a zero-argument callable that enqueues the same call."""
+    ws = mla_decode_q8(q, q_scale, kv, kv_scales, kv_indptr, kv_indices, out, lse, q_scale_mode=q_scale_mode,
+                       total_kv=total_kv, kv_dtype=kv_dtype, kv_last_page_len=kv_last_page_len,
+                       page_size=page_size, sm_scale=sm_scale, workspace=workspace, flags=flags)
+    B = int(kv_indptr.shape[0]) - 1
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    args = (_ptr(q), _ptr(q_scale), int(q_scale_mode), _ptr(kv), _ptr(kv_scales), _ptr(kv_indptr), _ptr(kv_indices),
+            _ptr(kv_last_page_len), int(page_size), _ptr(out), _ptr(lse), B, int(total_kv), int(kv_dtype),
+            float(sm_scale), _ptr(ws), ws_bytes, int(flags), _stream(q.device))
+    fn = _lib.mla_decode_q8
+    keep = (q, q_scale, kv, kv_scales, kv_indptr, kv_indices, kv_last_page_len, out, lse, ws)
+
+    def call():
+        rc = fn(*args)
+        if rc != 0:
+            raise MlaError(rc, "mla_decode_q8")
+        return keep
+
+    return call
+
+
+def mla_quantize_q8_debug(q, q_scale, q_scale_mode: int, codes=None, workspace=None):
+    """The query quantisation of mla_decode_q8 on its own: e4m3fn codes uint8 [B,16,576]
+    (q_scale read for Q_SCALE_STATIC, written for Q_SCALE_DYNAMIC). Returns codes."""
+    _need(q.is_cuda and q.dtype == torch.bfloat16 and q.is_contiguous() and q.dim() == 3
+          and tuple(q.shape[1:]) == (NUM_HEADS, QK_DIM), "q must be contiguous bf16 [batch, 16, 576]")
+    _check_q_scale(q_scale, q_scale_mode)
+    B = int(q.shape[0])
+    if codes is None:
+        codes = torch.empty((B, NUM_HEADS, QK_DIM), dtype=torch.uint8, device=q.device)
+    _need(codes.is_cuda and codes.dtype == torch.uint8 and codes.is_contiguous()
+          and tuple(codes.shape) == (B, NUM_HEADS, QK_DIM), "codes must be contiguous uint8 [batch, 16, 576]")
+    if workspace is None and q_scale_mode == Q_SCALE_DYNAMIC:
+        workspace = torch.empty(1024, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = _lib.mla_quantize_q8_debug(_ptr(q), B, _ptr(q_scale), int(q_scale_mode), _ptr(codes), _ptr(workspace),
+                                    ws_bytes, _stream(q.device))
+    if rc != 0:
+        raise MlaError(rc, "mla_quantize_q8_debug")
+    return codes

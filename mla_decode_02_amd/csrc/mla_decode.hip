@@ -82,6 +82,11 @@ struct Params {
     int grid;    // persistent: number of workgroups
     int total;   // kv_indptr[batch]
     float sm_scale;
+    // fp8 query only: the per-tensor scale (static: read; dynamic: written by
+    // workgroup 0) and, for the dynamic scale, the partial maxima of |q|.
+    float* q_scale;
+    const float* q_amax;
+    int q_amax_n;
 };
 
 // ---------------------------------------------------------------------------
@@ -327,23 +332,87 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// Eight e4m3fn codes per operand (byte k is k-slot 8G + k, as for bf16).
+__device__ __forceinline__ f32x4 mfma32(long a, long b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// fp8 query (the a8w8 path; submission 593653, `_quantize_q_static_into` and
+// `_quantize_q_dynamic_into`): the bf16 query is quantised with one per-tensor
+// fp32 scale, code = e4m3fn(clamp(q / scale, -448, 448)) rounded to nearest
+// even, and the attention uses the decoded query code * scale. The kernels
+// keep the codes and fold the scale into the score scale. Dynamic scale:
+// max(max |q|, 1e-12) / 448, reduced in two steps (q_amax_kernel writes
+// partial maxima, every stage-1 workgroup reduces them).
+// ---------------------------------------------------------------------------
+constexpr float kFp8Max = 448.0f;
+
+// Two fp32 values -> e4m3fn codes (v_cvt_pk_fp8_f32 rounds to nearest even;
+// the inputs are already clamped to the finite range) into half HI of w.
+template <bool HI>
+__device__ __forceinline__ uint32_t q8_pack2(float a, float b, uint32_t w) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)w, HI);
+}
+
+// Eight bf16 query elements -> eight e4m3fn codes (element k in byte k).
+// Each quotient is an IEEE binary32 division, as the definition states.
+__device__ __forceinline__ u32x2 q8_codes8(bf16x8 x, float scale) {
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = __builtin_amdgcn_fmed3f((float)x[e] / scale, -kFp8Max, kFp8Max);
+    u32x2 c;
+    c[0] = q8_pack2<true>(y[2], y[3], q8_pack2<false>(y[0], y[1], 0u));
+    c[1] = q8_pack2<true>(y[6], y[7], q8_pack2<false>(y[4], y[5], 0u));
+    return c;
+}
+
+// Dynamic scale from the partial maxima: `part` is this thread's partial
+// (0 for threads beyond the count); red is 4 floats of LDS. Contains a
+// workgroup barrier.
+__device__ __forceinline__ float q8_dynamic_scale(float part, float* red, int tid) {
+    float m = part;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    return fmaxf(m, 1e-12f) / kFp8Max;
+}
 
 constexpr int kHalfK = kKSteps / 2;            // 9 score k-steps per wave
 constexpr int kWaveBlocks = kBlocks / kWaves;  // 8 output blocks (128 columns) per wave
 
 // Partial scores of one wave: tile t, score k-steps kHalfK * HF .. +kHalfK-1.
 // Result: lane (G, r) holds S^T[token 4G+i of tile t][head r] over those dims.
-template <int KV, int HF>
-__device__ __forceinline__ f32x4 qk_partial(const uint8_t* step, const bf16x8 (&qB)[kHalfK], int t, int lane) {
+// With an fp8 query on the fp8 cache (QOp = long) the cache codes enter the
+// MFMA as they are: the eight bytes of row r at dims dbase(ks, G)..+7.
+template <int KV, int HF, typename QOp>
+__device__ __forceinline__ f32x4 qk_partial(const uint8_t* step, const QOp (&qB)[kHalfK], int t, int lane) {
     f32x4 e0 = {0.f, 0.f, 0.f, 0.f}, e1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < kHalfK; ++j) {
-        const bf16x8 k = qk_operand<KV>(step, t, kHalfK * HF + j, lane);
+        const int ks = kHalfK * HF + j;
+        QOp k;
+        if constexpr (__is_same(QOp, long)) {
+            static_assert(KV == MLA_KV_FP8_E4M3, "fp8 score operands need the fp8 cache");
+            k = *reinterpret_cast<const long*>(step + t * Fmt<KV>::kTileBytes + 1024 * (ks >> 1) + 16 * lane +
+                                               8 * (ks & 1));
+        } else {
+            k = qk_operand<KV>(step, t, ks, lane);
+        }
         if (j & 1) e1 = mfma32(k, qB[j], e1);
         else e0 = mfma32(k, qB[j], e0);
     }
     return e0 + e1;
 }
+
+// Query operand type: bf16 (also the decoded fp8 query codes, which bf16
+// holds exactly), or raw e4m3fn codes when both operands are fp8.
+template <int KV, int QF>
+struct QOperand { using T = bf16x8; };
+template <>
+struct QOperand<MLA_KV_FP8_E4M3, 1> { using T = long; };
 
 struct WaveAcc {
     f32x4 o[kWaveBlocks];  // o[j][i]: head 4G+i, column dcol(kWaveBlocks * wave + j, r)
@@ -537,8 +606,13 @@ __device__ __forceinline__ void wait_own(int groups, int hi) {
 // 9 (w / 2) .. +8, the partial scores are summed through LDS in a fixed order,
 // and every wave then runs the same softmax and accumulates P . V for its own
 // 128 output columns.
-template <int KV>
-__device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, int t1, bool final, int slot) {
+//
+// QF = 1: fp8 query. Q is quantised here (static scale read, or the dynamic
+// scale reduced from the partial maxima); `scale_out` makes this workgroup
+// publish a dynamic scale.
+template <int KV, int QF>
+__device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, int t1, bool final, int slot,
+                       bool scale_out) {
     using L = Layout<KV>;
     constexpr int R = Fmt<KV>::kRing;
     constexpr int D = R - 1;  // steps issued ahead of the one computed
@@ -553,7 +627,6 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
 
     float kv_scale = 1.0f;
     if constexpr (KV == MLA_KV_FP8_E4M3) kv_scale = *reinterpret_cast<const float*>(P.kv_scales);
-    const float qk_scale = P.sm_scale * kv_scale * kLog2e;
 
     // The first index window and this wave's half of Q^T are requested together
     // so that the workgroup start pays one memory round trip for both.
@@ -577,19 +650,42 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
         }
     };
     load_idx(t0, min(kIdxWindow, t1 - t0));
-    bf16x8 qB[kHalfK];
+    bf16x8 qraw[kHalfK];
     {
         const __bf16* qrow = P.q + ((int64_t)b * kHeads + r) * kDqk;
 #pragma unroll
         for (int j = 0; j < kHalfK; ++j)
-            qB[j] = *reinterpret_cast<const bf16x8*>(qrow + dbase<KV>(kHalfK * hf + j, G));
+            qraw[j] = *reinterpret_cast<const bf16x8*>(qrow + dbase<KV>(kHalfK * hf + j, G));
     }
-    // Consume Q^T and the scale here: the compiler's wait for these loads must
+    float q_scale = 1.0f, q_part = 0.0f;
+    if constexpr (QF) {
+        if (P.q_amax) q_part = tid < P.q_amax_n ? P.q_amax[tid] : 0.0f;
+        else q_scale = *P.q_scale;
+    }
+    // Consume Q^T and the scales here: the compiler's wait for these loads must
     // not land inside the token loop, where the count it waits for would also
     // drain the gathers in flight (it does not see the LDS-DMA loads).
 #pragma unroll
-    for (int j = 0; j < kHalfK; ++j) asm volatile("" ::"v"(qB[j]));
-    asm volatile("" ::"v"(qk_scale), "v"(kv_scale));
+    for (int j = 0; j < kHalfK; ++j) asm volatile("" ::"v"(qraw[j]));
+    asm volatile("" ::"v"(kv_scale), "v"(q_part), "v"(q_scale));
+
+    typename QOperand<KV, QF>::T qB[kHalfK];
+    if constexpr (QF) {
+        if (P.q_amax) {
+            q_scale = q8_dynamic_scale(q_part, reinterpret_cast<float*>(sbuf), tid);
+            if (scale_out && tid == 0) P.q_scale[0] = q_scale;
+        }
+#pragma unroll
+        for (int j = 0; j < kHalfK; ++j) {
+            const u32x2 c = q8_codes8(qraw[j], q_scale);
+            if constexpr (KV == MLA_KV_FP8_E4M3) qB[j] = __builtin_bit_cast(long, c);
+            else qB[j] = fp8x8_to_bf16(c[0], c[1]);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kHalfK; ++j) qB[j] = qraw[j];
+    }
+    const float qk_scale = P.sm_scale * kv_scale * q_scale * kLog2e;
 
     WaveAcc a;
 #pragma unroll
@@ -690,7 +786,7 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
 // identity; correctness never depends on where a workgroup runs.
 __device__ __forceinline__ int xcd_order(int x, int n) { return (n & 7) ? x : (x & 7) * (n >> 3) + (x >> 3); }
 
-template <int KV>
+template <int KV, int QF>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Fmt<KV>::kWgsPerCU, Fmt<KV>::kWgsPerCU)))
 void split_kernel(Params P) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[Layout<KV>::kBytes];
@@ -702,21 +798,31 @@ void split_kernel(Params P) {
     const int chunk = ((L + P.nsplit - 1) / P.nsplit + kStepTokens - 1) / kStepTokens * kStepTokens;
     const int t0 = min(L, s * chunk);
     const int t1 = min(L, t0 + chunk);
-    run_wg<KV>(P, smem, b, base, t0, t1, P.nsplit == 1, b * P.nsplit + s);
+    run_wg<KV, QF>(P, smem, b, base, t0, t1, P.nsplit == 1, b * P.nsplit + s, blockIdx.x == 0);
 }
 
 // Largest p whose share [floor(p T / G), floor((p+1) T / G)) starts at or before t.
 __device__ __forceinline__ int share_of(int64_t t, int64_t T, int64_t G) { return (int)(((t + 1) * G - 1) / T); }
 __device__ __forceinline__ int64_t share_start(int64_t p, int64_t T, int64_t G) { return p * T / G; }
 
-template <int KV>
+template <int KV, int QF>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Fmt<KV>::kWgsPerCU, Fmt<KV>::kWgsPerCU)))
 void persistent_kernel(Params P) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[Layout<KV>::kBytes];
     const int64_t T = P.total, Gn = P.grid;
     const int p = xcd_order(blockIdx.x, gridDim.x);
     const int64_t g0 = share_start(p, T, Gn), g1 = share_start(p + 1, T, Gn);
-    if (g0 >= g1) return;
+    if (g0 >= g1) {
+        // an empty share; workgroup 0 still publishes a dynamic query scale
+        if (QF && P.q_amax && blockIdx.x == 0) {
+            const int tid = threadIdx.x;
+            const float q = q8_dynamic_scale(tid < P.q_amax_n ? P.q_amax[tid] : 0.0f,
+                                             reinterpret_cast<float*>(smem), tid);
+            if (tid == 0) P.q_scale[0] = q;
+        }
+        return;
+    }
+    bool scale_out = blockIdx.x == 0;
     // first sequence b with indptr[b] <= g0 < indptr[b+1]
     int lo = 0, hi = P.batch - 1;
     while (lo < hi) {
@@ -730,7 +836,8 @@ void persistent_kernel(Params P) {
         if (t0 >= t1) continue;
         const bool whole = (s >= g0) && (e <= g1);
         __syncthreads();  // the previous sequence's epilogue has finished reading LDS
-        run_wg<KV>(P, smem, b, s, t0 - s, t1 - s, whole, p + b);  // page size 1: entries are tokens
+        run_wg<KV, QF>(P, smem, b, s, t0 - s, t1 - s, whole, p + b, scale_out);  // page size 1: entries are tokens
+        scale_out = false;
     }
 }
 
@@ -939,6 +1046,47 @@ __global__ __launch_bounds__(64) void dequant_kernel(Params P, int64_t rows, int
     }
 }
 
+// Dynamic fp8 query scale, first step: part[i] = max |q| over the query rows
+// of sequences [i B / n, (i + 1) B / n), n = gridDim.x (at most 256). The
+// magnitude of a bf16 value orders like its low 15 bits, so the maximum is
+// taken on those bits; it is exact in fp32.
+__global__ __launch_bounds__(256) void q_amax_kernel(const __bf16* q, int batch, float* part) {
+    __shared__ uint32_t red[4];
+    const int n = gridDim.x, i = blockIdx.x, tid = threadIdx.x;
+    const int64_t b0 = (int64_t)i * batch / n, b1 = (int64_t)(i + 1) * batch / n;
+    const u32x4* v = reinterpret_cast<const u32x4*>(q + b0 * kHeads * kDqk);
+    const int64_t cnt = (b1 - b0) * (kHeads * kDqk / 8);  // 16-byte vectors
+    uint32_t m = 0;
+    for (int64_t k = tid; k < cnt; k += 256) {
+        const u32x4 w = v[k];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = max(m, max(w[e] & 0x7fffu, (w[e] >> 16) & 0x7fffu));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    if (tid == 0) part[i] = __uint_as_float(max(max(red[0], red[1]), max(red[2], red[3])) << 16);
+}
+
+// Quantiser check: the e4m3fn codes of every query element, through the same
+// scale reduction and code routine as the attention kernels. Workgroup b
+// writes sequence b's 16 x 576 codes; workgroup 0 publishes a dynamic scale.
+__global__ __launch_bounds__(256) void q8_debug_kernel(Params P, uint8_t* codes) {
+    __shared__ float red[4];
+    const int tid = threadIdx.x, b = blockIdx.x;
+    float q_scale;
+    if (P.q_amax) {
+        q_scale = q8_dynamic_scale(tid < P.q_amax_n ? P.q_amax[tid] : 0.0f, red, tid);
+        if (b == 0 && tid == 0) P.q_scale[0] = q_scale;
+    } else {
+        q_scale = *P.q_scale;
+    }
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(P.q + (int64_t)b * kHeads * kDqk);
+    u32x2* dst = reinterpret_cast<u32x2*>(codes + (int64_t)b * kHeads * kDqk);
+    for (int k = tid; k < kHeads * kDqk / 8; k += 256) dst[k] = q8_codes8(src[k], q_scale);
+}
+
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
@@ -960,12 +1108,20 @@ static int check_device() {
     return ok ? MLA_OK : MLA_ERR_UNSUPPORTED;
 }
 
-template <int KV>
+// Partial-maximum workgroups of the dynamic query scale for `batch` sequences.
+static int q_amax_parts(int batch) { return batch < kQ8AmaxParts ? batch : kQ8AmaxParts; }
+
+template <int KV, int QF>
 static int launch(const mla_plan_info& plan, const Params& P, hipStream_t stream) {
+    if (QF && P.q_amax) {
+        hipLaunchKernelGGL(q_amax_kernel, dim3(P.q_amax_n), dim3(256), 0, stream, P.q, P.batch,
+                           const_cast<float*>(P.q_amax));
+        if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+    }
     if (plan.mode == 0)
-        hipLaunchKernelGGL(split_kernel<KV>, dim3(plan.grid), dim3(kThreads), 0, stream, P);
+        hipLaunchKernelGGL((split_kernel<KV, QF>), dim3(plan.grid), dim3(kThreads), 0, stream, P);
     else
-        hipLaunchKernelGGL(persistent_kernel<KV>, dim3(plan.grid), dim3(kThreads), 0, stream, P);
+        hipLaunchKernelGGL((persistent_kernel<KV, QF>), dim3(plan.grid), dim3(kThreads), 0, stream, P);
     if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
     if (plan.combine) {
         CombineParams C;
@@ -990,15 +1146,20 @@ static int launch(const mla_plan_info& plan, const Params& P, hipStream_t stream
 
 namespace mla {
 
-// Shared body of mla_decode (page size 1) and mla_decode_paged.
+// Shared body of mla_decode (page size 1), mla_decode_paged and mla_decode_q8
+// (q_mode < 0: bf16 query; else MLA_Q_SCALE_*, with q_scale).
 static int decode_impl(const void* q, const void* kv, const void* kv_scales, const int32_t* kv_indptr,
                        const int32_t* kv_indices, const int32_t* kv_last_page_len, int page_size, void* out,
                        float* lse, int batch, int64_t total_kv, int kv_dtype, float sm_scale, void* workspace,
-                       size_t workspace_bytes, int flags, void* stream) {
+                       size_t workspace_bytes, int flags, void* stream, int q_mode = -1, float* q_scale = nullptr) {
     mla_plan_info plan;
     int rc = make_plan(batch, total_kv, kv_dtype, flags, &plan);
     if (rc != MLA_OK) return rc;
+    const bool dyn = q_mode == MLA_Q_SCALE_DYNAMIC;
+    const size_t need = dyn ? q8_amax_offset(plan.workspace_bytes) + kQ8AmaxParts * sizeof(float)
+                            : plan.workspace_bytes;
     if (batch == 0) return MLA_OK;
+    if (q_mode >= 0 && (!q_scale || !aligned(q_scale, 4))) return MLA_ERR_INVALID_ARG;
     if (!q || !kv || !kv_indptr || !out) return MLA_ERR_INVALID_ARG;
     if (total_kv > 0 && !kv_indices) return MLA_ERR_INVALID_ARG;
     if (kv_dtype != MLA_KV_BF16 && !kv_scales) return MLA_ERR_INVALID_ARG;
@@ -1007,8 +1168,8 @@ static int decode_impl(const void* q, const void* kv, const void* kv_scales, con
         (kv_indices && !aligned(kv_indices, 4)) || (lse && !aligned(lse, 4)) ||
         (kv_dtype == MLA_KV_FP8_E4M3 && !aligned(kv_scales, 4)))
         return MLA_ERR_INVALID_ARG;
-    if (plan.workspace_bytes > 0) {
-        if (!workspace || workspace_bytes < plan.workspace_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE_TOO_SMALL;
         if (!aligned(workspace, 16)) return MLA_ERR_INVALID_ARG;
     }
     rc = check_device();
@@ -1033,12 +1194,24 @@ static int decode_impl(const void* q, const void* kv, const void* kv_scales, con
     P.grid = plan.grid;
     P.total = (int)total_kv;
     P.sm_scale = (sm_scale > 0.f) ? sm_scale : 1.0f / 24.0f;  // NaN compares false -> default
+    P.q_scale = q_scale;
+    P.q_amax = dyn ? reinterpret_cast<const float*>(reinterpret_cast<char*>(workspace) +
+                                                    q8_amax_offset(plan.workspace_bytes))
+                   : nullptr;
+    P.q_amax_n = dyn ? q_amax_parts(batch) : 0;
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (q_mode >= 0) {
+        switch (kv_dtype) {
+            case MLA_KV_BF16: return launch<MLA_KV_BF16, 1>(plan, P, s);
+            case MLA_KV_FP8_E4M3: return launch<MLA_KV_FP8_E4M3, 1>(plan, P, s);
+            default: return launch<MLA_KV_MXFP4, 1>(plan, P, s);
+        }
+    }
     switch (kv_dtype) {
-        case MLA_KV_BF16: return launch<MLA_KV_BF16>(plan, P, s);
-        case MLA_KV_FP8_E4M3: return launch<MLA_KV_FP8_E4M3>(plan, P, s);
-        default: return launch<MLA_KV_MXFP4>(plan, P, s);
+        case MLA_KV_BF16: return launch<MLA_KV_BF16, 0>(plan, P, s);
+        case MLA_KV_FP8_E4M3: return launch<MLA_KV_FP8_E4M3, 0>(plan, P, s);
+        default: return launch<MLA_KV_MXFP4, 0>(plan, P, s);
     }
 }
 
@@ -1065,6 +1238,51 @@ extern "C" int mla_decode_paged(const void* q, const void* kv, const void* kv_sc
     }
     return mla::decode_impl(q, kv, kv_scales, kv_indptr, kv_indices, kv_last_page_len, page_size, out, lse, batch,
                             total_kv, kv_dtype, sm_scale, workspace, workspace_bytes, flags, stream);
+}
+
+extern "C" int mla_decode_q8(const void* q, float* q_scale, int q_scale_mode, const void* kv, const void* kv_scales,
+                             const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                             int page_size, void* out, float* lse, int batch, int64_t total_kv, int kv_dtype,
+                             float sm_scale, void* workspace, size_t workspace_bytes, int flags, void* stream) {
+    if (q_scale_mode != MLA_Q_SCALE_STATIC && q_scale_mode != MLA_Q_SCALE_DYNAMIC) return MLA_ERR_INVALID_ARG;
+    if (page_size < 1 || page_size > (1 << 16)) return MLA_ERR_INVALID_ARG;
+    if (page_size > 1) {
+        if (flags & MLA_FLAG_FORCE_PERSISTENT) return MLA_ERR_INVALID_ARG;
+        flags |= MLA_FLAG_FORCE_SPLIT;
+    }
+    return mla::decode_impl(q, kv, kv_scales, kv_indptr, kv_indices, kv_last_page_len, page_size, out, lse, batch,
+                            total_kv, kv_dtype, sm_scale, workspace, workspace_bytes, flags, stream, q_scale_mode,
+                            q_scale);
+}
+
+extern "C" int mla_quantize_q8_debug(const void* q, int batch, float* q_scale, int q_scale_mode, uint8_t* codes,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+    using namespace mla;
+    if (q_scale_mode != MLA_Q_SCALE_STATIC && q_scale_mode != MLA_Q_SCALE_DYNAMIC) return MLA_ERR_INVALID_ARG;
+    if (batch < 0) return MLA_ERR_INVALID_ARG;
+    if (batch == 0) return MLA_OK;
+    if (!q || !q_scale || !codes || !aligned(q, 16) || !aligned(q_scale, 4) || !aligned(codes, 8))
+        return MLA_ERR_INVALID_ARG;
+    const bool dyn = q_scale_mode == MLA_Q_SCALE_DYNAMIC;
+    if (dyn && (!workspace || workspace_bytes < kQ8AmaxParts * sizeof(float))) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    if (dyn && !aligned(workspace, 16)) return MLA_ERR_INVALID_ARG;
+    int rc = check_device();
+    if (rc != MLA_OK) return rc;
+    Params P;
+    memset(&P, 0, sizeof P);
+    P.q = reinterpret_cast<const __bf16*>(q);
+    P.batch = batch;
+    P.q_scale = q_scale;
+    P.q_amax = dyn ? reinterpret_cast<const float*>(workspace) : nullptr;
+    P.q_amax_n = dyn ? q_amax_parts(batch) : 0;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (dyn) {
+        hipLaunchKernelGGL(q_amax_kernel, dim3(P.q_amax_n), dim3(256), 0, s, P.q, batch,
+                           reinterpret_cast<float*>(workspace));
+        if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+    }
+    hipLaunchKernelGGL(q8_debug_kernel, dim3(batch), dim3(256), 0, s, P, codes);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 extern "C" int mla_dequant_debug(int kv_dtype, const void* kv, const void* kv_scales, int64_t rows, int path,

@@ -31,6 +31,8 @@ static size_t partial_bytes(int num_partials) {
     return ((o + 255) / 256) * 256 + ((l + 255) / 256) * 256;
 }
 
+size_t q8_amax_offset(size_t plan_bytes) { return (plan_bytes + 255) & ~(size_t)255; }
+
 size_t partial_lse_offset(int num_partials) {
     size_t o = (size_t)num_partials * kHeads * kDv * sizeof(float);
     return ((o + 255) / 256) * 256;
@@ -134,6 +136,15 @@ extern "C" size_t mla_decode_workspace_size(int batch, int64_t total_kv, int kv_
     mla_plan_info p;
     if (mla::make_plan(batch, total_kv, kv_dtype, flags, &p) != MLA_OK) return 0;
     return p.workspace_bytes;
+}
+
+extern "C" size_t mla_decode_q8_workspace_size(int batch, int64_t total_kv, int kv_dtype, int flags,
+                                               int q_scale_mode) {
+    mla_plan_info p;
+    if (q_scale_mode != MLA_Q_SCALE_STATIC && q_scale_mode != MLA_Q_SCALE_DYNAMIC) return 0;
+    if (mla::make_plan(batch, total_kv, kv_dtype, flags, &p) != MLA_OK) return 0;
+    if (q_scale_mode == MLA_Q_SCALE_STATIC) return p.workspace_bytes;
+    return mla::q8_amax_offset(p.workspace_bytes) + mla::kQ8AmaxParts * sizeof(float);
 }
 
 extern "C" const char* mla_status_string(int status) {

@@ -19,6 +19,7 @@ constexpr int kStepTokens = 32;       // tokens per workgroup step (two 16-token
 constexpr int kMinTokensPerWg = 4 * kStepTokens;  // enough steps for the gather pipeline to overlap
 constexpr int kMaxSplits = 64;
 constexpr int kPersistentMinTokensPerCU = 1024;
+constexpr int kQ8AmaxParts = 256;     // partial maxima of the dynamic fp8 query scale (at most)
 
 // Stage-1 workgroups resident per compute unit (bound by the LDS ring size:
 // bf16 one, fp8 and MXFP4 two).
@@ -28,5 +29,7 @@ int make_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_inf
 int heuristic_splits(int batch, int64_t total_kv, int kv_dtype);
 int heuristic_grid(int64_t total_kv, int kv_dtype);
 size_t partial_lse_offset(int num_partials);
+// Offset of the dynamic fp8 query scale's partial maxima: after the plan's bytes.
+size_t q8_amax_offset(size_t plan_bytes);
 
 }  // namespace mla

@@ -35,7 +35,8 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("mla_decode", "mla_decode_plan", "mla_decode_workspace_size", "mla_dequant_debug", "mla_status_string"):
+    for n in ("mla_decode", "mla_decode_paged", "mla_decode_q8", "mla_decode_plan", "mla_decode_workspace_size",
+              "mla_decode_q8_workspace_size", "mla_quantize_q8_debug", "mla_dequant_debug", "mla_status_string"):
         assert n in names
 
 
@@ -185,6 +186,52 @@ def test_paged_validation(raw_lib, mla):
     # paged calls plan split-K: without a workspace a multi-split plan reports it
     assert _call_paged(raw_lib, flags=mla.flags_for(splits=4)) == -3
     assert _call_paged(raw_lib, batch=0, total=0) == 0
+
+
+def _call_q8(raw_lib, q_scale=A, mode=1, page_size=1, last=None, flags=0, batch=2, total=64, ws=None, ws_bytes=0):
+    f = raw_lib.mla_decode_q8
+    f.restype = ctypes.c_int
+    vp = ctypes.c_void_p
+    f.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, ctypes.c_int64,
+                  ctypes.c_int, ctypes.c_float, vp, ctypes.c_size_t, ctypes.c_int, vp]
+    return f(A, q_scale, mode, A, A, A, A, last, page_size, A, None, batch, total, 1, 0.0, ws, ws_bytes, flags, None)
+
+
+def test_q8_validation(raw_lib, mla):
+    assert _call_q8(raw_lib, mode=2) == -1
+    assert _call_q8(raw_lib, mode=-1) == -1
+    assert _call_q8(raw_lib, q_scale=None) == -1
+    assert _call_q8(raw_lib, q_scale=A + 2) == -1
+    assert _call_q8(raw_lib, page_size=0) == -1
+    assert _call_q8(raw_lib, page_size=8, last=None) == -1
+    assert _call_q8(raw_lib, page_size=8, last=A, flags=mla.flags_for(persistent=True)) == -1
+    # the dynamic scale needs its partial maxima even when the plan needs no partials
+    assert mla.mla_decode_workspace_size(2, 64, 1, mla.flags_for(splits=1)) == 0
+    assert _call_q8(raw_lib, flags=mla.flags_for(splits=1)) == -3
+    assert _call_q8(raw_lib, mode=0, q_scale=None, batch=0, total=0) == 0
+
+
+def test_q8_workspace_size(mla):
+    for flags in (0, mla.flags_for(splits=1), mla.flags_for(splits=8), mla.flags_for(persistent=True, grid=100)):
+        base = mla.mla_decode_workspace_size(32, 32 * 1024, 1, flags)
+        assert mla.mla_decode_q8_workspace_size(32, 32 * 1024, 1, flags, mla.Q_SCALE_STATIC) == base
+        dyn = mla.mla_decode_q8_workspace_size(32, 32 * 1024, 1, flags, mla.Q_SCALE_DYNAMIC)
+        assert dyn >= base + 1024 and dyn - 1024 == (base + 255) // 256 * 256
+    assert mla.mla_decode_q8_workspace_size(32, 1024, 1, 0, 7) == 0
+
+
+def test_quantize_q8_debug_validation(raw_lib):
+    f = raw_lib.mla_quantize_q8_debug
+    f.restype = ctypes.c_int
+    vp = ctypes.c_void_p
+    f.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, ctypes.c_size_t, vp]
+    assert f(A, 2, A, 3, A, A, 1024, None) == -1
+    assert f(A, -1, A, 0, A, None, 0, None) == -1
+    assert f(A + 2, 2, A, 0, A, None, 0, None) == -1
+    assert f(A, 2, None, 0, A, None, 0, None) == -1
+    assert f(A, 2, A, 1, A, None, 0, None) == -3
+    assert f(A, 2, A, 1, A, A, 1023, None) == -3
+    assert f(A, 0, None, 0, None, None, 0, None) == 0
 
 
 def test_batch_zero_is_a_noop(raw_lib):
