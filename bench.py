@@ -60,6 +60,9 @@ def parse_args():
                     help="skip measurement; run this many back-to-back calls of --workload (for profilers)")
     ap.add_argument("--cold", action="store_true",
                     help="with --only-gpu-loop: read-flush the caches before every call")
+    ap.add_argument("--q8", choices=["static", "dynamic"], default=None,
+                    help="with --only-gpu-loop: the fp8-query entry point (mla_decode_q8) with this Q scale mode")
+    ap.add_argument("--no-q8-grid", action="store_true", help="skip timing the fp8-query variants")
     return ap.parse_args()
 
 
@@ -89,11 +92,26 @@ def upload(case, dev):
     return q, kv, sc, torch.from_numpy(case.kv_indptr).to(dev), torch.from_numpy(case.kv_indices).to(dev)
 
 
-def prepare(mla, case, q, kv, sc, indptr, indices, out, lse, flags, dev):
-    """The pre-marshalled decode call: mla_decode, or mla_decode_paged for a paged workload."""
+# The pages' static fp8 query scale: absmax 6 over the e4m3fn maximum 448.
+STATIC_Q_SCALE = 6.0 / 448.0
+
+
+def prepare(mla, case, q, kv, sc, indptr, indices, out, lse, flags, dev, q8=None):
+    """The pre-marshalled decode call: mla_decode, or mla_decode_paged for a paged workload,
+    or mla_decode_q8 (fp8 query, `q8` = "static" / "dynamic" scale)."""
     import torch
 
     paged = case.meta.get("paged")
+    if q8 is not None:
+        mode = mla.Q_SCALE_STATIC if q8 == "static" else mla.Q_SCALE_DYNAMIC
+        q_scale = torch.tensor([STATIC_Q_SCALE], dtype=torch.float32, device=dev)
+        extra = {}
+        if paged is not None:
+            t = {k: torch.from_numpy(paged[k]).to(dev) for k in ("kv_indptr", "kv_indices", "kv_last_page_len")}
+            indptr, indices = t["kv_indptr"], t["kv_indices"]
+            extra = dict(kv_last_page_len=t["kv_last_page_len"], page_size=paged["page_size"])
+        return mla.prepare_decode_q8(q, q_scale, kv, sc, indptr, indices, out, lse, q_scale_mode=mode,
+                                     total_kv=case.total_kv, kv_dtype=case.kv_dtype, flags=flags, **extra)
     if paged is None:
         return mla.prepare_decode(q, kv, sc, indptr, indices, out, lse, total_kv=case.total_kv,
                                   kv_dtype=case.kv_dtype, flags=flags)
@@ -103,7 +121,7 @@ def prepare(mla, case, q, kv, sc, indptr, indices, out, lse, flags, dev):
                                     flags=flags)
 
 
-def measure(name, args, dev, flush):
+def measure(name, args, dev, flush, q8=None):
     import torch
 
     import mla_decode_02_amd as mla
@@ -114,7 +132,7 @@ def measure(name, args, dev, flush):
     B = case.batch
     out = torch.empty((B, 16, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, 16), dtype=torch.float32, device=dev)
-    call = prepare(mla, case, q, kv, sc, indptr, indices, out, lse, args.flags, dev)
+    call = prepare(mla, case, q, kv, sc, indptr, indices, out, lse, args.flags, dev, q8=q8)
     paged = case.meta.get("paged")
     plan_flags = args.flags | (mla.FLAG_FORCE_SPLIT if paged and paged["page_size"] > 1 else 0)
     plan = mla.mla_decode_plan(B, case.total_kv, case.kv_dtype, plan_flags)
@@ -149,6 +167,7 @@ def measure(name, args, dev, flush):
     kv_bytes, tot_bytes = case.kv_bytes(), case.total_bytes()
     return {
         "workload": name,
+        "query": "bf16" if q8 is None else f"fp8 ({q8} per-tensor scale)",
         "kv_format": syn.KV_NAMES[case.kv_dtype],
         "page_size": case.meta.get("paged", {}).get("page_size", 1),
         "batch": B,
@@ -241,14 +260,14 @@ def main():
         q, kv, sc, indptr, indices = upload(case, dev)
         out = torch.empty((case.batch, 16, 512), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((case.batch, 16), dtype=torch.float32, device=dev)
-        call = prepare(mla, case, q, kv, sc, indptr, indices, out, lse, args.flags, dev)
+        call = prepare(mla, case, q, kv, sc, indptr, indices, out, lse, args.flags, dev, q8=args.q8)
         flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev) if args.cold else None
         for _ in range(args.only_gpu_loop):
             if flush is not None:
                 flush_read(flush)
             call()
         torch.cuda.synchronize()
-        print(json.dumps({"workload": args.workload, "calls": args.only_gpu_loop}), flush=True)
+        print(json.dumps({"workload": args.workload, "q8": args.q8, "calls": args.only_gpu_loop}), flush=True)
         return
 
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
@@ -260,6 +279,19 @@ def main():
         print(f"# {n}: cold {r['cold_us_median']:.2f} us (p10 {r['cold_us_p10']:.2f}, p90 {r['cold_us_p90']:.2f}), "
               f"warm {r['warm_us']:.2f} us, {r['effective_kv_GBps']:.0f} GB/s KV ({r['pct_hbm_peak_kv']:.1f}% of 8 TB/s)",
               file=sys.stderr, flush=True)
+    # The fp8-query entry point (the pages' a8w8 path) on the same workloads,
+    # with the static and with the dynamic query scale.
+    grid_q8 = None
+    if not args.no_q8_grid:
+        grid_q8 = {}
+        todo = [(n, mode) for n in names for mode in ("static", "dynamic")]
+        for n, mode in todo:
+            r = measure(n, args, dev, flush, q8=mode)
+            r.pop("_case", None)
+            grid_q8[f"{n}/{mode}"] = r
+            print(f"# q8 {mode} {n}: cold {r['cold_us_median']:.2f} us, warm {r['warm_us']:.2f} us, "
+                  f"{r['effective_kv_GBps']:.0f} GB/s KV ({r['pct_hbm_peak_kv']:.1f}% of 8 TB/s)",
+                  file=sys.stderr, flush=True)
     head = results[args.workload]
     case = head.pop("_case")
     for r in results.values():
@@ -312,6 +344,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "grid": results,
+        "grid_q8": grid_q8,
         "sweep": sweep,
         "kernel_source_hash": source_hash(),
         "host": platform.node(),

@@ -156,6 +156,7 @@ struct Layout {
     static_assert(kBytes * Fmt<KV>::kWgsPerCU <= 160 * 1024, "stage-1 LDS exceeds 160 KiB per CU");
     static_assert(Fmt<KV>::kIdxWindow % kThreads == 0, "index window is loaded by whole workgroups");
     static_assert(Fmt<KV>::kTileBytes % 16 == 0, "tiles stay 16-byte aligned");
+    static_assert(kStepBytes >= kHeads * kDqk, "a ring slot holds one sequence's fp8 query codes");
 };
 
 // First score dim of the eight held by lane group G in k-step ks. Q^T is
@@ -355,16 +356,69 @@ __device__ __forceinline__ uint32_t q8_pack2(float a, float b, uint32_t w) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)w, HI);
 }
 
+// Division by the query scale, rounded like an IEEE binary32 division
+// wherever the e4m3fn code can depend on it. Fast form, for
+// 2^-80 <= s <= 2^80: x is first clamped to +-1024 s (a quotient beyond
+// +-1024 codes to +-448 either way, and the clamp keeps every intermediate
+// finite); then y = x * inv with inv = RN(1 / s), followed by two residual
+// corrections y += (x - y s) inv, each residual exact by FMA; a zero quotient
+// takes the sign of x. This equals RN(x / s) whenever |x / s| >= 2^-12 (below
+// that every quotient codes to a zero of x's sign). Other scales take the
+// IEEE division itself. The choice is uniform over the launch.
+struct Q8Div {
+    float s, inv, lim;
+    bool fast;
+};
+__device__ __forceinline__ Q8Div q8_divider(float s) {
+    return {s, 1.0f / s, 1024.0f * s, s >= 0x1p-80f && s <= 0x1p80f};
+}
+template <bool FAST>
+__device__ __forceinline__ float q8_div(float x, const Q8Div& d) {
+    if constexpr (!FAST) {
+        return x / d.s;
+    } else {
+        x = __builtin_amdgcn_fmed3f(x, -d.lim, d.lim);
+        const float y0 = x * d.inv;
+        float y = fmaf(fmaf(-y0, d.s, x), d.inv, y0);
+        y = fmaf(fmaf(-y, d.s, x), d.inv, y);
+        return __uint_as_float(__float_as_uint(y) | (__float_as_uint(x) & 0x80000000u));
+    }
+}
+
 // Eight bf16 query elements -> eight e4m3fn codes (element k in byte k).
-// Each quotient is an IEEE binary32 division, as the definition states.
-__device__ __forceinline__ u32x2 q8_codes8(bf16x8 x, float scale) {
+template <bool FAST>
+__device__ __forceinline__ u32x2 q8_codes8(bf16x8 x, const Q8Div& d) {
     float y[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = __builtin_amdgcn_fmed3f((float)x[e] / scale, -kFp8Max, kFp8Max);
+    for (int e = 0; e < 8; ++e) y[e] = __builtin_amdgcn_fmed3f(q8_div<FAST>((float)x[e], d), -kFp8Max, kFp8Max);
     u32x2 c;
     c[0] = q8_pack2<true>(y[2], y[3], q8_pack2<false>(y[0], y[1], 0u));
     c[1] = q8_pack2<true>(y[6], y[7], q8_pack2<false>(y[4], y[5], 0u));
     return c;
+}
+
+// Scales outside the fast form's range: the same codes through the IEEE
+// division, reading the query from src (global memory) again. Kept out of
+// line so that its instructions are never fetched in the common case.
+__device__ __noinline__ void q8_quantise_slow(const __bf16* src, int tid, int step, int n, float scale, uint8_t* dst) {
+    const Q8Div dv = q8_divider(scale);
+    for (int k = tid; k < n; k += step)
+        *reinterpret_cast<u32x2*>(dst + 8 * k) = q8_codes8<false>(*reinterpret_cast<const bf16x8*>(src + 8 * k), dv);
+}
+
+// Codes of query groups tid, tid + step, ... (< n) into dst (8 bytes per
+// group); g holds this thread's groups, src is the query in global memory.
+template <int PER>
+__device__ __forceinline__ void q8_quantise(const bf16x8 (&g)[PER], const __bf16* src, int tid, int step, int n,
+                                            float scale, uint8_t* dst) {
+    const Q8Div dv = q8_divider(scale);
+    if (__builtin_amdgcn_readfirstlane((int)dv.fast)) {
+#pragma unroll
+        for (int k = 0; k < PER; ++k)
+            if (tid + k * step < n) *reinterpret_cast<u32x2*>(dst + 8 * (tid + k * step)) = q8_codes8<true>(g[k], dv);
+    } else {
+        q8_quantise_slow(src, tid, step, n, scale, dst);
+    }
 }
 
 // Dynamic scale from the partial maxima: `part` is this thread's partial
@@ -650,40 +704,44 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
         }
     };
     load_idx(t0, min(kIdxWindow, t1 - t0));
-    bf16x8 qraw[kHalfK];
-    {
-        const __bf16* qrow = P.q + ((int64_t)b * kHeads + r) * kDqk;
-#pragma unroll
-        for (int j = 0; j < kHalfK; ++j)
-            qraw[j] = *reinterpret_cast<const bf16x8*>(qrow + dbase<KV>(kHalfK * hf + j, G));
-    }
+    // bf16 query: this wave's half of Q^T straight into the score operands.
+    // fp8 query: thread tid loads the 8-element groups tid, tid + 256, ... of
+    // the sequence's 16 x 576 query, which are quantised once per workgroup
+    // after the first gathers are issued (below).
+    constexpr int kQGroups = kHeads * kDqk / 8;
+    constexpr int kQPer = (kQGroups + kThreads - 1) / kThreads;
+    using QOp = typename QOperand<KV, QF>::T;
+    QOp qB[kHalfK];
+    bf16x8 qg[QF ? kQPer : 1];
     float q_scale = 1.0f, q_part = 0.0f;
+    const __bf16* qseq = P.q + (int64_t)b * kHeads * kDqk;
     if constexpr (QF) {
+#pragma unroll
+        for (int k = 0; k < kQPer; ++k) {
+            qg[k] = bf16x8{};
+            if (tid + k * kThreads < kQGroups) qg[k] = *reinterpret_cast<const bf16x8*>(qseq + 8 * (tid + k * kThreads));
+        }
         if (P.q_amax) q_part = tid < P.q_amax_n ? P.q_amax[tid] : 0.0f;
         else q_scale = *P.q_scale;
+#pragma unroll
+        for (int k = 0; k < kQPer; ++k) asm volatile("" ::"v"(qg[k]));
+    } else {
+        const __bf16* qrow = qseq + r * kDqk;
+#pragma unroll
+        for (int j = 0; j < kHalfK; ++j)
+            qB[j] = *reinterpret_cast<const bf16x8*>(qrow + dbase<KV>(kHalfK * hf + j, G));
+#pragma unroll
+        for (int j = 0; j < kHalfK; ++j) asm volatile("" ::"v"(qB[j]));
     }
-    // Consume Q^T and the scales here: the compiler's wait for these loads must
+    // Consume Q and the scales here: the compiler's wait for these loads must
     // not land inside the token loop, where the count it waits for would also
     // drain the gathers in flight (it does not see the LDS-DMA loads).
-#pragma unroll
-    for (int j = 0; j < kHalfK; ++j) asm volatile("" ::"v"(qraw[j]));
     asm volatile("" ::"v"(kv_scale), "v"(q_part), "v"(q_scale));
-
-    typename QOperand<KV, QF>::T qB[kHalfK];
     if constexpr (QF) {
         if (P.q_amax) {
             q_scale = q8_dynamic_scale(q_part, reinterpret_cast<float*>(sbuf), tid);
             if (scale_out && tid == 0) P.q_scale[0] = q_scale;
         }
-#pragma unroll
-        for (int j = 0; j < kHalfK; ++j) {
-            const u32x2 c = q8_codes8(qraw[j], q_scale);
-            if constexpr (KV == MLA_KV_FP8_E4M3) qB[j] = __builtin_bit_cast(long, c);
-            else qB[j] = fp8x8_to_bf16(c[0], c[1]);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < kHalfK; ++j) qB[j] = qraw[j];
     }
     const float qk_scale = P.sm_scale * kv_scale * q_scale * kLog2e;
 
@@ -719,8 +777,25 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
 #pragma unroll
         for (int d = 0; d < D; ++d)
             if (d < nsteps) issue_step(d);
+        // fp8 query, first window: quantise while the first gathers are in
+        // flight. The codes ([head][576] bytes) pass through ring slot D, whose
+        // step is issued only after the next two barriers.
+        uint8_t* qcodes = smem + (D % R) * L::kStepBytes;
+        if constexpr (QF) {
+            if (w0 == t0) q8_quantise<kQPer>(qg, qseq, tid, kThreads, kQGroups, q_scale, qcodes);
+        }
         wait_own<KV>(min(D - 1, nsteps - 1), hf);
-        __syncthreads();  // step 0 has landed
+        __syncthreads();  // step 0 has landed (and the query codes are written)
+        if constexpr (QF) {
+            if (w0 == t0) {
+#pragma unroll
+                for (int j = 0; j < kHalfK; ++j) {
+                    const u32x2 c = *reinterpret_cast<const u32x2*>(qcodes + r * kDqk + dbase<KV>(kHalfK * hf + j, G));
+                    if constexpr (__is_same(QOp, long)) qB[j] = __builtin_bit_cast(long, c);
+                    else qB[j] = fp8x8_to_bf16(c[0], c[1]);
+                }
+            }
+        }
         put_scores(0, scores(0));
         // Software pipeline: iteration s computes the scores of step s + 1
         // while it runs the softmax and P . V of step s, so the score MFMAs
@@ -1056,11 +1131,20 @@ __global__ __launch_bounds__(256) void q_amax_kernel(const __bf16* q, int batch,
     const int64_t b0 = (int64_t)i * batch / n, b1 = (int64_t)(i + 1) * batch / n;
     const u32x4* v = reinterpret_cast<const u32x4*>(q + b0 * kHeads * kDqk);
     const int64_t cnt = (b1 - b0) * (kHeads * kDqk / 8);  // 16-byte vectors
+    constexpr int kInFlight = 8;                           // loads per thread issued together
     uint32_t m = 0;
-    for (int64_t k = tid; k < cnt; k += 256) {
-        const u32x4 w = v[k];
+    for (int64_t base = 0; base < cnt; base += 256 * kInFlight) {
+        u32x4 w[kInFlight];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) m = max(m, max(w[e] & 0x7fffu, (w[e] >> 16) & 0x7fffu));
+        for (int u = 0; u < kInFlight; ++u) {
+            const int64_t k = base + tid + 256 * u;
+            w[u] = u32x4{0u, 0u, 0u, 0u};
+            if (k < cnt) w[u] = v[k];
+        }
+#pragma unroll
+        for (int u = 0; u < kInFlight; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m = max(m, max(w[u][e] & 0x7fffu, (w[u][e] >> 16) & 0x7fffu));
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
@@ -1082,9 +1166,16 @@ __global__ __launch_bounds__(256) void q8_debug_kernel(Params P, uint8_t* codes)
     } else {
         q_scale = *P.q_scale;
     }
+    constexpr int kGroups = kHeads * kDqk / 8, kPer = (kGroups + 255) / 256;
     const bf16x8* src = reinterpret_cast<const bf16x8*>(P.q + (int64_t)b * kHeads * kDqk);
-    u32x2* dst = reinterpret_cast<u32x2*>(codes + (int64_t)b * kHeads * kDqk);
-    for (int k = tid; k < kHeads * kDqk / 8; k += 256) dst[k] = q8_codes8(src[k], q_scale);
+    bf16x8 g[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        g[k] = bf16x8{};
+        if (tid + 256 * k < kGroups) g[k] = src[tid + 256 * k];
+    }
+    q8_quantise<kPer>(g, P.q + (int64_t)b * kHeads * kDqk, tid, 256, kGroups, q_scale,
+                      codes + (int64_t)b * kHeads * kDqk);
 }
 
 // ---------------------------------------------------------------------------

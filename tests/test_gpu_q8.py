@@ -108,7 +108,9 @@ def _all_finite_bf16_query():
     return q.reshape(B, 16, 576)
 
 
-@pytest.mark.parametrize("scale", [1.0, 0.0133928571, STATIC_SCALE, 3.0e-5])
+# 2^-90 and 2^85 lie outside the range where the kernels use the FMA-corrected
+# reciprocal; they take the IEEE division instead.
+@pytest.mark.parametrize("scale", [1.0, 0.0133928571, STATIC_SCALE, 3.0e-5, 0.7390851, 2.0 ** -90, 2.0 ** 85])
 def test_quantiser_static_all_bf16_values(mla, orc, dev, scale):
     q = _all_finite_bf16_query()
     qt = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).to(dev)
