@@ -82,6 +82,12 @@ def _load():
         ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
     ]
+    lib.oracle_mla_decode_mtp.restype = ctypes.c_int
+    lib.oracle_mla_decode_mtp.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+    ]
     lib.oracle_e4m3fn_encode.restype = ctypes.c_uint8
     lib.oracle_e4m3fn_encode.argtypes = [ctypes.c_float]
     lib.oracle_quantize_q_fp8.restype = ctypes.c_int
@@ -185,6 +191,36 @@ def mla_decode_q8(q_codes: np.ndarray, q_scale: float, kv_dtype: int, kv: np.nda
     )
     if rc != 0:
         raise ValueError("oracle_mla_decode_q8: invalid argument")
+    return out, lse
+
+
+def mla_decode_mtp(q: np.ndarray, qo_indptr: np.ndarray, causal: bool, kv_dtype: int, kv: np.ndarray,
+                   scales: np.ndarray | None, kv_indptr: np.ndarray, kv_indices: np.ndarray, sm_scale: float = SM_SCALE,
+                   rows=None, route: int = ROUTE_MAIN, nthreads: int = 0):
+    """Reference MLA decode with several query tokens per sequence: q bf16 bits
+    [total_q, 16, 576], qo_indptr [B+1]; causal as in oracle_mla_decode_mtp.
+    Returns (out [n,16,512] f64, lse [n,16] f64) for the listed query rows (all by default)."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    qo_indptr = np.ascontiguousarray(qo_indptr, dtype=np.int32)
+    kv = np.ascontiguousarray(kv)
+    scales = None if scales is None else np.ascontiguousarray(scales)
+    kv_indptr = np.ascontiguousarray(kv_indptr, dtype=np.int32)
+    kv_indices = np.ascontiguousarray(kv_indices, dtype=np.int32)
+    batch = kv_indptr.shape[0] - 1
+    if rows is None:
+        rlist, n = None, int(qo_indptr[batch])
+    else:
+        rlist = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+        n = rlist.shape[0]
+    out = np.zeros((n, NUM_HEADS, DV), dtype=np.float64)
+    lse = np.zeros((n, NUM_HEADS), dtype=np.float64)
+    rc = _load().oracle_mla_decode_mtp(
+        _ptr(q), _ptr(qo_indptr), int(bool(causal)), kv_dtype, _ptr(kv), _ptr(scales), _ptr(kv_indptr),
+        _ptr(kv_indices) if kv_indices.size else None, batch, float(sm_scale), _ptr(rlist), n, route, nthreads,
+        _ptr(out), _ptr(lse),
+    )
+    if rc != 0:
+        raise ValueError("oracle_mla_decode_mtp: invalid argument")
     return out, lse
 
 

@@ -425,6 +425,70 @@ int oracle_mla_decode_q8(const uint8_t* q_codes, float q_scale, int kv_dtype, co
 }
 
 /*
+ * Several query tokens per sequence (multi-token decode: MTP / speculative
+ * decoding, the pages' `qo_indptr` with q_seq_len tokens per sequence):
+ * query row r belongs to the sequence b with qo_indptr[b] <= r <
+ * qo_indptr[b+1]; it is token i = r - qo_indptr[b] of that sequence's
+ * n = qo_indptr[b+1] - qo_indptr[b] query tokens. It attends
+ *   causal = 0: every cache token of sequence b;
+ *   causal = 1: the first L - n + 1 + i tokens (the query tokens are the
+ *               sequence's last n positions; the last one sees all L tokens,
+ *               earlier ones one token fewer each; none when that count <= 0).
+ * q is bf16 [total_q, 16, 576]; rows (optional) lists the query rows to
+ * compute (n_list of them), else all total_q = qo_indptr[batch]; out and lse
+ * get one entry per computed row. route 0: single pass; 1: brute force.
+ */
+int oracle_mla_decode_mtp(const uint16_t* q, const int32_t* qo_indptr, int causal, int kv_dtype, const void* kv,
+                          const void* scales, const int32_t* kv_indptr, const int32_t* kv_indices, int batch,
+                          double sm_scale, const int32_t* rows, int n_list, int route, int nthreads, double* out,
+                          double* lse) {
+    int i, total_q;
+    if (!q || !qo_indptr || !kv || !kv_indptr || !out || !lse || batch < 1 || n_list < 0) return -1;
+    if (kv_dtype < 0 || kv_dtype > 2 || (kv_dtype != OR_KV_BF16 && !scales)) return -1;
+    if (route < 0 || route > 1 || causal < 0 || causal > 1) return -1;
+    total_q = qo_indptr[batch];
+    if (!rows) n_list = total_q;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    for (i = 0; i < n_list; ++i) {
+        int r = rows ? rows[i] : i;
+        int b = 0, h;
+        int64_t start, L, n, t;
+        double* x;
+        if (r < 0 || r >= total_q) return -1;
+        while (!(qo_indptr[b] <= r && r < qo_indptr[b + 1])) ++b;  /* the sequence holding row r */
+        n = (int64_t)qo_indptr[b + 1] - qo_indptr[b];
+        t = r - qo_indptr[b];
+        start = kv_indptr[b];
+        L = (int64_t)kv_indptr[b + 1] - start;
+        if (L < 0) return -1;
+        if (causal) {
+            L = L - n + 1 + t;
+            if (L < 0) L = 0;
+        }
+        if (L > 0 && !kv_indices) return -1;
+        x = gather_sequence(kv_dtype, kv, scales, kv_indices, start, L);
+        if (!x) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+        for (h = 0; h < OR_HEADS; ++h) {
+            double qh[OR_DQK];
+            double* o = out + ((int64_t)i * OR_HEADS + h) * OR_DV;
+            double* l = lse + (int64_t)i * OR_HEADS + h;
+            decode_query(0, q, 1.0f, (int64_t)r * OR_HEADS + h, qh);
+            if (route == 0)
+                attend_head(qh, x, 0, L, sm_scale, o, l);
+            else
+                attend_head_brute(qh, x, L, sm_scale, o, l);
+        }
+        free(x);
+    }
+    return 0;
+}
+
+/*
  * Nearest e4m3fn code to a binary32 value, ties to the code with an even
  * mantissa (round to nearest even), by search over the 127 non-negative finite
  * codes. |x| above 448 saturates to 448 (the quantiser clamps before it

@@ -178,6 +178,18 @@ def make_case(batch: int, kv_lens, kv_dtype: int, seed: int, shuffle: bool = Fal
                 meta={"batch": batch, "seed": seed, "shuffle": shuffle, "kv_dtype": KV_NAMES[kv_dtype]})
 
 
+def make_mtp_query(q_lens, seed: int):
+    """Query for several tokens per sequence (multi-token decode): bf16 bits
+    [total_q, 16, 576] ~ N(0, 1) and qo_indptr [B + 1] with q_lens[b] query
+    tokens in sequence b."""
+    lens = np.asarray(q_lens, dtype=np.int64)
+    qo = np.zeros(lens.shape[0] + 1, dtype=np.int64)
+    qo[1:] = np.cumsum(lens)
+    rng = np.random.default_rng(seed)
+    q = f32_to_bf16_bits(rng.standard_normal((int(qo[-1]), NUM_HEADS, DQK), dtype=np.float32))
+    return q, qo.astype(np.int32)
+
+
 def make_paged_case(batch: int, kv_lens, kv_dtype: int, page_size: int, seed: int, shuffle: bool = True,
                     extra_pages: int = 0):
     """A seeded workload over a paged cache: each sequence's tokens fill whole

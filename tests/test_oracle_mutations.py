@@ -32,6 +32,10 @@ MUTANTS = {
     "encode_drops_sign": ("signbit(x) ? (best | 0x80) : best", "best"),
     "quant_scale_inverted": ("s = amax / 448.0f;", "s = 448.0f / amax;"),
     "quant_multiplies": ("oracle_bf16_value(q[i]) / s;", "oracle_bf16_value(q[i]) * s;"),
+    "mtp_causal_off_by_one": ("L = L - n + 1 + t;", "L = L - n + t;"),
+    "mtp_token_order": ("t = r - qo_indptr[b];", "t = n - 1 - (r - qo_indptr[b]);"),
+    "mtp_query_row": ("decode_query(0, q, 1.0f, (int64_t)r * OR_HEADS + h, qh);",
+                      "decode_query(0, q, 1.0f, (int64_t)b * OR_HEADS + h, qh);"),
 }
 
 

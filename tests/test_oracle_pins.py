@@ -404,3 +404,80 @@ def test_q8_exact_scale_equals_bf16_query(oracle_mod, kv_dtype):
     a = oracle_mod.mla_decode_q8(codes, scale, kv_dtype, case.kv, case.kv_scales, case.kv_indptr, case.kv_indices)
     b = oracle_mod.mla_decode(qbits, kv_dtype, case.kv, case.kv_scales, case.kv_indptr, case.kv_indices)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# --------------------------------------------------------------------------- several query tokens
+
+def _mtp_sdpa_ref(case, q_bits, qo, causal, oracle_mod, sm_scale=1.0 / 24.0):
+    """torch fp64 SDPA per sequence with an explicit visibility mask (bottom-right causal or none)."""
+    x = _decoded_torch(case, oracle_mod)
+    q = torch.from_numpy(q_bits.view(np.int16)).view(torch.bfloat16).to(torch.float64)
+    outs, lses = [], []
+    for b in range(case.batch):
+        s, e = int(case.kv_indptr[b]), int(case.kv_indptr[b + 1])
+        r0, r1 = int(qo[b]), int(qo[b + 1])
+        n, L = r1 - r0, e - s
+        K = x[torch.from_numpy(case.kv_indices[s:e].astype(np.int64))]
+        for t in range(n):
+            vis = L - n + 1 + t if causal else L
+            vis = max(0, min(L, vis))
+            qt = q[r0 + t]                                    # [16, 576]
+            if vis == 0:
+                outs.append(torch.zeros(16, 512, dtype=torch.float64))
+                lses.append(torch.full((16,), -math.inf, dtype=torch.float64))
+                continue
+            mask = torch.zeros(1, 1, 1, L, dtype=torch.bool)
+            mask[..., :vis] = True
+            o = torch.nn.functional.scaled_dot_product_attention(
+                qt[None, :, None, :], K[None, None].expand(1, 16, -1, -1),
+                K[:, :512].contiguous()[None, None].expand(1, 16, -1, -1), attn_mask=mask, scale=sm_scale)
+            outs.append(o[0, :, 0, :])
+            lses.append(torch.logsumexp((qt @ K[:vis].T) * sm_scale, dim=1))
+    return torch.stack(outs).numpy(), torch.stack(lses).numpy()
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+@pytest.mark.parametrize("causal", [False, True])
+def test_mtp_vs_torch_sdpa_masked(oracle_mod, kv_dtype, causal):
+    """Ragged query counts (1..4, one sequence shorter than its query count) against masked SDPA."""
+    case = syn.make_case(4, [9, 2, 30, 17], kv_dtype, seed=41, shuffle=True, extra_rows=3)
+    q, qo = syn.make_mtp_query([1, 3, 2, 4], seed=42)
+    out, lse = oracle_mod.mla_decode_mtp(q, qo, causal, kv_dtype, case.kv, case.kv_scales, case.kv_indptr,
+                                         case.kv_indices)
+    ref_o, ref_l = _mtp_sdpa_ref(case, q, qo, causal, oracle_mod)
+    np.testing.assert_allclose(out, ref_o, rtol=1e-12, atol=1e-13)
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(np.isneginf(lse), ~fin)
+    np.testing.assert_allclose(lse[fin], ref_l[fin], rtol=1e-13, atol=1e-12)
+    if causal:
+        assert (~fin).any()   # the 2-token sequence with 3 query tokens: its first query sees nothing
+
+
+def test_mtp_causal_first_query_sees_one_row(oracle_mod):
+    """n query tokens over n cache tokens, causal: query 0 sees only row 0, so its output is that row's V."""
+    case = syn.make_case(1, [5], syn.KV_BF16, seed=43)
+    q, qo = syn.make_mtp_query([5], seed=44)
+    out, lse = oracle_mod.mla_decode_mtp(q, qo, True, syn.KV_BF16, case.kv, None, case.kv_indptr, case.kv_indices)
+    v0 = syn.bf16_bits_to_f32(case.kv[case.kv_indices[0]])[:512].astype(np.float64)
+    assert np.array_equal(out[0], np.broadcast_to(v0, (16, 512)))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mtp_brute_matches_main(oracle_mod, causal):
+    case = syn.make_case(2, [12, 7], syn.KV_FP8, seed=45)
+    q, qo = syn.make_mtp_query([3, 2], seed=46)
+    a = oracle_mod.mla_decode_mtp(q, qo, causal, syn.KV_FP8, case.kv, case.kv_scales, case.kv_indptr, case.kv_indices)
+    b = oracle_mod.mla_decode_mtp(q, qo, causal, syn.KV_FP8, case.kv, case.kv_scales, case.kv_indptr, case.kv_indices,
+                                  route=oracle_mod.ROUTE_BRUTE)
+    np.testing.assert_allclose(a[0], b[0], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(a[1], b[1], rtol=1e-13, atol=1e-13)
+
+
+def test_mtp_row_subset(oracle_mod):
+    case = syn.make_case(3, [4, 11, 6], syn.KV_MXFP4, seed=47)
+    q, qo = syn.make_mtp_query([2, 2, 2], seed=48)
+    full = oracle_mod.mla_decode_mtp(q, qo, True, syn.KV_MXFP4, case.kv, case.kv_scales, case.kv_indptr,
+                                     case.kv_indices)
+    sub = oracle_mod.mla_decode_mtp(q, qo, True, syn.KV_MXFP4, case.kv, case.kv_scales, case.kv_indptr,
+                                    case.kv_indices, rows=[5, 0, 3])
+    assert np.array_equal(sub[0], full[0][[5, 0, 3]]) and np.array_equal(sub[1], full[1][[5, 0, 3]])
