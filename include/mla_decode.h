@@ -221,6 +221,48 @@ int mla_quantize_q8_debug(const void* q, int batch, float* q_scale, int q_scale_
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_decode_mtp: the decode attention with several query tokens per sequence
+ * (multi-token prediction / speculative decoding; the pages' `qo_indptr` with
+ * `max_seqlen_qo` / `uni_seqlen_qo`, submission 593653 `_aiter_persistent`).
+ * Query row r (of total_q) belongs to sequence b with
+ * qo_indptr[b] <= r < qo_indptr[b+1] and is token t = r - qo_indptr[b] of
+ * that sequence's n query tokens. It attends
+ *   causal = 0: every cache token of sequence b;
+ *   causal = 1: the first L_b - n + 1 + t cache tokens (the query tokens are
+ *               the sequence's last n positions); none when that count is
+ *               <= 0 (out = 0, lse = -inf).
+ *   q          device bf16 [total_q, 16, 576]
+ *   qo_indptr  device int32 [batch + 1], non-decreasing, qo_indptr[0] = 0,
+ *              qo_indptr[batch] = total_q; not read when uni_q_len > 0 (may
+ *              then be NULL)
+ *   total_q    host copy of qo_indptr[batch]
+ *   uni_q_len  > 0: every sequence has exactly uni_q_len query tokens
+ *              (total_q must equal batch * uni_q_len); 0: ragged, from qo_indptr
+ *   causal     0 or 1 as above
+ *   out, lse   device bf16 [total_q, 16, 512] and fp32 [total_q, 16] (or NULL)
+ *   kv .. page_size, batch, total_kv, kv_dtype, sm_scale, stream
+ *              as mla_decode_paged (page_size 1: the layout of mla_decode)
+ *   workspace  at least mla_decode_mtp_workspace_size(...) bytes, 16-byte
+ *              aligned (NULL allowed when that size is 0)
+ *   flags      MLA_FLAG_FORCE_SPLIT with a split count, or 0 (heuristic); the
+ *              plan is always split-K over the query rows, and
+ *              MLA_FLAG_FORCE_PERSISTENT is rejected
+ * Returns as mla_decode_paged; MLA_ERR_INVALID_ARG also for a bad causal,
+ * total_q or uni_q_len, or a NULL / misaligned qo_indptr when uni_q_len = 0.
+ */
+int mla_decode_mtp(const void* q, const int32_t* qo_indptr, int total_q, int uni_q_len, int causal, const void* kv,
+                   const void* kv_scales, const int32_t* kv_indptr, const int32_t* kv_indices,
+                   const int32_t* kv_last_page_len, int page_size, void* out, float* lse, int batch, int64_t total_kv,
+                   int kv_dtype, float sm_scale, void* workspace, size_t workspace_bytes, int flags, void* stream);
+
+/*
+ * mla_decode_mtp_workspace_size: bytes of workspace mla_decode_mtp needs
+ * (the split partials of its plan over total_q query rows). Pure host
+ * function; 0 for invalid arguments.
+ */
+size_t mla_decode_mtp_workspace_size(int batch, int total_q, int64_t total_kv, int kv_dtype, int flags);
+
+/*
  * mla_dequant_debug: decode `rows` physical cache rows to fp32 [rows, 576]
  * through the attention kernel's own staging and decode routines (test aid
  * for the bit-exact decoder check). For fp8 the value written is the binary32

@@ -24,6 +24,8 @@ from ._lib import (  # noqa: F401
     PlanInfo,
     flags_for,
     mla_decode,
+    mla_decode_mtp,
+    mla_decode_mtp_workspace_size,
     mla_decode_paged,
     mla_decode_plan,
     mla_decode_q8,
@@ -33,6 +35,7 @@ from ._lib import (  # noqa: F401
     mla_quantize_q8_debug,
     mla_status_string,
     prepare_decode,
+    prepare_decode_mtp,
     prepare_decode_paged,
     prepare_decode_q8,
 )

@@ -22,8 +22,9 @@ FLAG_FORCE_SPLIT, FLAG_FORCE_PERSISTENT = 0x1, 0x2
 FLAG_SPLITS_SHIFT, FLAG_GRID_SHIFT = 8, 16
 Q_SCALE_STATIC, Q_SCALE_DYNAMIC = 0, 1
 
-_EXPORTS = ("mla_decode", "mla_decode_paged", "mla_decode_q8", "mla_decode_plan", "mla_decode_workspace_size",
-            "mla_decode_q8_workspace_size", "mla_quantize_q8_debug", "mla_dequant_debug", "mla_status_string")
+_EXPORTS = ("mla_decode", "mla_decode_paged", "mla_decode_q8", "mla_decode_mtp", "mla_decode_plan",
+            "mla_decode_workspace_size", "mla_decode_q8_workspace_size", "mla_decode_mtp_workspace_size",
+            "mla_quantize_q8_debug", "mla_dequant_debug", "mla_status_string")
 
 
 class MlaError(RuntimeError):
@@ -70,6 +71,11 @@ def _load():
     lib.mla_decode_q8_workspace_size.argtypes = [i32, i64, i32, i32, i32]
     lib.mla_quantize_q8_debug.restype = i32
     lib.mla_quantize_q8_debug.argtypes = [vp, i32, vp, i32, vp, vp, sz, vp]
+    lib.mla_decode_mtp.restype = i32
+    lib.mla_decode_mtp.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, i32, i64, i32,
+                                   ctypes.c_float, vp, sz, i32, vp]
+    lib.mla_decode_mtp_workspace_size.restype = sz
+    lib.mla_decode_mtp_workspace_size.argtypes = [i32, i32, i64, i32, i32]
     lib.mla_decode_plan.restype = i32
     lib.mla_decode_plan.argtypes = [i32, i64, i32, i32, ctypes.POINTER(_Plan)]
     lib.mla_decode_workspace_size.restype = sz
@@ -116,6 +122,11 @@ def mla_decode_q8_workspace_size(batch: int, total_kv: int, kv_dtype: int, flags
                                  q_scale_mode: int = Q_SCALE_DYNAMIC) -> int:
     return int(_lib.mla_decode_q8_workspace_size(int(batch), int(total_kv), int(kv_dtype), int(flags),
                                                  int(q_scale_mode)))
+
+
+def mla_decode_mtp_workspace_size(batch: int, total_q: int, total_kv: int, kv_dtype: int, flags: int = 0) -> int:
+    return int(_lib.mla_decode_mtp_workspace_size(int(batch), int(total_q), int(total_kv), int(kv_dtype),
+                                                  int(flags)))
 
 
 def _ptr(t):
@@ -385,3 +396,75 @@ def mla_quantize_q8_debug(q, q_scale, q_scale_mode: int, codes=None, workspace=N
     if rc != 0:
         raise MlaError(rc, "mla_quantize_q8_debug")
     return codes
+
+
+def _mtp_args(q, qo_indptr, kv, kv_scales, kv_indptr, kv_indices, kv_last_page_len, out, lse, total_q, uni_q_len,
+              causal, total_kv, kv_dtype, page_size, sm_scale, workspace, flags):
+    B = int(kv_indptr.shape[0]) - 1
+    _need(q.is_cuda and q.dtype == torch.bfloat16 and q.is_contiguous()
+          and tuple(q.shape) == (total_q, NUM_HEADS, QK_DIM), "q must be contiguous bf16 [total_q, 16, 576]")
+    if uni_q_len:
+        _need(int(uni_q_len) * B == int(total_q), "uniform query length: total_q must be batch * uni_q_len")
+    else:
+        _need(qo_indptr is not None and qo_indptr.is_cuda and qo_indptr.dtype == torch.int32
+              and qo_indptr.is_contiguous() and qo_indptr.numel() == B + 1,
+              "qo_indptr must be a contiguous device int32 tensor [batch + 1]")
+    _check_kv(kv, kv_scales, kv_dtype)
+    _need(kv.shape[0] % max(int(page_size), 1) == 0, "kv rows must be a whole number of pages")
+    _need(kv_indptr.is_cuda and kv_indptr.dtype == torch.int32 and kv_indptr.is_contiguous(),
+          "kv_indptr must be a contiguous device int32 tensor")
+    _need(kv_indices.is_cuda and kv_indices.dtype == torch.int32 and kv_indices.is_contiguous(),
+          "kv_indices must be a contiguous device int32 tensor")
+    if page_size > 1:
+        _need(kv_last_page_len is not None and kv_last_page_len.is_cuda and kv_last_page_len.dtype == torch.int32
+              and kv_last_page_len.is_contiguous() and kv_last_page_len.numel() == B,
+              "kv_last_page_len must be a contiguous device int32 tensor [batch]")
+    _need(out.is_cuda and out.dtype == torch.bfloat16 and out.is_contiguous()
+          and tuple(out.shape) == (total_q, NUM_HEADS, V_DIM), "out must be contiguous bf16 [total_q, 16, 512]")
+    if lse is not None:
+        _need(lse.is_cuda and lse.dtype == torch.float32 and lse.is_contiguous()
+              and tuple(lse.shape) == (total_q, NUM_HEADS), "lse must be contiguous fp32 [total_q, 16]")
+    need = mla_decode_mtp_workspace_size(B, total_q, total_kv, kv_dtype, flags)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (_ptr(q), _ptr(qo_indptr), int(total_q), int(uni_q_len), int(bool(causal)), _ptr(kv), _ptr(kv_scales),
+            _ptr(kv_indptr), _ptr(kv_indices), _ptr(kv_last_page_len), int(page_size), _ptr(out), _ptr(lse), B,
+            int(total_kv), int(kv_dtype), float(sm_scale), _ptr(workspace), ws_bytes, int(flags), _stream(q.device))
+    return args, workspace
+
+
+def mla_decode_mtp(q, qo_indptr, kv, kv_scales, kv_indptr, kv_indices, out, lse=None, *, total_q: int,
+                   causal: bool, total_kv: int, kv_dtype: int, uni_q_len: int = 0, kv_last_page_len=None,
+                   page_size: int = 1, sm_scale: float = 0.0, workspace=None, flags: int = 0):
+    """Enqueue MLA decode with several query tokens per sequence (see include/mla_decode.h,
+    mla_decode_mtp). q [total_q,16,576] bf16, qo_indptr [B+1] int32 (may be None when
+    uni_q_len > 0), out [total_q,16,512], lse [total_q,16]. Returns the workspace used."""
+    args, ws = _mtp_args(q, qo_indptr, kv, kv_scales, kv_indptr, kv_indices, kv_last_page_len, out, lse, total_q,
+                         uni_q_len, causal, total_kv, kv_dtype, page_size, sm_scale, workspace, flags)
+    rc = _lib.mla_decode_mtp(*args)
+    if rc != 0:
+        raise MlaError(rc, "mla_decode_mtp")
+    return ws
+
+
+def prepare_decode_mtp(q, qo_indptr, kv, kv_scales, kv_indptr, kv_indices, out, lse=None, *, total_q: int,
+                       causal: bool, total_kv: int, kv_dtype: int, uni_q_len: int = 0, kv_last_page_len=None,
+                       page_size: int = 1, sm_scale: float = 0.0, workspace=None, flags: int = 0):
+    """prepare_decode for mla_decode_mtp: checks once (one checked call), then
+    returns a zero-argument callable that enqueues the same call."""
+    ws = mla_decode_mtp(q, qo_indptr, kv, kv_scales, kv_indptr, kv_indices, out, lse, total_q=total_q, causal=causal,
+                        total_kv=total_kv, kv_dtype=kv_dtype, uni_q_len=uni_q_len, kv_last_page_len=kv_last_page_len,
+                        page_size=page_size, sm_scale=sm_scale, workspace=workspace, flags=flags)
+    args, _ = _mtp_args(q, qo_indptr, kv, kv_scales, kv_indptr, kv_indices, kv_last_page_len, out, lse, total_q,
+                        uni_q_len, causal, total_kv, kv_dtype, page_size, sm_scale, ws, flags)
+    fn = _lib.mla_decode_mtp
+    keep = (q, qo_indptr, kv, kv_scales, kv_indptr, kv_indices, kv_last_page_len, out, lse, ws)
+
+    def call():
+        rc = fn(*args)
+        if rc != 0:
+            raise MlaError(rc, "mla_decode_mtp")
+        return keep
+
+    return call

@@ -87,6 +87,15 @@ struct Params {
     float* q_scale;
     const float* q_amax;
     int q_amax_n;
+    // Several query tokens per sequence: query row r of `rows` (q, out, lse
+    // rows) belongs to sequence b with qo_indptr[b] <= r < qo_indptr[b+1]
+    // (uni_q > 0: every sequence has uni_q rows and qo_indptr is not read).
+    // causal: token t of n sees the first L - n + 1 + t cache tokens.
+    // qo_indptr NULL and uni_q 0: one row per sequence (rows = batch).
+    const int32_t* qo_indptr;
+    int uni_q;
+    int causal;
+    int rows;
 };
 
 // ---------------------------------------------------------------------------
@@ -650,9 +659,10 @@ __device__ __forceinline__ void wait_own(int groups, int hi) {
     else wait_vmcnt<N * k0>();
 }
 
-// Attend tokens [t0, t1) (positions within sequence b, whose kv_indices
-// entries start at `base`) with the whole workgroup and write the result:
-// final bf16 output + lse when `final`, else partial slot `slot`. Token j of
+// Attend tokens [t0, t1) (positions within the sequence whose kv_indices
+// entries start at `base`) with query row b, with the whole workgroup, and
+// write the result: final bf16 output row b + lse when `final`, else partial
+// slot `slot`. Token j of
 // the sequence is cache row indices[base + j] (page size 1), or row
 // indices[base + j / page_size] * page_size + j % page_size.
 // The four waves work on the same 32-token step: wave w gathers half w / 2 of
@@ -861,19 +871,53 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
 // identity; correctness never depends on where a workgroup runs.
 __device__ __forceinline__ int xcd_order(int x, int n) { return (n & 7) ? x : (x & 7) * (n >> 3) + (x >> 3); }
 
+// Sequence of query row `row` from a ragged qo_indptr: the number of k in
+// 1..batch with qo_indptr[k] <= row, counted by the whole workgroup (wave
+// ballots summed through the 4 ints at cnt, in LDS).
+__device__ __forceinline__ int row_sequence(const Params& P, int row, int* cnt) {
+    int b = 0;
+    const int tid = threadIdx.x;
+    for (int c = 0; c < P.batch; c += kThreads) {
+        const int k = c + tid + 1;
+        const uint64_t m = __ballot(k <= P.batch && P.qo_indptr[k] <= row);
+        if ((tid & 63) == 0) cnt[tid >> 6] = __popcll(m);
+        __syncthreads();
+        b += cnt[0] + cnt[1] + cnt[2] + cnt[3];
+        __syncthreads();
+    }
+    return b;
+}
+
 template <int KV, int QF>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Fmt<KV>::kWgsPerCU, Fmt<KV>::kWgsPerCU)))
 void split_kernel(Params P) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[Layout<KV>::kBytes];
     const int item = xcd_order(blockIdx.x, gridDim.x);
-    const int b = item / P.nsplit, s = item % P.nsplit;
+    const int row = item / P.nsplit, s = item % P.nsplit;
+    // the sequence of this query row, and the cache tokens the causal reading hides from it
+    int b = row, hide = 0;
+    if (P.uni_q > 0 || P.qo_indptr) {
+        int t, n;
+        if (P.uni_q > 0) {
+            b = row / P.uni_q;
+            n = P.uni_q;
+            t = row - b * n;
+        } else {
+            b = row_sequence(P, row, reinterpret_cast<int*>(smem + Layout<KV>::kIdxOff));
+            const int r0 = P.qo_indptr[b];
+            n = P.qo_indptr[b + 1] - r0;
+            t = row - r0;
+        }
+        if (P.causal) hide = n - 1 - t;
+    }
     const int base = P.indptr[b], entries = P.indptr[b + 1] - base;
     // tokens of the sequence: its entries, or (pages - 1) full pages plus the last page's tokens
-    const int L = P.page_size == 1 ? entries : entries > 0 ? (entries - 1) * P.page_size + P.last_page[b] : 0;
+    const int Ls = P.page_size == 1 ? entries : entries > 0 ? (entries - 1) * P.page_size + P.last_page[b] : 0;
+    const int L = max(0, Ls - hide);
     const int chunk = ((L + P.nsplit - 1) / P.nsplit + kStepTokens - 1) / kStepTokens * kStepTokens;
     const int t0 = min(L, s * chunk);
     const int t1 = min(L, t0 + chunk);
-    run_wg<KV, QF>(P, smem, b, base, t0, t1, P.nsplit == 1, b * P.nsplit + s, blockIdx.x == 0);
+    run_wg<KV, QF>(P, smem, row, base, t0, t1, P.nsplit == 1, row * P.nsplit + s, blockIdx.x == 0);
 }
 
 // Largest p whose share [floor(p T / G), floor((p+1) T / G)) starts at or before t.
@@ -1221,13 +1265,13 @@ static int launch(const mla_plan_info& plan, const Params& P, hipStream_t stream
         C.indptr = P.indptr;
         C.out = P.out;
         C.lse = P.lse;
-        C.batch = P.batch;
+        C.batch = P.rows;
         C.mode = plan.mode;
         C.nsplit = plan.num_splits;
         C.grid = plan.grid;
         C.total = P.total;
         C.items = combine_items(plan.mode, plan.num_splits);
-        hipLaunchKernelGGL(combine_kernel, dim3(kHeads * 4 * P.batch / C.items), dim3(kCombThreads), 0, stream, C);
+        hipLaunchKernelGGL(combine_kernel, dim3(kHeads * 4 * P.rows / C.items), dim3(kCombThreads), 0, stream, C);
         if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
     }
     return MLA_OK;
@@ -1239,18 +1283,31 @@ namespace mla {
 
 // Shared body of mla_decode (page size 1), mla_decode_paged and mla_decode_q8
 // (q_mode < 0: bf16 query; else MLA_Q_SCALE_*, with q_scale).
+// Several query tokens per sequence (mla_decode_mtp): qo_indptr / uni_q /
+// causal as in Params, total_q query rows; the plan is made over the rows.
+struct MtpArgs {
+    const int32_t* qo_indptr = nullptr;
+    int total_q = 0;
+    int uni_q = 0;
+    int causal = 0;
+};
+
 static int decode_impl(const void* q, const void* kv, const void* kv_scales, const int32_t* kv_indptr,
                        const int32_t* kv_indices, const int32_t* kv_last_page_len, int page_size, void* out,
                        float* lse, int batch, int64_t total_kv, int kv_dtype, float sm_scale, void* workspace,
-                       size_t workspace_bytes, int flags, void* stream, int q_mode = -1, float* q_scale = nullptr) {
+                       size_t workspace_bytes, int flags, void* stream, int q_mode = -1, float* q_scale = nullptr,
+                       const MtpArgs* mtp = nullptr) {
     mla_plan_info plan;
-    int rc = make_plan(batch, total_kv, kv_dtype, flags, &plan);
+    const int rows = mtp ? mtp->total_q : batch;
+    int rc = mtp ? mtp_plan(batch, mtp->total_q, total_kv, kv_dtype, flags, &plan)
+                 : make_plan(batch, total_kv, kv_dtype, flags, &plan);
     if (rc != MLA_OK) return rc;
     const bool dyn = q_mode == MLA_Q_SCALE_DYNAMIC;
     const size_t need = dyn ? q8_amax_offset(plan.workspace_bytes) + kQ8AmaxParts * sizeof(float)
                             : plan.workspace_bytes;
-    if (batch == 0) return MLA_OK;
+    if (batch == 0 || rows == 0) return MLA_OK;
     if (q_mode >= 0 && (!q_scale || !aligned(q_scale, 4))) return MLA_ERR_INVALID_ARG;
+    if (mtp && mtp->uni_q == 0 && (!mtp->qo_indptr || !aligned(mtp->qo_indptr, 4))) return MLA_ERR_INVALID_ARG;
     if (!q || !kv || !kv_indptr || !out) return MLA_ERR_INVALID_ARG;
     if (total_kv > 0 && !kv_indices) return MLA_ERR_INVALID_ARG;
     if (kv_dtype != MLA_KV_BF16 && !kv_scales) return MLA_ERR_INVALID_ARG;
@@ -1290,6 +1347,10 @@ static int decode_impl(const void* q, const void* kv, const void* kv_scales, con
                                                     q8_amax_offset(plan.workspace_bytes))
                    : nullptr;
     P.q_amax_n = dyn ? q_amax_parts(batch) : 0;
+    P.qo_indptr = mtp ? mtp->qo_indptr : nullptr;
+    P.uni_q = mtp ? mtp->uni_q : 0;
+    P.causal = mtp ? mtp->causal : 0;
+    P.rows = rows;
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (q_mode >= 0) {
@@ -1344,6 +1405,24 @@ extern "C" int mla_decode_q8(const void* q, float* q_scale, int q_scale_mode, co
     return mla::decode_impl(q, kv, kv_scales, kv_indptr, kv_indices, kv_last_page_len, page_size, out, lse, batch,
                             total_kv, kv_dtype, sm_scale, workspace, workspace_bytes, flags, stream, q_scale_mode,
                             q_scale);
+}
+
+extern "C" int mla_decode_mtp(const void* q, const int32_t* qo_indptr, int total_q, int uni_q_len, int causal,
+                              const void* kv, const void* kv_scales, const int32_t* kv_indptr,
+                              const int32_t* kv_indices, const int32_t* kv_last_page_len, int page_size, void* out,
+                              float* lse, int batch, int64_t total_kv, int kv_dtype, float sm_scale, void* workspace,
+                              size_t workspace_bytes, int flags, void* stream) {
+    if (page_size < 1 || page_size > (1 << 16) || total_q < 0 || uni_q_len < 0 || causal < 0 || causal > 1)
+        return MLA_ERR_INVALID_ARG;
+    if (uni_q_len > 0 && (int64_t)uni_q_len * batch != total_q) return MLA_ERR_INVALID_ARG;
+    if (flags & MLA_FLAG_FORCE_PERSISTENT) return MLA_ERR_INVALID_ARG;
+    mla::MtpArgs m;
+    m.qo_indptr = qo_indptr;
+    m.total_q = total_q;
+    m.uni_q = uni_q_len;
+    m.causal = causal;
+    return mla::decode_impl(q, kv, kv_scales, kv_indptr, kv_indices, kv_last_page_len, page_size, out, lse, batch,
+                            total_kv, kv_dtype, sm_scale, workspace, workspace_bytes, flags, stream, -1, nullptr, &m);
 }
 
 extern "C" int mla_quantize_q8_debug(const void* q, int batch, float* q_scale, int q_scale_mode, uint8_t* codes,

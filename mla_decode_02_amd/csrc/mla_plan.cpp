@@ -126,6 +126,16 @@ int make_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_inf
     return MLA_OK;
 }
 
+int mtp_plan(int batch, int total_q, int64_t total_kv, int kv_dtype, int flags, mla_plan_info* p) {
+    if (batch < 0 || total_q < 0 || total_kv < 0 || total_kv > INT32_MAX) return MLA_ERR_INVALID_ARG;
+    if (flags & MLA_FLAG_FORCE_PERSISTENT) return MLA_ERR_INVALID_ARG;
+    // every query row reads its sequence: the rows together see about
+    // total_kv * total_q / batch tokens (capped to the planner's range)
+    int64_t tokens = batch > 0 ? total_kv * (int64_t)total_q / batch : 0;
+    if (tokens > INT32_MAX) tokens = INT32_MAX;
+    return make_plan(total_q, tokens, kv_dtype, flags | MLA_FLAG_FORCE_SPLIT, p);
+}
+
 }  // namespace mla
 
 extern "C" int mla_decode_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_info* plan) {
@@ -135,6 +145,12 @@ extern "C" int mla_decode_plan(int batch, int64_t total_kv, int kv_dtype, int fl
 extern "C" size_t mla_decode_workspace_size(int batch, int64_t total_kv, int kv_dtype, int flags) {
     mla_plan_info p;
     if (mla::make_plan(batch, total_kv, kv_dtype, flags, &p) != MLA_OK) return 0;
+    return p.workspace_bytes;
+}
+
+extern "C" size_t mla_decode_mtp_workspace_size(int batch, int total_q, int64_t total_kv, int kv_dtype, int flags) {
+    mla_plan_info p;
+    if (mla::mtp_plan(batch, total_q, total_kv, kv_dtype, flags, &p) != MLA_OK) return 0;
     return p.workspace_bytes;
 }
 

@@ -29,6 +29,10 @@ int make_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_inf
 int heuristic_splits(int batch, int64_t total_kv, int kv_dtype);
 int heuristic_grid(int64_t total_kv, int kv_dtype);
 size_t partial_lse_offset(int num_partials);
+// Plan for total_q query rows over `batch` sequences holding total_kv cache
+// tokens (several query tokens per sequence): always split-K, made as for
+// total_q sequences of the average length.
+int mtp_plan(int batch, int total_q, int64_t total_kv, int kv_dtype, int flags, mla_plan_info* p);
 // Offset of the dynamic fp8 query scale's partial maxima: after the plan's bytes.
 size_t q8_amax_offset(size_t plan_bytes);
 

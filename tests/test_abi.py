@@ -35,8 +35,9 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("mla_decode", "mla_decode_paged", "mla_decode_q8", "mla_decode_plan", "mla_decode_workspace_size",
-              "mla_decode_q8_workspace_size", "mla_quantize_q8_debug", "mla_dequant_debug", "mla_status_string"):
+    for n in ("mla_decode", "mla_decode_paged", "mla_decode_q8", "mla_decode_mtp", "mla_decode_plan",
+              "mla_decode_workspace_size", "mla_decode_q8_workspace_size", "mla_decode_mtp_workspace_size",
+              "mla_quantize_q8_debug", "mla_dequant_debug", "mla_status_string"):
         assert n in names
 
 
@@ -232,6 +233,40 @@ def test_quantize_q8_debug_validation(raw_lib):
     assert f(A, 2, A, 1, A, None, 0, None) == -3
     assert f(A, 2, A, 1, A, A, 1023, None) == -3
     assert f(A, 0, None, 0, None, None, 0, None) == 0
+
+
+def _call_mtp(raw_lib, qo=A, total_q=4, uni=2, causal=1, page_size=1, last=None, flags=0, batch=2, total=64,
+              ws=None, ws_bytes=0):
+    f = raw_lib.mla_decode_mtp
+    f.restype = ctypes.c_int
+    vp = ctypes.c_void_p
+    f.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp,
+                  ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_float, vp, ctypes.c_size_t, ctypes.c_int, vp]
+    return f(A, qo, total_q, uni, causal, A, A, A, A, last, page_size, A, None, batch, total, 1, 0.0, ws, ws_bytes,
+             flags, None)
+
+
+def test_mtp_validation(raw_lib, mla):
+    assert _call_mtp(raw_lib, causal=2) == -1
+    assert _call_mtp(raw_lib, uni=3) == -1                          # total_q != batch * uni_q_len
+    assert _call_mtp(raw_lib, uni=-1) == -1
+    assert _call_mtp(raw_lib, total_q=-1, uni=0) == -1
+    assert _call_mtp(raw_lib, uni=0, qo=None) == -1                 # ragged needs qo_indptr
+    assert _call_mtp(raw_lib, uni=0, qo=A + 2) == -1
+    assert _call_mtp(raw_lib, flags=mla.flags_for(persistent=True)) == -1
+    assert _call_mtp(raw_lib, page_size=8, last=None) == -1
+    assert _call_mtp(raw_lib, flags=mla.flags_for(splits=4)) == -3  # partials need a workspace
+    assert _call_mtp(raw_lib, total_q=0, uni=0, qo=None) == 0       # no query rows: a no-op
+    assert _call_mtp(raw_lib, batch=0, total=0, total_q=0, uni=0) == 0
+
+
+def test_mtp_plan_is_split_over_rows(mla):
+    # 32 sequences x 2 query tokens plan like 64 single-token sequences of the same length
+    assert mla.mla_decode_mtp_workspace_size(32, 64, 32 * 1024, 1, 0) == \
+        mla.mla_decode_workspace_size(64, 64 * 1024, 1, mla.FLAG_FORCE_SPLIT)
+    assert mla.mla_decode_mtp_workspace_size(4, 8, 4 * 8192, 1, mla.flags_for(splits=5)) == \
+        mla.mla_decode_workspace_size(8, 8 * 8192, 1, mla.flags_for(splits=5))
+    assert mla.mla_decode_mtp_workspace_size(4, 8, 4 * 8192, 1, mla.flags_for(persistent=True)) == 0
 
 
 def test_batch_zero_is_a_noop(raw_lib):
