@@ -63,6 +63,9 @@ def parse_args():
     ap.add_argument("--q8", choices=["static", "dynamic"], default=None,
                     help="with --only-gpu-loop: the fp8-query entry point (mla_decode_q8) with this Q scale mode")
     ap.add_argument("--no-q8-grid", action="store_true", help="skip timing the fp8-query variants")
+    ap.add_argument("--mtp", type=int, default=0,
+                    help="with --only-gpu-loop: this many causal query tokens per sequence (mla_decode_mtp)")
+    ap.add_argument("--no-mtp-grid", action="store_true", help="skip timing the several-query-token variants")
     return ap.parse_args()
 
 
@@ -96,12 +99,22 @@ def upload(case, dev):
 STATIC_Q_SCALE = 6.0 / 448.0
 
 
-def prepare(mla, case, q, kv, sc, indptr, indices, out, lse, flags, dev, q8=None):
+def prepare(mla, case, q, kv, sc, indptr, indices, out, lse, flags, dev, q8=None, mtp=0):
     """The pre-marshalled decode call: mla_decode, or mla_decode_paged for a paged workload,
-    or mla_decode_q8 (fp8 query, `q8` = "static" / "dynamic" scale)."""
+    or mla_decode_q8 (fp8 query, `q8` = "static" / "dynamic" scale), or mla_decode_mtp
+    (`mtp` causal query tokens per sequence; q, out and lse then have B * mtp rows)."""
     import torch
 
     paged = case.meta.get("paged")
+    if mtp:
+        extra = {}
+        if paged is not None:
+            t = {k: torch.from_numpy(paged[k]).to(dev) for k in ("kv_indptr", "kv_indices", "kv_last_page_len")}
+            indptr, indices = t["kv_indptr"], t["kv_indices"]
+            extra = dict(kv_last_page_len=t["kv_last_page_len"], page_size=paged["page_size"])
+        return mla.prepare_decode_mtp(q, None, kv, sc, indptr, indices, out, lse, total_q=q.shape[0], causal=True,
+                                      total_kv=case.total_kv, kv_dtype=case.kv_dtype, uni_q_len=mtp, flags=flags,
+                                      **extra)
     if q8 is not None:
         mode = mla.Q_SCALE_STATIC if q8 == "static" else mla.Q_SCALE_DYNAMIC
         q_scale = torch.tensor([STATIC_Q_SCALE], dtype=torch.float32, device=dev)
@@ -121,7 +134,18 @@ def prepare(mla, case, q, kv, sc, indptr, indices, out, lse, flags, dev, q8=None
                                     flags=flags)
 
 
-def measure(name, args, dev, flush, q8=None):
+def mtp_query(case, mtp, dev):
+    """bf16 query of `mtp` tokens per sequence, seeded from the workload's own seed."""
+    import numpy as np
+    import torch
+
+    import synthetic as syn
+
+    qb, _ = syn.make_mtp_query([mtp] * case.batch, seed=case.meta.get("seed", 0) + 1000 * mtp)
+    return torch.from_numpy(qb.view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def measure(name, args, dev, flush, q8=None, mtp=0):
     import torch
 
     import mla_decode_02_amd as mla
@@ -130,12 +154,18 @@ def measure(name, args, dev, flush, q8=None):
     case = syn.make_workload(name)
     q, kv, sc, indptr, indices = upload(case, dev)
     B = case.batch
-    out = torch.empty((B, 16, 512), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((B, 16), dtype=torch.float32, device=dev)
-    call = prepare(mla, case, q, kv, sc, indptr, indices, out, lse, args.flags, dev, q8=q8)
+    rows = B * mtp if mtp else B
+    if mtp:
+        q = mtp_query(case, mtp, dev)
+    out = torch.empty((rows, 16, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((rows, 16), dtype=torch.float32, device=dev)
+    call = prepare(mla, case, q, kv, sc, indptr, indices, out, lse, args.flags, dev, q8=q8, mtp=mtp)
     paged = case.meta.get("paged")
-    plan_flags = args.flags | (mla.FLAG_FORCE_SPLIT if paged and paged["page_size"] > 1 else 0)
-    plan = mla.mla_decode_plan(B, case.total_kv, case.kv_dtype, plan_flags)
+    plan_flags = args.flags | (mla.FLAG_FORCE_SPLIT if (paged and paged["page_size"] > 1) or mtp else 0)
+    if mtp:  # the plan runs over the query rows, each seeing its sequence
+        plan = mla.mla_decode_plan(rows, min(case.total_kv * mtp, 2**31 - 1), case.kv_dtype, plan_flags)
+    else:
+        plan = mla.mla_decode_plan(B, case.total_kv, case.kv_dtype, plan_flags)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -165,9 +195,12 @@ def measure(name, args, dev, flush, q8=None):
 
     med = statistics.median(cold_us)
     kv_bytes, tot_bytes = case.kv_bytes(), case.total_bytes()
+    if mtp:  # the extra query rows: q, out and lse of each
+        tot_bytes += (rows - B) * (2 * 16 * 576 + 2 * 16 * 512 + 4 * 16)
     return {
         "workload": name,
-        "query": "bf16" if q8 is None else f"fp8 ({q8} per-tensor scale)",
+        "query": ("bf16" if q8 is None else f"fp8 ({q8} per-tensor scale)")
+                 + (f", {mtp} causal tokens per sequence" if mtp else ""),
         "kv_format": syn.KV_NAMES[case.kv_dtype],
         "page_size": case.meta.get("paged", {}).get("page_size", 1),
         "batch": B,
@@ -260,14 +293,19 @@ def main():
         q, kv, sc, indptr, indices = upload(case, dev)
         out = torch.empty((case.batch, 16, 512), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((case.batch, 16), dtype=torch.float32, device=dev)
-        call = prepare(mla, case, q, kv, sc, indptr, indices, out, lse, args.flags, dev, q8=args.q8)
+        if args.mtp:
+            q = mtp_query(case, args.mtp, dev)
+            out = torch.empty((q.shape[0], 16, 512), dtype=torch.bfloat16, device=dev)
+            lse = torch.empty((q.shape[0], 16), dtype=torch.float32, device=dev)
+        call = prepare(mla, case, q, kv, sc, indptr, indices, out, lse, args.flags, dev, q8=args.q8, mtp=args.mtp)
         flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev) if args.cold else None
         for _ in range(args.only_gpu_loop):
             if flush is not None:
                 flush_read(flush)
             call()
         torch.cuda.synchronize()
-        print(json.dumps({"workload": args.workload, "q8": args.q8, "calls": args.only_gpu_loop}), flush=True)
+        print(json.dumps({"workload": args.workload, "q8": args.q8, "mtp": args.mtp, "calls": args.only_gpu_loop}),
+              flush=True)
         return
 
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
@@ -292,6 +330,19 @@ def main():
             print(f"# q8 {mode} {n}: cold {r['cold_us_median']:.2f} us, warm {r['warm_us']:.2f} us, "
                   f"{r['effective_kv_GBps']:.0f} GB/s KV ({r['pct_hbm_peak_kv']:.1f}% of 8 TB/s)",
                   file=sys.stderr, flush=True)
+    # Several causal query tokens per sequence (mla_decode_mtp): 2 and 4 tokens on the headline
+    # workload and on the bandwidth-bound fp8 64 x 8192 workload. Effective GB/s counts the cache once.
+    grid_mtp = None
+    if not args.no_mtp_grid:
+        grid_mtp = {}
+        for n in dict.fromkeys([args.workload, "fp8_b64_kv8192"]):
+            for k in (2, 4):
+                r = measure(n, args, dev, flush, mtp=k)
+                r.pop("_case", None)
+                grid_mtp[f"{n}/q{k}"] = r
+                print(f"# mtp q{k} {n}: cold {r['cold_us_median']:.2f} us, warm {r['warm_us']:.2f} us, "
+                      f"{r['effective_kv_GBps']:.0f} GB/s KV counted once ({r['pct_hbm_peak_kv']:.1f}% of 8 TB/s)",
+                      file=sys.stderr, flush=True)
     head = results[args.workload]
     case = head.pop("_case")
     for r in results.values():
@@ -345,6 +396,7 @@ def main():
         "cpu_baseline": cpu,
         "grid": results,
         "grid_q8": grid_q8,
+        "grid_mtp": grid_mtp,
         "sweep": sweep,
         "kernel_source_hash": source_hash(),
         "host": platform.node(),
