@@ -384,7 +384,8 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": syn.KV_NAMES[case.kv_dtype] + "-kv/bf16-q/fp32-acc",
+        "dtype": "bf16",
+        "dtype_detail": f"{syn.KV_NAMES[case.kv_dtype]} cache decoded exactly to bf16; bf16 MFMA, fp32 accumulate",
         "data": "synthetic (seeded N(0,1) q and cache rows, quantised per format)",
         "config": {"workload": args.workload, "batch": head["batch"], "kv_len": head["kv_len"],
                    "kv_format": head["kv_format"], "heads": 16, "qk_dim": 576, "v_dim": 512, "page_size": 1,

@@ -119,3 +119,11 @@ def test_paged_case_follows_the_page_rule(page_size):
         for j in range(L):
             row = case.kv_indices[case.kv_indptr[b] + j]
             assert row == ids[pg["kv_indptr"][b] + j // page_size] * page_size + j % page_size
+
+
+def test_mtp_query_layout():
+    q, qo = syn.make_mtp_query([2, 0, 3], seed=5)
+    assert q.shape == (5, 16, 576) and q.dtype == np.uint16
+    assert qo.tolist() == [0, 2, 2, 5] and qo.dtype == np.int32
+    q2, _ = syn.make_mtp_query([2, 0, 3], seed=5)
+    assert np.array_equal(q, q2)
