@@ -52,6 +52,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -470,12 +471,63 @@ __device__ __forceinline__ f32x4 qk_partial(const uint8_t* step, const QOp (&qB)
     return e0 + e1;
 }
 
+// fp8 query on the MXFP4 cache: the scores run on the MX-scaled MFMA
+// v_mfma_scale_f32_16x16x128_f8f6f4 with the cache's e2m1 codes and e8m0
+// block scales as operand A and the query's e4m3fn codes (scale 1) as operand
+// B, so no cache code is converted. Operand layouts of this instruction on
+// gfx950 (16 x 128 per operand, lane group G = lane / 16, row / column
+// lane % 16): an e2m1 operand holds k = 32 G .. 32 G + 31, element i in
+// nibble i (low nibble first); an e4m3 operand holds k = 16 G + i in bytes
+// 0-15 and k = 64 + 16 G + i in bytes 16-31; the A scale of lane (G, r) is
+// the e8m0 of (row r, k block G). A score tile is five such products: the
+// four 128-dim blocks of the no-RoPE dims (block u is exactly code load u of
+// the staged tile, 16 bytes per lane) and the 64 RoPE dims, zero-padded to
+// 128. Wave half 0 takes blocks 0-2, half 1 block 3 and the RoPE block.
+__device__ __forceinline__ f32x4 mfma_mx(i32x8 a, i32x8 b, int scale_a, f32x4 c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, scale_a, 0, 127);
+}
+
+// e8m0 scale code of block bi (0..17) of tile row r, from the staged scale
+// dwords (codes 2p, 2p + 1 of row r in the low half of the dword at
+// kScaleOff + 256 (p / 4) + 4 (16 (p % 4) + r)).
+__device__ __forceinline__ int mx_scale_code(const uint8_t* tile, int bi, int r) {
+    const int p = bi >> 1;
+    return tile[Fmt<MLA_KV_MXFP4>::kScaleOff + 256 * (p >> 2) + 4 * (16 * (p & 3) + r) + (bi & 1)];
+}
+
+template <int HF>
+__device__ __forceinline__ f32x4 qk_partial_mx(const uint8_t* step, const i32x8 (&qm)[3], int t, int lane) {
+    const uint8_t* tile = step + t * Fmt<MLA_KV_MXFP4>::kTileBytes;
+    const int G = lane >> 4, r = lane & 15;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < (HF ? 2 : 3); ++j) {
+        const int u = HF ? 3 + j : j;
+        i32x8 a = {0, 0, 0, 0, 0, 0, 0, 0};
+        int sc = 127;
+        if (u < 4) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(tile + 1024 * u + 16 * lane);
+            a[0] = (int)w[0]; a[1] = (int)w[1]; a[2] = (int)w[2]; a[3] = (int)w[3];
+            sc = mx_scale_code(tile, 4 * u + G, r);
+        } else if (G < 2) {  // RoPE dims 512 + 32 G ..: lanes 0..31 of the RoPE load
+            const u32x4 w = *reinterpret_cast<const u32x4*>(tile + Fmt<MLA_KV_MXFP4>::kRopeOff + 16 * lane);
+            a[0] = (int)w[0]; a[1] = (int)w[1]; a[2] = (int)w[2]; a[3] = (int)w[3];
+            sc = mx_scale_code(tile, 16 + G, r);
+        }
+        acc = mfma_mx(a, qm[j], sc, acc);
+    }
+    return acc;
+}
+
 // Query operand type: bf16 (also the decoded fp8 query codes, which bf16
-// holds exactly), or raw e4m3fn codes when both operands are fp8.
+// holds exactly), raw e4m3fn codes when both operands are fp8, or the
+// MX-scaled MFMA's e4m3fn operand on the MXFP4 cache.
 template <int KV, int QF>
 struct QOperand { using T = bf16x8; };
 template <>
 struct QOperand<MLA_KV_FP8_E4M3, 1> { using T = long; };
+template <>
+struct QOperand<MLA_KV_MXFP4, 1> { using T = i32x8; };
 
 struct WaveAcc {
     f32x4 o[kWaveBlocks];  // o[j][i]: head 4G+i, column dcol(kWaveBlocks * wave + j, r)
@@ -721,7 +773,8 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
     constexpr int kQGroups = kHeads * kDqk / 8;
     constexpr int kQPer = (kQGroups + kThreads - 1) / kThreads;
     using QOp = typename QOperand<KV, QF>::T;
-    QOp qB[kHalfK];
+    constexpr bool kMx = QF && KV == MLA_KV_MXFP4;  // scores on the MX-scaled MFMA
+    QOp qB[kMx ? 3 : kHalfK];
     bf16x8 qg[QF ? kQPer : 1];
     float q_scale = 1.0f, q_part = 0.0f;
     const __bf16* qseq = P.q + (int64_t)b * kHeads * kDqk;
@@ -781,7 +834,11 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
         auto scores = [&](int i) -> f32x4 {
             const uint8_t* st = smem + (i % R) * L::kStepBytes;
             if constexpr (KV == MLA_KV_MXFP4) convert_scales(st, fs_buf + (i & 1) * (L::kFsBytes / 4), tid);
-            return hf ? qk_partial<KV, 1>(st, qB, tile, lane) : qk_partial<KV, 0>(st, qB, tile, lane);
+            if constexpr (kMx) {
+                return hf ? qk_partial_mx<1>(st, qB, tile, lane) : qk_partial_mx<0>(st, qB, tile, lane);
+            } else {
+                return hf ? qk_partial<KV, 1>(st, qB, tile, lane) : qk_partial<KV, 0>(st, qB, tile, lane);
+            }
         };
         auto put_scores = [&](int i, f32x4 part) { sbuf[(i & 1) * (kWaves * 64) + wave * 64 + lane] = part; };
 #pragma unroll
@@ -796,7 +853,26 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
         }
         wait_own<KV>(min(D - 1, nsteps - 1), hf);
         __syncthreads();  // step 0 has landed (and the query codes are written)
-        if constexpr (QF) {
+        if constexpr (kMx) {
+            if (w0 == t0) {
+                // B operand of block u for head r: dims 128 u + 16 G + (0..15) and 128 u + 64 + 16 G + (0..15);
+                // the RoPE block has dims 512 + 16 G + (0..15) and zeros (dims 576.. do not exist)
+                const uint8_t* qr = qcodes + r * kDqk;
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    const int u = hf ? 3 + j : j;
+                    u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+                    if (u < 4) {
+                        lo = *reinterpret_cast<const u32x4*>(qr + 128 * u + 16 * G);
+                        hi = *reinterpret_cast<const u32x4*>(qr + 128 * u + 64 + 16 * G);
+                    } else if (u == 4) {
+                        lo = *reinterpret_cast<const u32x4*>(qr + 512 + 16 * G);
+                    }
+                    qB[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                }
+            }
+        } else if constexpr (QF) {
             if (w0 == t0) {
 #pragma unroll
                 for (int j = 0; j < kHalfK; ++j) {
