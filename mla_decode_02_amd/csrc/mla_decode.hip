@@ -1,36 +1,38 @@
-// MI355X (gfx950) single-token MLA decode: split-K / persistent stage 1, the
-// log-sum-exp combine, and a decode-check kernel, behind the C ABI declared in
-// include/mla_decode.h.
+// MI355X (gfx950) MLA decode: split-K / persistent stage 1, the log-sum-exp
+// combine, the fp8-query scale reduction, and decode / quantiser check
+// kernels, behind the C ABI declared in include/mla_decode.h.
 //
 // The operation is the one on the amd-mixed-mla pages (submission 593653,
 // `_bmm_reference` and the module constants): 16 query heads share one latent
 // KV row per token; scores over 576 dims (512 no-RoPE + 64 RoPE), softmax over
 // the tokens, output over the first 512 dims of the same rows.
 //
-// Stage 1, one workgroup = 4 independent waves over one token range. A wave
-// owns 32-token steps (two 16-token tiles) of the range. Per step:
-//   1. The 32 cache rows are gathered through kv_indices straight from HBM
-//      into the wave's LDS ring with LDS-DMA loads (global_load_lds_dwordx4;
-//      MXFP4 scales with byte DMA), one step ahead of use, so no VGPRs hold
-//      data in flight. Lane (G, r) of a 16-row tile fetches bytes 64u + 16G of
-//      row r for load u, which is the MFMA A-operand layout of the scores.
-//   2. Scores S^T[16 tokens x 16 heads] = K . Q^T per tile on
-//      v_mfma_f32_16x16x32_bf16 (18 k-steps; Q^T lives in VGPRs). fp8 and
-//      MXFP4 codes are dequantised in registers with the gfx950 scaled
-//      converts; fp8 -> bf16 is exact and kv_scale is folded into the score
-//      scale and the output; e2m1 * 2^(e8m0 - 127) -> bf16 is exact.
-//   3. Online softmax in the log2 domain with lazy rescaling: the running max
-//      only moves when a score exceeds it by 2^8, so the 16x512 accumulator
-//      is rarely rescaled. The S^T accumulator is already the A-operand
-//      layout of P for the second product.
-//   4. O[16 x 512] += P . V on v_mfma_f32_16x16x32_bf16, one per 16-column
-//      block. The token-major V operand comes from LDS transpose reads
+// Stage 1: one workgroup of four waves attends one token range of one query
+// row, in 32-token steps (two 16-token tiles). Per step:
+//   1. The step's 32 cache rows are gathered through kv_indices straight from
+//      HBM into an LDS ring with LDS-DMA loads (global_load_lds_dwordx4; the
+//      MXFP4 scales with two-byte DMAs), kRing - 1 steps ahead of use. Each
+//      wave issues one half of one tile. Lane (G, r) of a tile fetches bytes
+//      64u + 16G of row r for load u: the MFMA operand layout of the scores.
+//   2. Scores S^T[16 tokens x 16 heads] = K . Q^T: wave w computes tile w % 2
+//      over half w / 2 of the score dims on v_mfma_f32_16x16x32_bf16 (Q^T in
+//      VGPRs), and the four partial products are summed through LDS. fp8 and
+//      MXFP4 codes are decoded exactly to bf16 with the gfx950 scaled converts
+//      (fp8: kv_scale folded into the score scale and the output). With an fp8
+//      query the scores run on fp8 x fp8 (fp8 cache) or MX-scaled fp4 x fp8
+//      (MXFP4 cache) MFMAs on the raw codes.
+//   3. Online softmax in the log2 domain with lazy rescaling (the running max
+//      only moves when a score exceeds it by 2^8). Every wave runs it on the
+//      full step and holds the same max and sum. The S^T accumulator is
+//      already the A-operand layout of P for the second product.
+//   4. O[16 x 512] += P . V on v_mfma_f32_16x16x32_bf16, each wave for its own
+//      128 columns. The token-major V operand comes from LDS transpose reads
 //      (ds_read_b64_tr_b8 for fp8 / MXFP4 bytes, ds_read_b64_tr_b16 for bf16)
 //      of the same staged rows: V is the first 512 columns of K, so each row is
 //      fetched from HBM once.
-// The four waves' (max, sum, O) are merged through LDS and written either as
-// the final bf16 output + lse or as an fp32 partial (normalised O and its lse)
-// for the combine kernel (flash-decoding split partials and log-sum-exp merge:
+// The loop is software-pipelined with one barrier per step. The result is the
+// final bf16 output + lse, or an fp32 partial (normalised O and its lse) for
+// the combine kernel (flash-decoding split partials and log-sum-exp merge:
 // submission 593653, `_flash_fp8_split_s1` / `_flash_fp8_split_s2`).
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -711,17 +713,17 @@ __device__ __forceinline__ void wait_own(int groups, int hi) {
     else wait_vmcnt<N * k0>();
 }
 
-// Attend tokens [t0, t1) (positions within the sequence whose kv_indices
-// entries start at `base`) with query row b, with the whole workgroup, and
-// write the result: final bf16 output row b + lse when `final`, else partial
-// slot `slot`. Token j of
-// the sequence is cache row indices[base + j] (page size 1), or row
+// Attend tokens [t0, t1) of one sequence (positions within it; its
+// kv_indices entries start at `base`) with query row b, using the whole
+// workgroup, and write the result: the final bf16 output row b + lse when
+// `final`, else partial slot `slot`. Token j of the sequence is cache row
+// indices[base + j] (page size 1), or row
 // indices[base + j / page_size] * page_size + j % page_size.
 // The four waves work on the same 32-token step: wave w gathers half w / 2 of
-// tile w % 2 and computes the scores of tile w % 2 over score k-steps
-// 9 (w / 2) .. +8, the partial scores are summed through LDS in a fixed order,
-// and every wave then runs the same softmax and accumulates P . V for its own
-// 128 output columns.
+// tile w % 2 and computes the scores of tile w % 2 over half w / 2 of the
+// score dims (k-steps 9 (w / 2) .. +8, or MX blocks 0-2 / 3 and RoPE), the
+// partial scores are summed through LDS in a fixed order, and every wave then
+// runs the same softmax and accumulates P . V for its own 128 output columns.
 //
 // QF = 1: fp8 query. Q is quantised here (static scale read, or the dynamic
 // scale reduced from the partial maxima); `scale_out` makes this workgroup
