@@ -167,3 +167,36 @@ def test_mtp_full_size_sampled(mla, orc, dev, name, qlen):
     TQ = q.shape[0]
     sample = sorted({0, 1, qlen - 1, TQ // 2, TQ - qlen, TQ - 1})
     check((go[sample], gl[sample]), mtp_ref(orc, case, q, qo, True, rows=sample), f"mtp {name} q{qlen}")
+
+
+def test_prepared_mtp_call_matches_direct_call(mla, dev):
+    """prepare_decode_mtp (the benchmark's marshalled call) gives bitwise the direct call's result."""
+    case = syn.make_case(3, [700, 20, 1500], syn.KV_FP8, seed=595)
+    q, qo = syn.make_mtp_query([2, 2, 2], seed=596)
+    t = to_dev(case, dev)
+    qt = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).to(dev)
+    outs = []
+    for prepared in (False, True):
+        out = torch.empty((6, 16, 512), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((6, 16), dtype=torch.float32, device=dev)
+        kw = dict(total_q=6, causal=True, total_kv=case.total_kv, kv_dtype=syn.KV_FP8, uni_q_len=2)
+        args = (qt, None, t["kv"], t["kv_scales"], t["kv_indptr"], t["kv_indices"], out, lse)
+        if prepared:
+            call = mla.prepare_decode_mtp(*args, **kw)
+            out.fill_(float("nan"))
+            call()
+        else:
+            mla.mla_decode_mtp(*args, **kw)
+        torch.cuda.synchronize()
+        outs.append((out.float().cpu().numpy(), lse.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+def test_mtp_one_token_ragged_indptr_matches_uniform(mla, dev, kv_dtype):
+    """One query token per sequence through a ragged qo_indptr equals the uniform count of one."""
+    case = syn.make_case(5, [33, 0, 900, 64, 2], kv_dtype, seed=597)
+    qo = np.arange(6, dtype=np.int32)
+    a = run_mtp(mla, case, case.q, qo, dev, True, uni=1)
+    b = run_mtp(mla, case, case.q, qo, dev, False, uni=0)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

@@ -215,3 +215,38 @@ def test_q8_full_size_sampled(mla, orc, dev, name):
     ref, (_, rsc) = q8_ref(orc, case, batches=sample)
     assert gsc[0] == rsc[0]
     check((go[sample], gl[sample]), ref, f"q8 {name}")
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+def test_q8_scale_outside_fast_range_through_attention(mla, orc, dev, kv_dtype):
+    """A static scale of 2^-90 takes the kernels' IEEE-division fallback inside stage 1; the query saturates."""
+    case = syn.make_case(2, [150, 33], kv_dtype, seed=470 + kv_dtype)
+    scale = 2.0 ** -90
+    ref, (codes, _) = q8_ref(orc, case, scale=scale, sm_scale=2.0 ** 80)
+    assert ((codes & 0x7F) == 0x7E).mean() > 0.9
+    go, gl, _ = run_q8(mla, case, dev, 0, scale=scale, sm_scale=2.0 ** 80)
+    check((go, gl), ref, "q8 slow division")
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+def test_prepared_q8_call_matches_direct_call(mla, dev, kv_dtype):
+    """prepare_decode_q8 (the benchmark's marshalled call) gives bitwise the direct call's result."""
+    case = syn.make_case(3, [700, 20, 1500], kv_dtype, seed=480 + kv_dtype)
+    t = to_dev(case, dev)
+    outs = []
+    for prepared in (False, True):
+        out = torch.empty((3, 16, 512), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((3, 16), dtype=torch.float32, device=dev)
+        qs = torch.empty(1, dtype=torch.float32, device=dev)
+        kw = dict(q_scale_mode=mla.Q_SCALE_DYNAMIC, total_kv=case.total_kv, kv_dtype=kv_dtype)
+        args = (t["q"], qs, t["kv"], t["kv_scales"], t["kv_indptr"], t["kv_indices"], out, lse)
+        if prepared:
+            call = mla.prepare_decode_q8(*args, **kw)
+            out.fill_(float("nan"))
+            call()
+        else:
+            mla.mla_decode_q8(*args, **kw)
+        torch.cuda.synchronize()
+        outs.append((out.float().cpu().numpy(), lse.cpu().numpy(), qs.item()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    assert outs[0][2] == outs[1][2]
