@@ -243,6 +243,13 @@ def cpu_baseline(case, target_s):
         t += time.perf_counter() - t0
         reps += 1
     t /= reps
+    threads = oracle.max_threads()
+    # the same oracle on one thread, on a sample of at most a few sequences
+    n1 = max(1, min(n, 4))
+    t0 = time.perf_counter()
+    oracle.mla_decode(case.q, case.kv_dtype, case.kv, case.kv_scales, case.kv_indptr, case.kv_indices,
+                      batches=list(range(n1)), nthreads=1)
+    t1 = time.perf_counter() - t0
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -255,13 +262,37 @@ def cpu_baseline(case, target_s):
     return {
         "value": t * 1e6 * B / n,
         "unit": "us/call",
-        "cores": oracle.max_threads(),
+        "cores": threads,
         "kind": "oracle",
         "sample": f"{n} of {B} sequences of {case.meta['workload']} (fp64 C oracle, OpenMP over heads), "
                   f"mean of {reps} runs of {t:.3f} s, scaled by {B}/{n}",
         "host_cpu": cpu,
         "host_nproc": os.cpu_count(),
+        "single_thread": {"value": t1 * 1e6 * B / n1, "unit": "us/call", "cores": 1,
+                          "sample": f"{n1} of {B} sequences, one run of {t1:.3f} s, scaled by {B}/{n1}"},
     }
+
+
+def read_ceiling(dev, flush, nbytes=302 << 20, steps=10):
+    """Practical HBM read reference on this machine: a plain cold streaming read of nbytes (a torch
+    row-wise max over 4 KiB rows, the fastest plain torch read measured here), after the same
+    1 GiB read flush, HIP events around it, median GB/s."""
+    import torch
+
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    rows = buf.view(-1, 1024)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    rows.amax(dim=1)
+    for i in range(steps):
+        flush_read(flush)
+        ev[i][0].record()
+        rows.amax(dim=1)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    us = statistics.median(a.elapsed_time(b) * 1e3 for a, b in ev)
+    del rows, buf
+    return {"bytes": nbytes, "cold_us_median": us, "GBps": nbytes / (us * 1e-6) / 1e9,
+            "kernel": "torch amax over 4 KiB rows of a contiguous fp32 buffer"}
 
 
 def load_traffic(name):
@@ -373,6 +404,9 @@ def main():
         "timing": "HIP events on the launch stream, cold cache, mean over steps",
     }
     cpu = None if args.no_cpu_baseline else cpu_baseline(case, args.cpu_seconds)
+    ceiling = read_ceiling(dev, flush)
+    print(f"# plain cold read of {ceiling['bytes'] / 1e6:.0f} MB: {ceiling['cold_us_median']:.1f} us, "
+          f"{ceiling['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
     line = {
         "metric": "us/call and effective KV HBM GB/s (% of peak), MLA decode bs x kv grid",
         "value": head["cold_us_median"],
@@ -394,6 +428,7 @@ def main():
         "pct_hbm_peak_kv": head["pct_hbm_peak_kv"],
         "warm_us": head["warm_us"],
         "roofline": roofline,
+        "hbm_read_ceiling": ceiling,
         "cpu_baseline": cpu,
         "grid": results,
         "grid_q8": grid_q8,

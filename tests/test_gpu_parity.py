@@ -92,6 +92,9 @@ def check(got, ref, name=""):
     ro, rl = ref[0], ref[1]
     assert not np.any(np.isnan(go)), f"{name}: NaN in output"
     err = np.abs(go - ro)
+    rms = float(np.sqrt(np.mean(ro ** 2))) if ro.size else 0.0
+    print(f"{name}: max |gpu - oracle| {err.max() if err.size else 0.0:.3e}, "
+          f"err / rms(out) {(err.max() / rms) if rms > 0 else 0.0:.3e}")
     bad = err > ATOL + RTOL * np.abs(ro)
     assert not np.any(bad), f"{name}: {bad.sum()} outputs outside the band, max err {err.max():.3e}"
     if len(ref) > 2:
