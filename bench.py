@@ -310,8 +310,8 @@ def load_traffic(name):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(the decode path runs on a single MI355X; see DESIGN.md for how it would shard).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the decode path runs on a "
+              "single MI355X (decode would shard by batch, one share per GPU).", file=sys.stderr)
         sys.exit(2)
     import torch
 

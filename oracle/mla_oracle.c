@@ -31,7 +31,7 @@
  *    (the fp8-Q path): the query itself quantised to fp8 with one per-tensor
  *    scale; the attention then uses the decoded query (oracle_mla_decode_q8).
  *
- * Readings where the pages leave a step open (each is listed in the design doc):
+ * Readings where the pages leave a step open:
  *  - fp8 decoded value = binary32 product (code value) * kv_scale, one RNE
  *    rounding.
  *  - e8m0 code 255 is NaN; e4m3fn codes 0x7F / 0xFF are NaN.
