@@ -49,7 +49,8 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=HEADLINE, choices=sorted(set(syn.WORKLOADS) | set(syn.SWEEP) | set(syn.PAGED)))
+    ap.add_argument("--workload", default=HEADLINE,
+                    choices=sorted(set(syn.WORKLOADS) | set(syn.SWEEP) | set(syn.PAGED) | set(syn.RAGGED)))
     ap.add_argument("--flags", type=int, default=0, help="MLA_FLAG_* word (0 = library heuristic)")
     ap.add_argument("--no-grid", action="store_true", help="time only the headline workload")
     ap.add_argument("--sweep", action="store_true",
@@ -66,6 +67,7 @@ def parse_args():
     ap.add_argument("--mtp", type=int, default=0,
                     help="with --only-gpu-loop: this many causal query tokens per sequence (mla_decode_mtp)")
     ap.add_argument("--no-mtp-grid", action="store_true", help="skip timing the several-query-token variants")
+    ap.add_argument("--no-mixed-grid", action="store_true", help="skip timing the mixed-length batches")
     return ap.parse_args()
 
 
@@ -361,6 +363,23 @@ def main():
             print(f"# q8 {mode} {n}: cold {r['cold_us_median']:.2f} us, warm {r['warm_us']:.2f} us, "
                   f"{r['effective_kv_GBps']:.0f} GB/s KV ({r['pct_hbm_peak_kv']:.1f}% of 8 TB/s)",
                   file=sys.stderr, flush=True)
+    # Mixed-length batches (lengths uniform in [256, 16128]): the default plan (split-K) and the
+    # mixed-lengths hint (persistent grid).
+    grid_mixed = None
+    if not args.no_mixed_grid:
+        grid_mixed = {}
+        base_flags = args.flags
+        for n in syn.RAGGED:
+            for hint in (False, True):
+                args.flags = base_flags | (mla.FLAG_MIXED_LENGTHS if hint else 0)
+                r = measure(n, args, dev, flush)
+                r.pop("_case", None)
+                key = f"{n}/{'mixed_lengths_hint' if hint else 'default'}"
+                grid_mixed[key] = r
+                print(f"# mixed {key}: cold {r['cold_us_median']:.2f} us, {r['effective_kv_GBps']:.0f} GB/s KV "
+                      f"({r['pct_hbm_peak_kv']:.1f}% of 8 TB/s), plan {r['plan']}", file=sys.stderr, flush=True)
+        args.flags = base_flags
+        torch.cuda.empty_cache()
     # Several causal query tokens per sequence (mla_decode_mtp): 2 and 4 tokens on the headline
     # workload and on the bandwidth-bound fp8 64 x 8192 workload. Effective GB/s counts the cache once.
     grid_mtp = None
@@ -433,6 +452,7 @@ def main():
         "grid": results,
         "grid_q8": grid_q8,
         "grid_mtp": grid_mtp,
+        "grid_mixed": grid_mixed,
         "sweep": sweep,
         "kernel_source_hash": source_hash(),
         "host": platform.node(),

@@ -66,6 +66,9 @@ extern "C" {
 /* Flags (bit field). Zero selects the built-in heuristic. */
 #define MLA_FLAG_FORCE_SPLIT 0x1       /* split-K grid: (splits x batch) workgroups      */
 #define MLA_FLAG_FORCE_PERSISTENT 0x2  /* fixed grid, equal token shares over all batches */
+#define MLA_FLAG_MIXED_LENGTHS 0x4     /* hint: sequence lengths differ widely; the heuristic then
+                                          picks the persistent grid (ignored by paged and
+                                          several-query-token calls, which are split-K)   */
 #define MLA_FLAG_SPLITS_SHIFT 8        /* bits 8..15: split count for split-K (1..255)   */
 #define MLA_FLAG_GRID_SHIFT 16         /* bits 16..27: workgroups for persistent (1..4095)*/
 

@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     FLAG_FORCE_PERSISTENT,
     FLAG_FORCE_SPLIT,
     FLAG_GRID_SHIFT,
+    FLAG_MIXED_LENGTHS,
     FLAG_SPLITS_SHIFT,
     KV_BF16,
     KV_FP8_E4M3,

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmla_decode.so")
 
 NUM_HEADS, QK_DIM, V_DIM = 16, 576, 512
 KV_BF16, KV_FP8_E4M3, KV_MXFP4 = 0, 1, 2
-FLAG_FORCE_SPLIT, FLAG_FORCE_PERSISTENT = 0x1, 0x2
+FLAG_FORCE_SPLIT, FLAG_FORCE_PERSISTENT, FLAG_MIXED_LENGTHS = 0x1, 0x2, 0x4
 FLAG_SPLITS_SHIFT, FLAG_GRID_SHIFT = 8, 16
 Q_SCALE_STATIC, Q_SCALE_DYNAMIC = 0, 1
 

@@ -91,8 +91,8 @@ int make_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_inf
     if (force_split && force_pers) return MLA_ERR_INVALID_ARG;
     const int forced_splits = (flags >> MLA_FLAG_SPLITS_SHIFT) & 0xFF;
     const int forced_grid = (flags >> MLA_FLAG_GRID_SHIFT) & 0xFFF;
-    if (flags & ~(MLA_FLAG_FORCE_SPLIT | MLA_FLAG_FORCE_PERSISTENT | (0xFF << MLA_FLAG_SPLITS_SHIFT) |
-                  (0xFFF << MLA_FLAG_GRID_SHIFT)))
+    if (flags & ~(MLA_FLAG_FORCE_SPLIT | MLA_FLAG_FORCE_PERSISTENT | MLA_FLAG_MIXED_LENGTHS |
+                  (0xFF << MLA_FLAG_SPLITS_SHIFT) | (0xFFF << MLA_FLAG_GRID_SHIFT)))
         return MLA_ERR_INVALID_ARG;
 
     p->reserved = 0;
@@ -105,7 +105,12 @@ int make_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_inf
         p->workspace_bytes = 0;
         return MLA_OK;
     }
-    bool persistent = force_pers || (!force_split && forced_splits == 0 && prefer_persistent(batch, total_kv, kv_dtype));
+    // The caller's hint that sequence lengths differ selects the persistent
+    // grid: its equal token shares balance mixed lengths, where split-K's
+    // per-sequence splits leave the longest sequences on the critical path.
+    const bool mixed = (flags & MLA_FLAG_MIXED_LENGTHS) != 0 && total_kv >= kNumCUs;
+    bool persistent = force_pers || (!force_split && forced_splits == 0 &&
+                                     (mixed || prefer_persistent(batch, total_kv, kv_dtype)));
     if (persistent) {
         int g = forced_grid ? forced_grid : heuristic_grid(total_kv, kv_dtype);
         p->mode = 1;

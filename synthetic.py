@@ -256,11 +256,28 @@ PAGED = {
 }
 
 
+def ragged_lens(batch: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """Seeded per-sequence lengths, uniform in [lo, hi] (a mixed-length decode batch)."""
+    return np.random.default_rng(seed).integers(lo, hi + 1, size=batch)
+
+
+# Mixed-length batches with the same mean length as the 8192-token shapes:
+# lengths uniform in [256, 16128].
+RAGGED = {
+    "fp8_b64_ragged": dict(batch=64, kv_lens=ragged_lens(64, 256, 16128, 7), kv_dtype=KV_FP8, seed=7,
+                           pool_rows=SWEEP_POOL_ROWS),
+    "mxfp4_b32_ragged": dict(batch=32, kv_lens=ragged_lens(32, 256, 16128, 8), kv_dtype=KV_MXFP4, seed=8,
+                             pool_rows=SWEEP_POOL_ROWS),
+}
+
+
 def make_workload(name: str) -> Case:
     """A named workload; for the paged ones the page-level arrays are in meta['paged']."""
     if name in PAGED:
         c, paged = make_paged_case(**PAGED[name])
         c.meta["paged"] = paged
+    elif name in RAGGED:
+        c = make_case(**RAGGED[name])
     else:
         c = make_case(**(WORKLOADS[name] if name in WORKLOADS else SWEEP[name]))
     c.meta["workload"] = name

@@ -108,6 +108,20 @@ def test_forced_plans(mla):
     assert p.mode == 1 and p.grid == 4000 // 128  # at least 128 tokens per workgroup
 
 
+def test_mixed_lengths_hint_selects_persistent(mla):
+    hint = mla.FLAG_MIXED_LENGTHS
+    p = mla.mla_decode_plan(64, 560343, 1, hint)
+    assert p.mode == 1 and p.grid == mla.mla_decode_plan(64, 560343, 1, mla.flags_for(persistent=True)).grid
+    assert p.num_partials == p.grid + 64 - 1 and p.combine == 1
+    # a forced split count or split-K wins over the hint; a tiny batch ignores it
+    assert mla.mla_decode_plan(64, 560343, 1, hint | mla.flags_for(splits=8)).mode == 0
+    assert mla.mla_decode_plan(64, 560343, 1, hint | mla.FLAG_FORCE_SPLIT).mode == 0
+    assert mla.mla_decode_plan(2, 100, 1, hint).mode == 0
+    # calls that always plan split-K accept the hint and stay split-K
+    assert mla.mla_decode_mtp_workspace_size(32, 64, 32 * 8192, 1, hint) == \
+        mla.mla_decode_mtp_workspace_size(32, 64, 32 * 8192, 1, 0)
+
+
 @pytest.mark.parametrize("args", [
     (-1, 10, 1, 0),            # negative batch
     (2, -1, 1, 0),             # negative total

@@ -339,6 +339,19 @@ def test_sweep_shape_sampled(mla, orc, dev, name):
     check((got_o[sample], got_l[sample]), oracle_ref(orc, case, batches=sample), name)
 
 
+@pytest.mark.parametrize("name", list(syn.RAGGED))
+@pytest.mark.parametrize("hint", [False, True])
+def test_mixed_length_workload_sampled(mla, orc, dev, name, hint):
+    """Full-size mixed-length batches, default plan (split-K) and with the mixed-lengths hint (persistent)."""
+    case = syn.make_workload(name)
+    flags = mla.FLAG_MIXED_LENGTHS if hint else 0
+    assert mla.mla_decode_plan(case.batch, case.total_kv, case.kv_dtype, flags).mode == (1 if hint else 0)
+    got_o, got_l = run_gpu(mla, case, dev, flags=flags, nan_workspace=False)
+    B = case.batch
+    sample = sorted({0, 1, B // 3, B // 2, B - 1})
+    check((got_o[sample], got_l[sample]), oracle_ref(orc, case, batches=sample), f"{name} hint={hint}")
+
+
 # ------------------------------------------------------------------ paged cache
 
 def run_gpu_paged(mla, case, paged, dev, flags=0):
