@@ -949,15 +949,16 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
 // identity; correctness never depends on where a workgroup runs.
 __device__ __forceinline__ int xcd_order(int x, int n) { return (n & 7) ? x : (x & 7) * (n >> 3) + (x >> 3); }
 
-// Sequence of query row `row` from a ragged qo_indptr: the number of k in
-// 1..batch with qo_indptr[k] <= row, counted by the whole workgroup (wave
-// ballots summed through the 4 ints at cnt, in LDS).
-__device__ __forceinline__ int row_sequence(const Params& P, int row, int* cnt) {
+// The number of k in 1..n with ptr[k] <= v, counted by the whole workgroup in
+// one pass of loads per 256 entries (wave ballots summed through the 4 ints
+// at cnt, in LDS). For a non-decreasing ptr with ptr[0] <= v < ptr[n] this is
+// the b with ptr[b] <= v < ptr[b + 1].
+__device__ __forceinline__ int count_le(const int32_t* ptr, int n, int v, int* cnt) {
     int b = 0;
     const int tid = threadIdx.x;
-    for (int c = 0; c < P.batch; c += kThreads) {
+    for (int c = 0; c < n; c += kThreads) {
         const int k = c + tid + 1;
-        const uint64_t m = __ballot(k <= P.batch && P.qo_indptr[k] <= row);
+        const uint64_t m = __ballot(k <= n && ptr[k] <= v);
         if ((tid & 63) == 0) cnt[tid >> 6] = __popcll(m);
         __syncthreads();
         b += cnt[0] + cnt[1] + cnt[2] + cnt[3];
@@ -981,7 +982,7 @@ void split_kernel(Params P) {
             n = P.uni_q;
             t = row - b * n;
         } else {
-            b = row_sequence(P, row, reinterpret_cast<int*>(smem + Layout<KV>::kIdxOff));
+            b = count_le(P.qo_indptr, P.batch, row, reinterpret_cast<int*>(smem + Layout<KV>::kIdxOff));
             const int r0 = P.qo_indptr[b];
             n = P.qo_indptr[b + 1] - r0;
             t = row - r0;
@@ -1021,11 +1022,7 @@ void persistent_kernel(Params P) {
     }
     bool scale_out = blockIdx.x == 0;
     // first sequence b with indptr[b] <= g0 < indptr[b+1]
-    int lo = 0, hi = P.batch - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (P.indptr[mid] <= g0) lo = mid; else hi = mid - 1;
-    }
+    const int lo = count_le(P.indptr, P.batch, (int)g0, reinterpret_cast<int*>(smem + Layout<KV>::kIdxOff));
     for (int b = lo; b < P.batch; ++b) {
         const int s = P.indptr[b], e = P.indptr[b + 1];
         if (s >= g1) break;
@@ -1074,10 +1071,12 @@ constexpr int kCombBatch = 8;                             // partials in flight 
 // Items per combine workgroup: as many as keep each thread at <= 8 partial
 // loads (one round trip). The persistent plan's per-sequence partial counts
 // vary, so it takes one item per workgroup.
-static int combine_items(int mode, int nsplit) {
-    if (mode != 0) return 1;
+// Items per combine workgroup for `parts` partials per sequence (split-K: the
+// split count; persistent: about grid / batch + 1 shares touch a sequence, and
+// any other count is merged correctly, only with other parallelism).
+static int combine_items(int parts) {
     int i = 8;
-    while (i > 1 && (nsplit * i + kCombGroups - 1) / kCombGroups > kCombBatch) i /= 2;
+    while (i > 1 && (parts * i + kCombGroups - 1) / kCombGroups > kCombBatch) i /= 2;
     return i;
 }
 
@@ -1119,8 +1118,10 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineParams C) 
             l[v] = -INFINITY;
             o[v] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (k < count) {
-                // an empty persistent share wrote nothing: its slot holds no partial
-                const bool empty = C.mode == 1 && share_start(p, C.total, C.grid) == share_start(p + 1, C.total, C.grid);
+                // an empty persistent share (only when there are fewer tokens than
+                // workgroups) wrote nothing: its slot holds no partial
+                const bool empty = C.mode == 1 && C.total < C.grid &&
+                                   share_start(p, C.total, C.grid) == share_start(p + 1, C.total, C.grid);
                 if (!empty) {
                     const int64_t slot = base + p;
                     l[v] = C.part_lse[slot * kHeads + h];
@@ -1348,7 +1349,7 @@ static int launch(const mla_plan_info& plan, const Params& P, hipStream_t stream
         C.nsplit = plan.num_splits;
         C.grid = plan.grid;
         C.total = P.total;
-        C.items = combine_items(plan.mode, plan.num_splits);
+        C.items = combine_items(plan.mode == 0 ? plan.num_splits : (plan.grid + P.rows - 1) / P.rows + 1);
         hipLaunchKernelGGL(combine_kernel, dim3(kHeads * 4 * P.rows / C.items), dim3(kCombThreads), 0, stream, C);
         if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
     }
