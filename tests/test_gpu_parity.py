@@ -220,6 +220,19 @@ def test_persistent_grid(mla, orc, dev, kv_dtype, grid):
           f"persistent grid={grid}")
 
 
+@pytest.mark.parametrize("grid", [97, 512])
+def test_persistent_many_sequences(mla, orc, dev, grid):
+    """More sequences than a workgroup's threads (the first-sequence count runs over several chunks), with empty
+    sequences; shares start inside, at and across sequence boundaries."""
+    rng = np.random.default_rng(611)
+    lens = rng.integers(0, 60, size=600)
+    lens[::7] = 0
+    case = syn.make_case(600, lens, syn.KV_FP8, seed=612, shuffle=True)
+    got_o, got_l = run_gpu(mla, case, dev, flags=mla.flags_for(persistent=True, grid=grid))
+    sample = sorted({0, 1, 7, 299, 300, 301, 511, 598, 599} | set(range(250, 262)))
+    check((got_o[sample], got_l[sample]), oracle_ref(orc, case, batches=sample), f"600 sequences grid={grid}")
+
+
 @pytest.mark.parametrize("kv_dtype", DTYPES)
 @pytest.mark.parametrize("L", [1, 15, 16, 17, 31, 32, 33, 63, 65, 127, 129, 1000])
 def test_lengths_single_sequence(mla, orc, dev, kv_dtype, L):
