@@ -224,6 +224,51 @@ def measure(name, args, dev, flush, q8=None, mtp=0):
     }
 
 
+def measure_graph(name, args, dev, flush):
+    """The same call captured once in a HIP graph and replayed: cold median per replay (events around each
+    replay, read flush before it), as a serving loop that captures its decode step would run it."""
+    import torch
+
+    import mla_decode_02_amd as mla
+    import synthetic as syn
+
+    case = syn.make_workload(name)
+    q, kv, sc, indptr, indices = upload(case, dev)
+    B = case.batch
+    out = torch.empty((B, 16, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, 16), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(mla.mla_decode_workspace_size(B, case.total_kv, case.kv_dtype, args.flags), 16),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        mla.mla_decode(q, kv, sc, indptr, indices, out, lse, total_kv=case.total_kv, kv_dtype=case.kv_dtype,
+                       workspace=ws, flags=args.flags)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        flush_read(flush)
+        ev[i][0].record()
+        g.replay()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    return {"workload": name, "cold_us_median": statistics.median(us), "cold_us_p10": us[len(us) // 10],
+            "cold_us_p90": us[(9 * len(us)) // 10],
+            "effective_kv_GBps": case.kv_bytes() / (statistics.median(us) * 1e-6) / 1e9}
+
+
 def cpu_baseline(case, target_s):
     """Time the fp64 oracle on a bounded sample of sequences; scale to the whole call."""
     import oracle
@@ -393,6 +438,11 @@ def main():
                 print(f"# mtp q{k} {n}: cold {r['cold_us_median']:.2f} us, warm {r['warm_us']:.2f} us, "
                       f"{r['effective_kv_GBps']:.0f} GB/s KV counted once ({r['pct_hbm_peak_kv']:.1f}% of 8 TB/s)",
                       file=sys.stderr, flush=True)
+    graph = None
+    if args.workload not in syn.PAGED:  # the graph leg replays mla_decode (page size 1)
+        graph = measure_graph(args.workload, args, dev, flush)
+        print(f"# graph replay {args.workload}: cold {graph['cold_us_median']:.2f} us "
+              f"(p10 {graph['cold_us_p10']:.2f}, p90 {graph['cold_us_p90']:.2f})", file=sys.stderr, flush=True)
     head = results[args.workload]
     case = head.pop("_case")
     for r in results.values():
@@ -448,6 +498,7 @@ def main():
         "warm_us": head["warm_us"],
         "roofline": roofline,
         "hbm_read_ceiling": ceiling,
+        "graph_replay": graph,
         "cpu_baseline": cpu,
         "grid": results,
         "grid_q8": grid_q8,
