@@ -99,6 +99,11 @@ struct Params {
     int uni_q;
     int causal;
     int rows;
+    // Split-K with page size 1 and one row per sequence, when total is a
+    // multiple of batch: uni_len = total / batch and its split chunk (the
+    // length every sequence has when the lengths are equal); else 0.
+    int uni_len;
+    int uni_chunk;
 };
 
 // ---------------------------------------------------------------------------
@@ -205,6 +210,11 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
 __device__ __forceinline__ void dma2(const void* g, uint32_t lds) {
     uint32_t save;
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_ushort %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(save) : "v"(g), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+    uint32_t save;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
                  : "=&s"(save) : "v"(g), "s"(lds) : "memory");
 }
 // Wave-uniform 32-bit LDS address of a pointer into shared memory.
@@ -713,6 +723,81 @@ __device__ __forceinline__ void wait_own(int groups, int hi) {
     else wait_vmcnt<N * k0>();
 }
 
+constexpr int kQGroups = kHeads * kDqk / 8;                   // 8-element groups of one query row
+constexpr int kQPer = (kQGroups + kThreads - 1) / kThreads;  // of them per thread (fp8 query)
+template <int KV>
+constexpr int kIdxPer = Fmt<KV>::kIdxWindow / kThreads;      // index entries per thread and window
+
+// Entries [w0, w0 + n) of a sequence whose kv_indices entries start at
+// `base`, as cache rows: thread tid takes entry w0 + tid + k * kThreads into
+// iv[k] (0 at or beyond n, never used). Token j is row indices[base + j]
+// (page size 1), else row indices[base + j / page_size] * page_size +
+// j % page_size.
+template <int KV>
+__device__ __forceinline__ void load_idx(const Params& P, int base, int w0, int n, int32_t (&iv)[kIdxPer<KV>]) {
+    const int tid = threadIdx.x, ps = P.page_size;
+#pragma unroll
+    for (int k = 0; k < kIdxPer<KV>; ++k) {
+        const int j = w0 + tid + k * kThreads;
+        iv[k] = 0;
+        if (tid + k * kThreads < n) {
+            if (ps == 1) {
+                iv[k] = P.indices[base + j];
+            } else {
+                const int pg = j / ps;
+                iv[k] = P.indices[base + pg] * ps + (j - pg * ps);
+            }
+        }
+    }
+}
+
+// Page size 1: entries [first, first + n) of kv_indices (n >= 1) straight
+// into the LDS index window idx, entry first + i at idx[i]; the threads past
+// n re-read entry first + n - 1 into idx[n..], which is never used.
+template <int KV>
+__device__ __forceinline__ void dma_idx(const Params& P, int first, int n, int32_t* idx) {
+    const int tid = threadIdx.x, wave0 = tid & ~63;
+#pragma unroll
+    for (int k = 0; k < kIdxPer<KV>; ++k)
+        dma4(P.indices + first + min(tid + k * kThreads, n - 1), lds_addr(idx + k * kThreads + wave0));
+}
+
+// One query row in registers, with the scales read alongside it.
+//   bf16 query: this wave's half of Q^T, straight in the score operand layout.
+//   fp8 query: thread tid holds the 8-element groups tid, tid + 256, ... of
+//   the row's 16 x 576 query, quantised once per workgroup later on.
+template <int KV, int QF>
+struct QueryRegs {
+    typename QOperand<KV, QF>::T qB[QF && KV == MLA_KV_MXFP4 ? 3 : kHalfK];
+    bf16x8 qg[QF ? kQPer : 1];
+    float kv_scale, q_scale, q_part;
+};
+
+template <int KV, int QF>
+__device__ __forceinline__ void load_query(const Params& P, int b, QueryRegs<KV, QF>& q) {
+    const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, r = lane & 15;
+    const int hf = __builtin_amdgcn_readfirstlane(tid >> 6) >> 1;
+    const __bf16* qseq = P.q + (int64_t)b * kHeads * kDqk;
+    q.kv_scale = 1.0f;
+    if constexpr (KV == MLA_KV_FP8_E4M3) q.kv_scale = *reinterpret_cast<const float*>(P.kv_scales);
+    q.q_scale = 1.0f;
+    q.q_part = 0.0f;
+    if constexpr (QF) {
+#pragma unroll
+        for (int k = 0; k < kQPer; ++k) {
+            q.qg[k] = bf16x8{};
+            if (tid + k * kThreads < kQGroups) q.qg[k] = *reinterpret_cast<const bf16x8*>(qseq + 8 * (tid + k * kThreads));
+        }
+        if (P.q_amax) q.q_part = tid < P.q_amax_n ? P.q_amax[tid] : 0.0f;
+        else q.q_scale = *P.q_scale;
+    } else {
+        const __bf16* qrow = qseq + r * kDqk;
+#pragma unroll
+        for (int j = 0; j < kHalfK; ++j)
+            q.qB[j] = *reinterpret_cast<const bf16x8*>(qrow + dbase<KV>(kHalfK * hf + j, G));
+    }
+}
+
 // Attend tokens [t0, t1) of one sequence (positions within it; its
 // kv_indices entries start at `base`) with query row b, using the whole
 // workgroup, and write the result: the final bf16 output row b + lse when
@@ -730,7 +815,7 @@ __device__ __forceinline__ void wait_own(int groups, int hi) {
 // publish a dynamic scale.
 template <int KV, int QF>
 __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, int t1, bool final, int slot,
-                       bool scale_out) {
+                       bool scale_out, QueryRegs<KV, QF>& qr, bool idx_dma, bool idx_staged) {
     using L = Layout<KV>;
     constexpr int R = Fmt<KV>::kRing;
     constexpr int D = R - 1;  // steps issued ahead of the one computed
@@ -743,65 +828,33 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
     float* fs_buf = reinterpret_cast<float*>(smem + L::kFsOff);
     const int pv_off = pv_lane_offset<KV>(lane, wave);
 
-    float kv_scale = 1.0f;
-    if constexpr (KV == MLA_KV_FP8_E4M3) kv_scale = *reinterpret_cast<const float*>(P.kv_scales);
-
-    // The first index window and this wave's half of Q^T are requested together
-    // so that the workgroup start pays one memory round trip for both.
+    // The first index window (unless the caller's LDS-DMA of a guessed window
+    // already holds it) and the query are in flight together here.
     constexpr int kIdxWindow = Fmt<KV>::kIdxWindow;
-    constexpr int kPer = kIdxWindow / kThreads;
+    constexpr int kPer = kIdxPer<KV>;
     int32_t iv[kPer];
-    auto load_idx = [&](int w0, int n) {
-        const int ps = P.page_size;
-#pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-            const int j = w0 + tid + k * kThreads;
-            iv[k] = 0;
-            if (tid + k * kThreads < n) {
-                if (ps == 1) {
-                    iv[k] = P.indices[base + j];
-                } else {
-                    const int pg = j / ps;
-                    iv[k] = P.indices[base + pg] * ps + (j - pg * ps);
-                }
-            }
-        }
-    };
-    load_idx(t0, min(kIdxWindow, t1 - t0));
-    // bf16 query: this wave's half of Q^T straight into the score operands.
-    // fp8 query: thread tid loads the 8-element groups tid, tid + 256, ... of
-    // the sequence's 16 x 576 query, which are quantised once per workgroup
-    // after the first gathers are issued (below).
-    constexpr int kQGroups = kHeads * kDqk / 8;
-    constexpr int kQPer = (kQGroups + kThreads - 1) / kThreads;
+    if (!idx_staged) load_idx<KV>(P, base, t0, min(kIdxWindow, t1 - t0), iv);
     using QOp = typename QOperand<KV, QF>::T;
     constexpr bool kMx = QF && KV == MLA_KV_MXFP4;  // scores on the MX-scaled MFMA
-    QOp qB[kMx ? 3 : kHalfK];
-    bf16x8 qg[QF ? kQPer : 1];
-    float q_scale = 1.0f, q_part = 0.0f;
+    auto& qB = qr.qB;
+    auto& qg = qr.qg;
+    const float kv_scale = qr.kv_scale, q_part = qr.q_part;
+    float q_scale = qr.q_scale;
     const __bf16* qseq = P.q + (int64_t)b * kHeads * kDqk;
-    if constexpr (QF) {
-#pragma unroll
-        for (int k = 0; k < kQPer; ++k) {
-            qg[k] = bf16x8{};
-            if (tid + k * kThreads < kQGroups) qg[k] = *reinterpret_cast<const bf16x8*>(qseq + 8 * (tid + k * kThreads));
-        }
-        if (P.q_amax) q_part = tid < P.q_amax_n ? P.q_amax[tid] : 0.0f;
-        else q_scale = *P.q_scale;
-#pragma unroll
-        for (int k = 0; k < kQPer; ++k) asm volatile("" ::"v"(qg[k]));
-    } else {
-        const __bf16* qrow = qseq + r * kDqk;
-#pragma unroll
-        for (int j = 0; j < kHalfK; ++j)
-            qB[j] = *reinterpret_cast<const bf16x8*>(qrow + dbase<KV>(kHalfK * hf + j, G));
-#pragma unroll
-        for (int j = 0; j < kHalfK; ++j) asm volatile("" ::"v"(qB[j]));
-    }
     // Consume Q and the scales here: the compiler's wait for these loads must
     // not land inside the token loop, where the count it waits for would also
     // drain the gathers in flight (it does not see the LDS-DMA loads).
+    if constexpr (QF) {
+#pragma unroll
+        for (int k = 0; k < kQPer; ++k) asm volatile("" ::"v"(qg[k]));
+    } else {
+#pragma unroll
+        for (int j = 0; j < kHalfK; ++j) asm volatile("" ::"v"(qB[j]));
+    }
     asm volatile("" ::"v"(kv_scale), "v"(q_part), "v"(q_scale));
+    // The caller's index DMA, kept or not, has landed before anything else
+    // touches the index window (no gathers are in flight yet).
+    if (idx_dma) wait_vmcnt<0>();
     if constexpr (QF) {
         if (P.q_amax) {
             q_scale = q8_dynamic_scale(q_part, reinterpret_cast<float*>(sbuf), tid);
@@ -819,10 +872,12 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
     for (int w0 = t0; w0 < t1; w0 += kIdxWindow) {
         const int n = min(kIdxWindow, t1 - w0);
         __syncthreads();  // every wave is done with the previous window / previous range
-        if (w0 != t0) load_idx(w0, n);
+        if (w0 != t0) load_idx<KV>(P, base, w0, n, iv);
+        if (w0 != t0 || !idx_staged) {
 #pragma unroll
-        for (int k = 0; k < kPer; ++k)
-            if (tid + k * kThreads < n) idx[tid + k * kThreads] = iv[k];
+            for (int k = 0; k < kPer; ++k)
+                if (tid + k * kThreads < n) idx[tid + k * kThreads] = iv[k];
+        }
         __syncthreads();
         const int nsteps = (n + kStepTokens - 1) / kStepTokens;
         // This wave's half of tile `tile` of step i into ring slot i % R; tokens
@@ -967,12 +1022,47 @@ __device__ __forceinline__ int count_le(const int32_t* ptr, int n, int v, int* c
     return b;
 }
 
+// The stage-1 kernels take the fields their first loads need ahead of Params
+// as plain arguments: those arrive in SGPRs when the waves start (kernel
+// argument preloading), so the query and index requests leave without first
+// waiting for the kernel-argument segment to be read.
+// (The launched grid size comes the same way: gridDim is read from the
+// kernel-argument segment.)
+#define STAGE1_ARGS                                                                                       \
+    const __bf16 *q_arg, const int32_t *indices_arg, const void *kv_scales_arg, int nsplit_arg, int uni_len_arg, \
+        int uni_chunk_arg, int nblocks, Params P_arg
+__device__ __forceinline__ Params stage1_params(const __bf16* q, const int32_t* indices, const void* kv_scales,
+                                                int nsplit, int uni_len, int uni_chunk, const Params& P_arg) {
+    Params P = P_arg;
+    P.q = q;
+    P.indices = indices;
+    P.kv_scales = kv_scales;
+    P.nsplit = nsplit;
+    P.uni_len = uni_len;
+    P.uni_chunk = uni_chunk;
+    return P;
+}
+
 template <int KV, int QF>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Fmt<KV>::kWgsPerCU, Fmt<KV>::kWgsPerCU)))
-void split_kernel(Params P) {
+void split_kernel(STAGE1_ARGS) {
+    const Params P = stage1_params(q_arg, indices_arg, kv_scales_arg, nsplit_arg, uni_len_arg, uni_chunk_arg, P_arg);
     __shared__ __attribute__((aligned(16))) uint8_t smem[Layout<KV>::kBytes];
-    const int item = xcd_order(blockIdx.x, gridDim.x);
+    const int item = xcd_order(blockIdx.x, nblocks);
     const int row = item / P.nsplit, s = item % P.nsplit;
+    QueryRegs<KV, QF> qr;
+    load_query<KV, QF>(P, row, qr);
+    // Sequences of one common length Lu (page size 1, one query row each):
+    // sequence b's entries would start at b * Lu, so this split's first index
+    // window is requested now, with the query, before kv_indptr arrives. It
+    // is kept when kv_indptr confirms the guess and read again otherwise; the
+    // guessed entries lie within kv_indices [batch * Lu] either way.
+    const int Lu = P.uni_len;
+    const int t0u = min(Lu, s * P.uni_chunk), t1u = min(Lu, t0u + P.uni_chunk);
+    const bool idx_dma = t1u > t0u;  // Lu > 0
+    if (idx_dma)
+        dma_idx<KV>(P, row * Lu + t0u, min(Fmt<KV>::kIdxWindow, t1u - t0u),
+                    reinterpret_cast<int32_t*>(smem + Layout<KV>::kIdxOff));
     // the sequence of this query row, and the cache tokens the causal reading hides from it
     int b = row, hide = 0;
     if (P.uni_q > 0 || P.qo_indptr) {
@@ -996,7 +1086,9 @@ void split_kernel(Params P) {
     const int chunk = ((L + P.nsplit - 1) / P.nsplit + kStepTokens - 1) / kStepTokens * kStepTokens;
     const int t0 = min(L, s * chunk);
     const int t1 = min(L, t0 + chunk);
-    run_wg<KV, QF>(P, smem, row, base, t0, t1, P.nsplit == 1, row * P.nsplit + s, blockIdx.x == 0);
+    const bool staged = idx_dma && base == row * Lu && L == Lu;  // then t0, t1 are t0u, t1u
+    run_wg<KV, QF>(P, smem, row, base, t0, t1, P.nsplit == 1, row * P.nsplit + s, blockIdx.x == 0, qr, idx_dma,
+                   staged);
 }
 
 // Largest p whose share [floor(p T / G), floor((p+1) T / G)) starts at or before t.
@@ -1005,10 +1097,11 @@ __device__ __forceinline__ int64_t share_start(int64_t p, int64_t T, int64_t G) 
 
 template <int KV, int QF>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Fmt<KV>::kWgsPerCU, Fmt<KV>::kWgsPerCU)))
-void persistent_kernel(Params P) {
+void persistent_kernel(STAGE1_ARGS) {
+    const Params P = stage1_params(q_arg, indices_arg, kv_scales_arg, nsplit_arg, uni_len_arg, uni_chunk_arg, P_arg);
     __shared__ __attribute__((aligned(16))) uint8_t smem[Layout<KV>::kBytes];
     const int64_t T = P.total, Gn = P.grid;
-    const int p = xcd_order(blockIdx.x, gridDim.x);
+    const int p = xcd_order(blockIdx.x, nblocks);
     const int64_t g0 = share_start(p, T, Gn), g1 = share_start(p + 1, T, Gn);
     if (g0 >= g1) {
         // an empty share; workgroup 0 still publishes a dynamic query scale
@@ -1030,7 +1123,10 @@ void persistent_kernel(Params P) {
         if (t0 >= t1) continue;
         const bool whole = (s >= g0) && (e <= g1);
         __syncthreads();  // the previous sequence's epilogue has finished reading LDS
-        run_wg<KV, QF>(P, smem, b, s, t0 - s, t1 - s, whole, p + b, scale_out);  // page size 1: entries are tokens
+        QueryRegs<KV, QF> qr;
+        load_query<KV, QF>(P, b, qr);
+        // page size 1: entries are tokens
+        run_wg<KV, QF>(P, smem, b, s, t0 - s, t1 - s, whole, p + b, scale_out, qr, false, false);
         scale_out = false;
     }
 }
@@ -1080,13 +1176,23 @@ static int combine_items(int parts) {
     return i;
 }
 
-__global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineParams C) {
+// (part_o, part_lse, mode, nsplit and items lead as plain arguments, preloaded
+// into SGPRs like the stage-1 kernels' first fields.)
+__global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* part_o_arg, const float* part_lse_arg,
+                                                               int mode_arg, int nsplit_arg, int items_arg,
+                                                               int nblocks, CombineParams C_arg) {
+    CombineParams C = C_arg;
+    C.part_o = part_o_arg;
+    C.part_lse = part_lse_arg;
+    C.mode = mode_arg;
+    C.nsplit = nsplit_arg;
+    C.items = items_arg;
     __shared__ f32x4 s_acc[kCombGroups][kCombQuads];
     __shared__ float s_m[kCombGroups];
     __shared__ float s_w[kCombGroups];
     const int I = C.items, gpi = kCombGroups / I;  // items per workgroup, groups per item
     const int wpb = 4 * kHeads / I;                // workgroups per sequence
-    const int L = xcd_order(blockIdx.x, gridDim.x);
+    const int L = xcd_order(blockIdx.x, nblocks);
     const int b = L / wpb, it0 = (L % wpb) * I;
     const int tid = threadIdx.x, quad = tid & (kCombQuads - 1), gi = tid / kCombQuads;
     const int u = gi / gpi, gq = gi % gpi;         // this thread's item and its group within the item
@@ -1333,9 +1439,11 @@ static int launch(const mla_plan_info& plan, const Params& P, hipStream_t stream
         if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
     }
     if (plan.mode == 0)
-        hipLaunchKernelGGL((split_kernel<KV, QF>), dim3(plan.grid), dim3(kThreads), 0, stream, P);
+        hipLaunchKernelGGL((split_kernel<KV, QF>), dim3(plan.grid), dim3(kThreads), 0, stream, P.q, P.indices,
+                           P.kv_scales, P.nsplit, P.uni_len, P.uni_chunk, plan.grid, P);
     else
-        hipLaunchKernelGGL((persistent_kernel<KV, QF>), dim3(plan.grid), dim3(kThreads), 0, stream, P);
+        hipLaunchKernelGGL((persistent_kernel<KV, QF>), dim3(plan.grid), dim3(kThreads), 0, stream, P.q, P.indices,
+                           P.kv_scales, P.nsplit, P.uni_len, P.uni_chunk, plan.grid, P);
     if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
     if (plan.combine) {
         CombineParams C;
@@ -1350,7 +1458,9 @@ static int launch(const mla_plan_info& plan, const Params& P, hipStream_t stream
         C.grid = plan.grid;
         C.total = P.total;
         C.items = combine_items(plan.mode == 0 ? plan.num_splits : (plan.grid + P.rows - 1) / P.rows + 1);
-        hipLaunchKernelGGL(combine_kernel, dim3(kHeads * 4 * P.rows / C.items), dim3(kCombThreads), 0, stream, C);
+        const int nblocks = kHeads * 4 * P.rows / C.items;
+        hipLaunchKernelGGL(combine_kernel, dim3(nblocks), dim3(kCombThreads), 0, stream, C.part_o, C.part_lse, C.mode,
+                           C.nsplit, C.items, nblocks, C);
         if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
     }
     return MLA_OK;
@@ -1430,6 +1540,13 @@ static int decode_impl(const void* q, const void* kv, const void* kv_scales, con
     P.uni_q = mtp ? mtp->uni_q : 0;
     P.causal = mtp ? mtp->causal : 0;
     P.rows = rows;
+    P.uni_len = 0;
+    P.uni_chunk = 0;
+    if (plan.mode == 0 && page_size == 1 && !mtp && total_kv > 0 && total_kv % batch == 0) {
+        const int Lu = (int)(total_kv / batch), ns = plan.num_splits;
+        P.uni_len = Lu;
+        P.uni_chunk = ((Lu + ns - 1) / ns + kStepTokens - 1) / kStepTokens * kStepTokens;  // as the kernel splits
+    }
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (q_mode >= 0) {

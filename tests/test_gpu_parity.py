@@ -249,6 +249,24 @@ def test_long_sequence_several_index_windows(mla, orc, dev, kv_dtype):
 
 
 @pytest.mark.parametrize("kv_dtype", DTYPES)
+@pytest.mark.parametrize("lens,splits", [
+    ([256] * 4, 0),       # equal lengths: every split keeps its guessed first index window
+    ([256] * 4, 3),
+    ([3000] * 2, 1),      # kept first window, the later windows read as usual
+    ([0, 600], 0),        # total a multiple of batch but lengths differ: guesses rejected, one range empty
+    ([100, 500], 2),
+    ([1, 2, 3, 2], 0),    # only the last sequence sits where the guess puts it
+])
+def test_equal_length_index_guess(mla, orc, dev, kv_dtype, lens, splits):
+    """Split-K requests the first index window of sequence b at entry b * total / batch
+    before kv_indptr arrives; kept or rejected, the result is the oracle's (shuffled
+    rows, so a wrongly kept window would attend the wrong tokens)."""
+    case = syn.make_case(len(lens), lens, kv_dtype, seed=71, shuffle=True)
+    flags = mla.flags_for(splits=splits) if splits else 0
+    check(run_gpu(mla, case, dev, flags), oracle_ref(orc, case), f"lens {lens} splits {splits}")
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
 def test_all_sequences_empty(mla, orc, dev, kv_dtype):
     case = syn.make_case(3, [0, 0, 0], kv_dtype, seed=61, extra_rows=4)
     for flags in (0, mla.flags_for(splits=4), mla.flags_for(persistent=True, grid=3)):
