@@ -266,6 +266,19 @@ def test_equal_length_index_guess(mla, orc, dev, kv_dtype, lens, splits):
     check(run_gpu(mla, case, dev, flags), oracle_ref(orc, case), f"lens {lens} splits {splits}")
 
 
+@pytest.mark.parametrize("kv_dtype", [syn.KV_FP8, syn.KV_MXFP4])
+@pytest.mark.parametrize("lens", [[5000, 37, 2600], [33, 64, 95, 1], [4097] * 2])
+def test_split_grids_around_one_per_cu(mla, orc, dev, kv_dtype, lens):
+    """The same batch under split grids from a few workgroups to just over one per compute
+    unit: odd and even step counts, empty and one-step ranges, several index windows."""
+    case = syn.make_case(len(lens), lens, kv_dtype, seed=72, shuffle=True)
+    ref = oracle_ref(orc, case)
+    for splits in (1, 3, 85, 86):  # grids 3..258 workgroups for three sequences
+        if splits * case.batch > 512:
+            continue
+        check(run_gpu(mla, case, dev, mla.flags_for(splits=splits)), ref, f"lens {lens} splits {splits}")
+
+
 @pytest.mark.parametrize("kv_dtype", DTYPES)
 def test_all_sequences_empty(mla, orc, dev, kv_dtype):
     case = syn.make_case(3, [0, 0, 0], kv_dtype, seed=61, extra_rows=4)
