@@ -8,7 +8,9 @@
 // the tokens, output over the first 512 dims of the same rows.
 //
 // Stage 1: one workgroup of four waves attends one token range of one query
-// row, in 32-token steps (two 16-token tiles). Per step:
+// row, in 32-token steps (two 16-token tiles). At wave start the query and,
+// on batches of equal lengths, a guessed first window of kv_indices are
+// requested together with the sequence's kv_indptr entries. Per step:
 //   1. The step's 32 cache rows are gathered through kv_indices straight from
 //      HBM into an LDS ring with LDS-DMA loads (global_load_lds_dwordx4; the
 //      MXFP4 scales with two-byte DMAs), kRing - 1 steps ahead of use. Each
@@ -16,7 +18,7 @@
 //      64u + 16G of row r for load u: the MFMA operand layout of the scores.
 //   2. Scores S^T[16 tokens x 16 heads] = K . Q^T: wave w computes tile w % 2
 //      over half w / 2 of the score dims on v_mfma_f32_16x16x32_bf16 (Q^T in
-//      VGPRs), and the four partial products are summed through LDS. fp8 and
+//      VGPRs), and each tile's two half products are summed through LDS. fp8 and
 //      MXFP4 codes are decoded exactly to bf16 with the gfx950 scaled converts
 //      (fp8: kv_scale folded into the score scale and the output). With an fp8
 //      query the scores run on fp8 x fp8 (fp8 cache) or MX-scaled fp4 x fp8
