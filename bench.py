@@ -208,7 +208,8 @@ def measure(name, args, dev, flush, q8=None, mtp=0):
         "batch": B,
         "kv_len": int(case.kv_indptr[1] - case.kv_indptr[0]),
         "plan": {"mode": "split" if plan.mode == 0 else "persistent", "splits": plan.num_splits,
-                 "grid": plan.grid, "combine_launch": bool(plan.combine)},
+                 "grid": plan.grid, "combine_launch": plan.combine == 1,
+                 "merge": ("none", "combine launch", "last-arriving split workgroup")[plan.combine]},
         "cold_us_median": med,
         "cold_us_p10": cold_us[len(cold_us) // 10],
         "cold_us_p90": cold_us[(9 * len(cold_us)) // 10],
@@ -237,8 +238,7 @@ def measure_graph(name, args, dev, flush):
     B = case.batch
     out = torch.empty((B, 16, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, 16), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(mla.mla_decode_workspace_size(B, case.total_kv, case.kv_dtype, args.flags), 16),
-                     dtype=torch.uint8, device=dev)
+    ws = mla.new_workspace(mla.mla_decode_workspace_size(B, case.total_kv, case.kv_dtype, args.flags), dev)
 
     def call():
         mla.mla_decode(q, kv, sc, indptr, indices, out, lse, total_kv=case.total_kv, kv_dtype=case.kv_dtype,
@@ -468,7 +468,7 @@ def main():
         "unit": "GB/s",
         "frac": achieved / HBM_PEAK_GBPS,
         "traffic": traffic,
-        "kernel": "mla decode call (stage-1 kernel + combine kernel when the plan has splits)",
+        "kernel": "mla decode call (stage-1 kernel, plus the combine kernel when the plan merges in a launch)",
         "bytes_per_launch": head["algorithmic_bytes"],
         "timing": "HIP events on the launch stream, cold cache, mean over steps",
     }

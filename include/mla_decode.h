@@ -69,8 +69,26 @@ extern "C" {
 #define MLA_FLAG_MIXED_LENGTHS 0x4     /* hint: sequence lengths differ widely; the heuristic then
                                           picks the persistent grid (ignored by paged and
                                           several-query-token calls, which are split-K)   */
+#define MLA_FLAG_COMBINE_LAUNCH 0x8    /* split-K: merge the split partials in a separate
+                                          combine launch instead of in the last-arriving
+                                          split workgroup of each sequence               */
 #define MLA_FLAG_SPLITS_SHIFT 8        /* bits 8..15: split count for split-K (1..255)   */
 #define MLA_FLAG_GRID_SHIFT 16         /* bits 16..27: workgroups for persistent (1..4095)*/
+
+/*
+ * Workspace layout. When a plan has split partials (workspace_bytes > 0), the
+ * first MLA_WORKSPACE_COUNTER_BYTES bytes of the workspace hold one 32-bit
+ * arrival counter per query row, used by plans with combine = 2: each split
+ * workgroup counts itself in after writing its partial, and the one that
+ * arrives last merges the row's partials and sets the counter back to zero.
+ * That region must be all zero when a call starts: zero the workspace (at
+ * least its first MLA_WORKSPACE_COUNTER_BYTES bytes) once after allocating
+ * it. Every call leaves the region all zero again, whatever its plan, so a
+ * workspace can be reused across calls and plans without clearing it. Write
+ * nothing else into that region. The partials follow it; their contents
+ * need no initialisation.
+ */
+#define MLA_WORKSPACE_COUNTER_BYTES 65536
 
 /* The launch plan the library would use (host-only, deterministic). */
 typedef struct mla_plan_info {
@@ -78,7 +96,9 @@ typedef struct mla_plan_info {
     int num_splits;         /* split-K: splits per sequence; persistent: 0              */
     int grid;               /* stage-1 workgroups                                       */
     int num_partials;       /* partial (output, lse) slots held in the workspace        */
-    int combine;            /* 1 when a stage-2 combine launch follows stage 1          */
+    int combine;            /* how the split partials are merged: 0 none (one split),
+                               1 a combine launch after stage 1, 2 inside stage 1 by
+                               the last-arriving split workgroup of each sequence  */
     int reserved;
     size_t workspace_bytes; /* bytes of workspace this plan needs (0 when none)          */
 } mla_plan_info;
@@ -100,7 +120,8 @@ int mla_decode_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_pl
 
 /*
  * mla_decode_workspace_size: bytes of device workspace `mla_decode` needs for
- * these sizes (the split partials). 0 means no workspace is needed. Pure host
+ * these sizes (arrival counters and split partials, laid out as described
+ * above mla_plan_info). 0 means no workspace is needed. Pure host
  * function. Returns 0 as well for invalid arguments (mla_decode reports them).
  */
 size_t mla_decode_workspace_size(int batch, int64_t total_kv, int kv_dtype, int flags);
@@ -123,8 +144,10 @@ size_t mla_decode_workspace_size(int batch, int64_t total_kv, int kv_dtype, int 
  *   kv_dtype   MLA_KV_*
  *   sm_scale   softmax scale; <= 0 (or NaN) selects 1/sqrt(576)
  *   workspace  device scratch of at least mla_decode_workspace_size(...) bytes,
- *              16-byte aligned (NULL allowed when that size is 0); contents
- *              need no initialisation and are clobbered
+ *              16-byte aligned (NULL allowed when that size is 0); its first
+ *              MLA_WORKSPACE_COUNTER_BYTES bytes must be zero (zeroed once
+ *              after allocation; every call leaves them zero), the rest need
+ *              no initialisation and is clobbered
  *   flags      MLA_FLAG_* (0 = heuristic)
  *   stream     hipStream_t as void*
  * An empty sequence (kv_indptr[b+1] == kv_indptr[b]) yields out = 0 and
@@ -216,7 +239,9 @@ size_t mla_decode_q8_workspace_size(int batch, int64_t total_kv, int kv_dtype, i
  *   q          device bf16 [batch, 16, 576], 16-byte aligned
  *   q_scale    device fp32 [1]: read (static) or written (dynamic)
  *   codes      device uint8 [batch, 16, 576], 8-byte aligned: the e4m3fn codes
- *   workspace  dynamic mode: at least 1 KiB, 16-byte aligned; else unused
+ *   workspace  dynamic mode: at least 1 KiB, 16-byte aligned, whose first
+ *              1 KiB is overwritten (so not a decode workspace, whose counter
+ *              region must stay zero); else unused
  * Returns MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_WORKSPACE_TOO_SMALL,
  * MLA_ERR_UNSUPPORTED or MLA_ERR_HIP.
  */

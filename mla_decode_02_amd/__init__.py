@@ -7,6 +7,7 @@ kernels. There is no fallback: if the library is missing or fails to load,
 importing this package raises.
 """
 from ._lib import (  # noqa: F401
+    FLAG_COMBINE_LAUNCH,
     FLAG_FORCE_PERSISTENT,
     FLAG_FORCE_SPLIT,
     FLAG_GRID_SHIFT,
@@ -19,6 +20,7 @@ from ._lib import (  # noqa: F401
     NUM_HEADS,
     QK_DIM,
     V_DIM,
+    WORKSPACE_COUNTER_BYTES,
     MlaError,
     Q_SCALE_DYNAMIC,
     Q_SCALE_STATIC,
@@ -35,6 +37,7 @@ from ._lib import (  # noqa: F401
     mla_dequant_debug,
     mla_quantize_q8_debug,
     mla_status_string,
+    new_workspace,
     prepare_decode,
     prepare_decode_mtp,
     prepare_decode_paged,

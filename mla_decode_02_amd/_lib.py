@@ -3,7 +3,8 @@
 Argument marshalling only: shape / dtype / device checks that the C side
 cannot make (it only sees pointers), pointer extraction, the current HIP
 stream, and -- when the caller passes none -- a workspace tensor of the size
-the library asks for. No arithmetic of the operation happens here.
+the library asks for, with its arrival-counter region zeroed as the C ABI
+requires. No arithmetic of the operation happens here.
 """
 from __future__ import annotations
 
@@ -18,7 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libmla_decode.so")
 
 NUM_HEADS, QK_DIM, V_DIM = 16, 576, 512
 KV_BF16, KV_FP8_E4M3, KV_MXFP4 = 0, 1, 2
-FLAG_FORCE_SPLIT, FLAG_FORCE_PERSISTENT, FLAG_MIXED_LENGTHS = 0x1, 0x2, 0x4
+FLAG_FORCE_SPLIT, FLAG_FORCE_PERSISTENT, FLAG_MIXED_LENGTHS, FLAG_COMBINE_LAUNCH = 0x1, 0x2, 0x4, 0x8
+WORKSPACE_COUNTER_BYTES = 65536  # leading workspace bytes that hold the arrival counters (zero between calls)
 FLAG_SPLITS_SHIFT, FLAG_GRID_SHIFT = 8, 16
 Q_SCALE_STATIC, Q_SCALE_DYNAMIC = 0, 1
 
@@ -45,8 +47,18 @@ class PlanInfo:
     num_splits: int
     grid: int
     num_partials: int
-    combine: int
+    combine: int         # 0 none, 1 combine launch, 2 merged by the last-arriving split workgroup
     workspace_bytes: int
+
+
+def new_workspace(nbytes: int, device, poison: bool = False):
+    """A decode workspace of nbytes: the arrival-counter region zeroed (the C ABI
+    requires it once; calls leave it zero). poison fills the rest with NaN, so a
+    read of a partial that no workgroup wrote would show in the output."""
+    ws = torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+    if poison and ws.numel() > WORKSPACE_COUNTER_BYTES:
+        ws[WORKSPACE_COUNTER_BYTES:].view(torch.float32).fill_(float("nan"))
+    return ws
 
 
 def _load():
@@ -184,7 +196,7 @@ def mla_decode(q, kv, kv_scales, kv_indptr, kv_indices, out, lse=None, *, total_
               "lse must be contiguous fp32 [batch, 16]")
     need = mla_decode_workspace_size(B, total_kv, kv_dtype, flags)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = new_workspace(need, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = _lib.mla_decode(_ptr(q), _ptr(kv), _ptr(kv_scales), _ptr(kv_indptr), _ptr(kv_indices), _ptr(out),
                          _ptr(lse), B, int(total_kv), int(kv_dtype), float(sm_scale), _ptr(workspace), ws_bytes,
@@ -224,7 +236,7 @@ def mla_decode_paged(q, kv, kv_scales, kv_indptr, kv_indices, kv_last_page_len, 
     plan_flags = flags | (FLAG_FORCE_SPLIT if page_size > 1 else 0)
     need = mla_decode_workspace_size(B, total_kv, kv_dtype, plan_flags)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = new_workspace(need, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = _lib.mla_decode_paged(_ptr(q), _ptr(kv), _ptr(kv_scales), _ptr(kv_indptr), _ptr(kv_indices),
                                _ptr(kv_last_page_len), int(page_size), _ptr(out), _ptr(lse), B, int(total_kv),
@@ -341,7 +353,7 @@ def mla_decode_q8(q, q_scale, kv, kv_scales, kv_indptr, kv_indices, out, lse=Non
     plan_flags = flags | (FLAG_FORCE_SPLIT if page_size > 1 else 0)
     need = mla_decode_q8_workspace_size(B, total_kv, kv_dtype, plan_flags, q_scale_mode)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = new_workspace(need, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = _lib.mla_decode_q8(_ptr(q), _ptr(q_scale), int(q_scale_mode), _ptr(kv), _ptr(kv_scales), _ptr(kv_indptr),
                             _ptr(kv_indices), _ptr(kv_last_page_len), int(page_size), _ptr(out), _ptr(lse), B,
@@ -426,7 +438,7 @@ def _mtp_args(q, qo_indptr, kv, kv_scales, kv_indptr, kv_indices, kv_last_page_l
               and tuple(lse.shape) == (total_q, NUM_HEADS), "lse must be contiguous fp32 [total_q, 16]")
     need = mla_decode_mtp_workspace_size(B, total_q, total_kv, kv_dtype, flags)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = new_workspace(need, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_ptr(q), _ptr(qo_indptr), int(total_q), int(uni_q_len), int(bool(causal)), _ptr(kv), _ptr(kv_scales),
             _ptr(kv_indptr), _ptr(kv_indices), _ptr(kv_last_page_len), int(page_size), _ptr(out), _ptr(lse), B,

@@ -106,6 +106,10 @@ struct Params {
     // length every sequence has when the lengths are equal); else 0.
     int uni_len;
     int uni_chunk;
+    // Split-K partials merged by the last-arriving split workgroup of each
+    // query row: one arrival counter per row (zero between calls); NULL when a
+    // combine launch merges them.
+    uint32_t* counters;
 };
 
 // ---------------------------------------------------------------------------
@@ -800,6 +804,98 @@ __device__ __forceinline__ void load_query(const Params& P, int b, QueryRegs<KV,
     }
 }
 
+// Buffer resource of `bytes` bytes at p for the raw buffer loads of the
+// merge (raw buffer, 32-bit data words; loads past the end return 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t merge_rsrc(const float* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), 0, bytes, 0x00020000);
+}
+// Cache-policy bits of the merge's loads: sc0 | sc1, the system-coherent
+// load, which is not served from a possibly stale line of this XCD's L2 (the
+// partials were written by workgroups on other XCDs).
+constexpr int kCoherentLoad = 0x11;
+
+// Split-K with the merge in stage 1: the partial of this workgroup (slot
+// `slot` of query row `row`) has been written with device-coherent stores.
+// Each workgroup waits for its own stores to complete, then counts itself in
+// on the row's arrival counter; the one that arrives last sets the counter
+// back to zero and merges the row's nsplit partials (the log-sum-exp merge of
+// the combine kernel):
+//     M = max_s lse_s,  w_s = exp(lse_s - M),
+//     out = sum_s w_s O_s / sum_s w_s  (bf16),  lse = M + ln sum_s w_s,
+// skipping empty partials (lse_s = -inf). No workgroup waits for another: the
+// last to arrive finds every partial complete (their stores completed before
+// their counts), so the merge needs no co-residency and no cache flush.
+// Thread (h, q) merges head h = tid / 16, columns 4 (q + 16 k) .. +3, k < 8.
+__device__ void merge_if_last(const Params& P, int row, uint8_t* smem) {
+    wait_vmcnt<0>();  // this thread's partial stores are complete
+    __syncthreads();  // ... and every thread's
+    int* flag = reinterpret_cast<int*>(smem);
+    const int tid = threadIdx.x, S = P.nsplit;
+    if (tid == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(P.counters + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = old == (uint32_t)(S - 1);
+        if (last) __hip_atomic_store(P.counters + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = last;
+    }
+    __syncthreads();
+    if (!*flag) return;
+    constexpr int kBatch = 4;  // partials whose loads are in flight together
+    constexpr int kQuads = kDv / 4 / 16;
+    const int h = tid >> 4, q = tid & 15;
+    const __amdgpu_buffer_rsrc_t ro = merge_rsrc(P.part_o + (int64_t)row * S * kHeads * kDv, S * kHeads * kDv * 4);
+    const __amdgpu_buffer_rsrc_t rl = merge_rsrc(P.part_lse + (int64_t)row * S * kHeads, S * kHeads * 4);
+    float m = -INFINITY, W = 0.f;
+    f32x4 acc[kQuads];
+#pragma unroll
+    for (int k = 0; k < kQuads; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += kBatch) {
+        float l[kBatch];
+        f32x4 o[kBatch][kQuads];
+#pragma unroll
+        for (int v = 0; v < kBatch; ++v) {
+            const int sl = s0 + v;
+            l[v] = -INFINITY;
+            if (sl < S) {
+                l[v] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * (sl * kHeads + h), 0,
+                                                                                      kCoherentLoad));
+#pragma unroll
+                for (int k = 0; k < kQuads; ++k)
+                    o[v][k] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, 4 * ((sl * kHeads + h) * kDv + 4 * (q + 16 * k)),
+                                                                     0, kCoherentLoad));
+            }
+        }
+        float mb = l[0];
+#pragma unroll
+        for (int v = 1; v < kBatch; ++v) mb = fmaxf(mb, l[v]);
+        if (mb == -INFINITY) continue;
+        const float mn = fmaxf(m, mb);
+        const float sc = __expf(m - mn);  // m = -inf: 0
+        W *= sc;
+#pragma unroll
+        for (int k = 0; k < kQuads; ++k) acc[k] *= sc;
+#pragma unroll
+        for (int v = 0; v < kBatch; ++v) {
+            if (l[v] == -INFINITY) continue;  // empty or absent: never multiplied
+            const float w = __expf(l[v] - mn);
+            W += w;
+#pragma unroll
+            for (int k = 0; k < kQuads; ++k) acc[k] += w * o[v][k];
+        }
+        m = mn;
+    }
+    const float inv = (W > 0.f) ? 1.f / W : 0.f;
+    __bf16* out = P.out + ((int64_t)row * kHeads + h) * kDv;
+#pragma unroll
+    for (int k = 0; k < kQuads; ++k) {
+        bf16x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(acc[k][e] * inv);
+        *reinterpret_cast<bf16x4*>(out + 4 * (q + 16 * k)) = pk;
+    }
+    if (q == 0 && P.lse) P.lse[(int64_t)row * kHeads + h] = (W > 0.f) ? m + logf(W) : -INFINITY;
+}
+
 // Attend tokens [t0, t1) of one sequence (positions within it; its
 // kv_indices entries start at `base`) with query row b, using the whole
 // workgroup, and write the result: the final bf16 output row b + lse when
@@ -815,7 +911,7 @@ __device__ __forceinline__ void load_query(const Params& P, int b, QueryRegs<KV,
 // QF = 1: fp8 query. Q is quantised here (static scale read, or the dynamic
 // scale reduced from the partial maxima); `scale_out` makes this workgroup
 // publish a dynamic scale.
-template <int KV, int QF>
+template <int KV, int QF, bool MG = false>
 __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, int t1, bool final, int slot,
                        bool scale_out, QueryRegs<KV, QF>& qr, bool idx_dma, bool idx_staged) {
     using L = Layout<KV>;
@@ -986,6 +1082,22 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
             for (int i = 0; i < 4; ++i) o[(4 * G + i) * kDv + col] = (__bf16)(a.o[j][i] * inv[i]);
         }
         if (wave == 0 && G == 0 && P.lse) P.lse[(int64_t)b * kHeads + r] = lse_r;
+    } else if constexpr (MG) {
+        // device-coherent stores (written through to memory), read back by
+        // whichever split workgroup of this row arrives last
+        float* o = P.part_o + (int64_t)slot * kHeads * kDv;
+#pragma unroll
+        for (int j = 0; j < kWaveBlocks; ++j) {
+            const int col = dcol<KV>(kWaveBlocks * wave + j, r);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __hip_atomic_store(o + (4 * G + i) * kDv + col, a.o[j][i] * inv[i], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (wave == 0 && G == 0)
+            __hip_atomic_store(P.part_lse + (int64_t)slot * kHeads + r, lse_r, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        merge_if_last(P, b, smem);
     } else {
         float* o = P.part_o + (int64_t)slot * kHeads * kDv;
 #pragma unroll
@@ -1045,7 +1157,10 @@ __device__ __forceinline__ Params stage1_params(const __bf16* q, const int32_t* 
     return P;
 }
 
-template <int KV, int QF>
+// MG: the plan merges the split partials here (the last-arriving split of
+// each row); a separate instantiation, so that plans merged by the combine
+// launch run a kernel without the merge code.
+template <int KV, int QF, bool MG>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Fmt<KV>::kWgsPerCU, Fmt<KV>::kWgsPerCU)))
 void split_kernel(STAGE1_ARGS) {
     const Params P = stage1_params(q_arg, indices_arg, kv_scales_arg, nsplit_arg, uni_len_arg, uni_chunk_arg, P_arg);
@@ -1089,7 +1204,7 @@ void split_kernel(STAGE1_ARGS) {
     const int t0 = min(L, s * chunk);
     const int t1 = min(L, t0 + chunk);
     const bool staged = idx_dma && base == row * Lu && L == Lu;  // then t0, t1 are t0u, t1u
-    run_wg<KV, QF>(P, smem, row, base, t0, t1, P.nsplit == 1, row * P.nsplit + s, blockIdx.x == 0, qr, idx_dma,
+    run_wg<KV, QF, MG>(P, smem, row, base, t0, t1, P.nsplit == 1, row * P.nsplit + s, blockIdx.x == 0, qr, idx_dma,
                    staged);
 }
 
@@ -1440,14 +1555,17 @@ static int launch(const mla_plan_info& plan, const Params& P, hipStream_t stream
                            const_cast<float*>(P.q_amax));
         if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
     }
-    if (plan.mode == 0)
-        hipLaunchKernelGGL((split_kernel<KV, QF>), dim3(plan.grid), dim3(kThreads), 0, stream, P.q, P.indices,
+    if (plan.mode == 0 && P.counters)
+        hipLaunchKernelGGL((split_kernel<KV, QF, true>), dim3(plan.grid), dim3(kThreads), 0, stream, P.q, P.indices,
+                           P.kv_scales, P.nsplit, P.uni_len, P.uni_chunk, plan.grid, P);
+    else if (plan.mode == 0)
+        hipLaunchKernelGGL((split_kernel<KV, QF, false>), dim3(plan.grid), dim3(kThreads), 0, stream, P.q, P.indices,
                            P.kv_scales, P.nsplit, P.uni_len, P.uni_chunk, plan.grid, P);
     else
         hipLaunchKernelGGL((persistent_kernel<KV, QF>), dim3(plan.grid), dim3(kThreads), 0, stream, P.q, P.indices,
                            P.kv_scales, P.nsplit, P.uni_len, P.uni_chunk, plan.grid, P);
     if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
-    if (plan.combine) {
+    if (plan.combine == 1) {
         CombineParams C;
         C.part_o = P.part_o;
         C.part_lse = P.part_lse;
@@ -1524,10 +1642,13 @@ static int decode_impl(const void* q, const void* kv, const void* kv_scales, con
     P.page_size = page_size;
     P.out = reinterpret_cast<__bf16*>(out);
     P.lse = lse;
-    P.part_o = reinterpret_cast<float*>(workspace);
+    // workspace: arrival counters, then the partials (O, then lse)
+    P.part_o = plan.num_partials ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + kCounterBytes)
+                                 : nullptr;
     P.part_lse = plan.num_partials ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
                                                              partial_lse_offset(plan.num_partials))
                                    : nullptr;
+    P.counters = plan.combine == 2 ? reinterpret_cast<uint32_t*>(workspace) : nullptr;
     P.batch = batch;
     P.nsplit = plan.num_splits;
     P.grid = plan.grid;

@@ -5,7 +5,9 @@
 //   split-K     (splits x batch) workgroups; split s of sequence b covers
 //               tokens [s*chunk, min(L_b, (s+1)*chunk)), chunk = ceil(L_b /
 //               splits) rounded up to the 32-token workgroup step. One partial
-//               slot per (b, s); a combine launch merges them when splits > 1.
+//               slot per (b, s); when splits > 1 the partials of a sequence
+//               are merged by its last-arriving split workgroup (up to
+//               kMaxMergeSplits splits) or by a combine launch.
 //               (Flash-decoding split-K: the split partial plus log-sum-exp
 //               merge of amd-mixed-mla submission 593653, `_flash_fp8_split_s1`
 //               and `_flash_fp8_split_s2`.)
@@ -24,18 +26,18 @@ namespace mla {
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 static size_t partial_bytes(int num_partials) {
-    // part_o [num_partials][16][512] fp32, then part_lse [num_partials][16] fp32,
-    // each section padded to 256 bytes.
+    // the arrival counters, then part_o [num_partials][16][512] fp32, then
+    // part_lse [num_partials][16] fp32, each section padded to 256 bytes.
     size_t o = (size_t)num_partials * kHeads * kDv * sizeof(float);
     size_t l = (size_t)num_partials * kHeads * sizeof(float);
-    return ((o + 255) / 256) * 256 + ((l + 255) / 256) * 256;
+    return kCounterBytes + ((o + 255) / 256) * 256 + ((l + 255) / 256) * 256;
 }
 
 size_t q8_amax_offset(size_t plan_bytes) { return (plan_bytes + 255) & ~(size_t)255; }
 
 size_t partial_lse_offset(int num_partials) {
     size_t o = (size_t)num_partials * kHeads * kDv * sizeof(float);
-    return ((o + 255) / 256) * 256;
+    return kCounterBytes + ((o + 255) / 256) * 256;
 }
 
 // Split count for split-K, the larger of two rules (each capped at kMaxSplits):
@@ -92,7 +94,7 @@ int make_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_inf
     const int forced_splits = (flags >> MLA_FLAG_SPLITS_SHIFT) & 0xFF;
     const int forced_grid = (flags >> MLA_FLAG_GRID_SHIFT) & 0xFFF;
     if (flags & ~(MLA_FLAG_FORCE_SPLIT | MLA_FLAG_FORCE_PERSISTENT | MLA_FLAG_MIXED_LENGTHS |
-                  (0xFF << MLA_FLAG_SPLITS_SHIFT) | (0xFFF << MLA_FLAG_GRID_SHIFT)))
+                  MLA_FLAG_COMBINE_LAUNCH | (0xFF << MLA_FLAG_SPLITS_SHIFT) | (0xFFF << MLA_FLAG_GRID_SHIFT)))
         return MLA_ERR_INVALID_ARG;
 
     p->reserved = 0;
@@ -125,7 +127,12 @@ int make_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_inf
         p->num_splits = s;
         p->grid = s * batch;
         p->num_partials = (s > 1) ? s * batch : 0;
-        p->combine = (s > 1) ? 1 : 0;
+        // The last-arriving split of a row merges the row's partials alone,
+        // so that merge pays only while it reads a few of them; many splits
+        // (short batches of long sequences) merge in the wide combine launch.
+        const bool merge_in_stage1 = s <= kMaxMergeSplits && batch <= kMaxCounterRows &&
+                                     (flags & MLA_FLAG_COMBINE_LAUNCH) == 0;
+        p->combine = (s > 1) ? (merge_in_stage1 ? 2 : 1) : 0;
         p->workspace_bytes = (s > 1) ? partial_bytes(p->num_partials) : 0;
     }
     return MLA_OK;

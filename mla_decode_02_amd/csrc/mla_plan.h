@@ -20,6 +20,9 @@ constexpr int kMinTokensPerWg = 4 * kStepTokens;  // enough steps for the gather
 constexpr int kMaxSplits = 64;
 constexpr int kPersistentMinTokensPerCU = 1024;
 constexpr int kQ8AmaxParts = 256;     // partial maxima of the dynamic fp8 query scale (at most)
+constexpr size_t kCounterBytes = MLA_WORKSPACE_COUNTER_BYTES;          // arrival counters ahead of the partials
+constexpr int kMaxCounterRows = (int)(kCounterBytes / sizeof(uint32_t));  // query rows with a counter
+constexpr int kMaxMergeSplits = 4;    // split-K plans merged by the last-arriving split (more: combine launch)
 
 // Stage-1 workgroups resident per compute unit (bound by the LDS ring size:
 // bf16 one, fp8 and MXFP4 two).

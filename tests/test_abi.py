@@ -64,7 +64,8 @@ def test_heuristic_plan_invariants(mla, B, L, kv_dtype):
     if p.mode == 0:
         assert 1 <= p.num_splits <= 64
         assert p.grid == p.num_splits * B
-        assert p.combine == (1 if p.num_splits > 1 else 0)
+        # the last-arriving split merges up to 4 splits; more merge in a combine launch
+        assert p.combine == (0 if p.num_splits == 1 else 2 if p.num_splits <= 4 else 1)
         assert p.num_partials == (p.num_splits * B if p.num_splits > 1 else 0)
     else:
         assert 1 <= p.grid <= 4095 and p.num_partials == p.grid + B - 1 and p.combine == 1
@@ -72,7 +73,7 @@ def test_heuristic_plan_invariants(mla, B, L, kv_dtype):
     if p.num_partials:
         o = p.num_partials * 16 * 512 * 4
         lse = p.num_partials * 16 * 4
-        expect = -(-o // 256) * 256 + -(-lse // 256) * 256
+        expect = mla.WORKSPACE_COUNTER_BYTES + -(-o // 256) * 256 + -(-lse // 256) * 256
     assert p.workspace_bytes == expect
     assert mla.mla_decode_workspace_size(B, B * L, kv_dtype) == expect
 
@@ -348,3 +349,24 @@ def test_split_ranges_cover_tokens_once(L, S):
         t1 = min(L, t0 + chunk)
         covered[t0:t1] += 1
     assert np.all(covered == 1)
+
+
+def test_plan_merge_rule(mla):
+    """Split-K plans of 2..4 splits merge in the last-arriving split workgroup
+    (combine = 2) unless MLA_FLAG_COMBINE_LAUNCH asks for the combine launch;
+    more splits, or more query rows than the counter region holds, use the launch.
+    The partials always start after the counter region."""
+    for s in range(1, 10):
+        p = mla.mla_decode_plan(8, 8 * 4096, 1, mla.flags_for(splits=s))
+        assert p.combine == (0 if s == 1 else 2 if s <= 4 else 1)
+        q = mla.mla_decode_plan(8, 8 * 4096, 1, mla.flags_for(splits=s) | mla.FLAG_COMBINE_LAUNCH)
+        assert q.combine == (0 if s == 1 else 1)
+        assert q.workspace_bytes == p.workspace_bytes
+        if s > 1:
+            assert p.workspace_bytes > mla.WORKSPACE_COUNTER_BYTES + s * 8 * 16 * 512 * 4
+    rows = mla.WORKSPACE_COUNTER_BYTES // 4
+    assert mla.mla_decode_plan(rows, rows * 64, 1, mla.flags_for(splits=2)).combine == 2
+    assert mla.mla_decode_plan(rows + 1, (rows + 1) * 64, 1, mla.flags_for(splits=2)).combine == 1
+    # several query tokens: the rows are the query tokens
+    assert mla.mla_decode_mtp_workspace_size(4, 16, 4 * 1024, 1, mla.flags_for(splits=3)) == \
+        mla.mla_decode_workspace_size(16, 16 * 1024, 1, mla.flags_for(splits=3))

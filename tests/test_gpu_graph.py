@@ -51,8 +51,7 @@ def test_captured_decode_replays(mla, dev, kv_dtype):
     B = case.batch
     out = torch.empty((B, 16, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, 16), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(mla.mla_decode_workspace_size(B, case.total_kv, kv_dtype), 16), dtype=torch.uint8,
-                     device=dev)
+    ws = mla.new_workspace(mla.mla_decode_workspace_size(B, case.total_kv, kv_dtype), dev)
     args = (t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], t["kv_indices"], out, lse)
     kw = dict(total_kv=case.total_kv, kv_dtype=kv_dtype, workspace=ws)
     g = _capture(lambda: mla.mla_decode(*args, **kw))
@@ -89,7 +88,7 @@ def test_captured_fp8_query_dynamic_scale_replays(mla, dev):
     lse = torch.empty((B, 16), dtype=torch.float32, device=dev)
     qs = torch.empty(1, dtype=torch.float32, device=dev)
     need = mla.mla_decode_q8_workspace_size(B, case.total_kv, syn.KV_MXFP4, 0, mla.Q_SCALE_DYNAMIC)
-    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws = mla.new_workspace(need, dev)
     kw = dict(q_scale_mode=mla.Q_SCALE_DYNAMIC, total_kv=case.total_kv, kv_dtype=syn.KV_MXFP4)
     g = _capture(lambda: mla.mla_decode_q8(t["q"], qs, t["kv"], t["kv_scales"], t["kv_indptr"], t["kv_indices"],
                                            out, lse, workspace=ws, **kw))

@@ -76,9 +76,7 @@ def run_mtp(mla, case, q, qo, dev, causal, uni=0, flags=0, paged=None, ws_nan=Tr
     need = mla.mla_decode_mtp_workspace_size(case.batch, TQ, case.total_kv, case.kv_dtype, flags)
     ws = None
     if need:
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
-        if ws_nan:
-            ws.view(torch.float32)[: need // 4].fill_(float("nan"))
+        ws = mla.new_workspace(need, dev, poison=ws_nan)
     mla.mla_decode_mtp(qt, qo_t, t["kv"], t["kv_scales"], indptr, indices, out, lse, total_q=TQ, causal=causal,
                        total_kv=case.total_kv, kv_dtype=case.kv_dtype, uni_q_len=uni, kv_last_page_len=last,
                        page_size=ps, workspace=ws, flags=flags)

@@ -63,15 +63,13 @@ def to_dev(case, dev):
 
 
 def new_workspace(mla, case, dev, flags=0, nan_fill=True):
-    """Workspace for one plan; by default NaN-filled so that an unwritten partial
-    surfaces as NaN (the contents need no initialisation)."""
+    """Workspace for one plan: arrival counters zeroed (the C ABI requires it) and,
+    by default, the partials NaN-filled so that an unwritten partial surfaces as NaN
+    (their contents need no initialisation)."""
     plan = mla.mla_decode_plan(case.batch, case.total_kv, case.kv_dtype, flags)
     if not plan.workspace_bytes:
         return None
-    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
-    if nan_fill:
-        ws.view(torch.float32).fill_(float("nan"))
-    return ws
+    return mla.new_workspace(plan.workspace_bytes, dev, poison=nan_fill)
 
 
 def run_gpu(mla, case, dev, flags=0, sm_scale=0.0, with_lse=True, nan_workspace=True, ws=None):
@@ -337,8 +335,7 @@ def test_workspace_reused_across_calls_and_plans(mla, orc, dev, kv_dtype):
              (big, mla.flags_for(persistent=True, grid=64)), (small, mla.flags_for(splits=64)), (big, 0),
              (big, mla.flags_for(splits=8))]
     need = max(mla.mla_decode_workspace_size(c.batch, c.total_kv, c.kv_dtype, f) for c, f in plans)
-    ws = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws.view(torch.float32)[: need // 4].fill_(float("nan"))
+    ws = mla.new_workspace(need, dev, poison=True)
     refs = {id(big): oracle_ref(orc, big), id(small): oracle_ref(orc, small)}
     for i, (c, f) in enumerate(plans):
         check(run_gpu(mla, c, dev, flags=f, ws=ws), refs[id(c)], f"call {i} flags={f:#x}")
@@ -408,8 +405,7 @@ def run_gpu_paged(mla, case, paged, dev, flags=0):
     need = mla.mla_decode_workspace_size(B, case.total_kv, case.kv_dtype, plan_flags)
     ws = None
     if need:
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
-        ws.view(torch.float32)[: need // 4].fill_(float("nan"))
+        ws = mla.new_workspace(need, dev, poison=True)
     mla.mla_decode_paged(t["q"], t["kv"], t["kv_scales"], torch.from_numpy(paged["kv_indptr"]).to(dev),
                          torch.from_numpy(paged["kv_indices"]).to(dev),
                          torch.from_numpy(paged["kv_last_page_len"]).to(dev), out, lse, page_size=ps,
@@ -453,3 +449,58 @@ def test_paged_full_size_page8_sampled(mla, orc, dev, kv_dtype, batch):
     got_o, got_l = run_gpu_paged(mla, case, paged, dev)
     sample = sorted({0, batch - 1, batch // 2})
     check((got_o[sample], got_l[sample]), oracle_ref(orc, case, batches=sample), f"paged {batch}x8192")
+
+
+# ---------------------------------------------------------------------------
+# Split partials merged by the last-arriving split workgroup (plan combine = 2)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("kv_dtype", [syn.KV_BF16, syn.KV_FP8, syn.KV_MXFP4])
+def test_merge_in_stage1_against_oracle_and_combine_launch(mla, orc, dev, kv_dtype):
+    """Every split count the merge takes (2..4) and two beyond it, on ragged,
+    shuffled sequences with an empty one and ones shorter than the splits: the
+    merged result within the oracle's bounds, the same as the combine launch's
+    up to the merge's rounding, and the arrival counters back to zero after each
+    call (the next call depends on it)."""
+    case = syn.make_case(6, [700, 1, 0, 2048, 33, 515], kv_dtype, seed=91, shuffle=True)
+    ref = oracle_ref(orc, case)
+    for splits in (2, 3, 4, 5, 8):
+        f = mla.flags_for(splits=splits)
+        plan = mla.mla_decode_plan(case.batch, case.total_kv, kv_dtype, f)
+        assert plan.combine == (2 if splits <= 4 else 1)
+        ws = new_workspace(mla, case, dev, f)
+        a = run_gpu(mla, case, dev, flags=f, ws=ws)
+        check(a, ref, f"merge in stage 1, {splits} splits")
+        counters = ws[: mla.WORKSPACE_COUNTER_BYTES]
+        assert int(torch.count_nonzero(counters)) == 0, "arrival counters not left at zero"
+        b = run_gpu(mla, case, dev, flags=f | mla.FLAG_COMBINE_LAUNCH)
+        check(b, ref, f"combine launch, {splits} splits")
+        assert np.abs(a[0] - b[0]).max() <= 2 * U_BF16 * max(np.abs(b[0]).max(), 1e-3)
+        fin = np.isfinite(b[1])
+        assert np.array_equal(np.isneginf(a[1]), np.isneginf(b[1]))
+        assert np.abs(a[1][fin] - b[1][fin]).max() <= 1e-5
+
+
+@pytest.mark.parametrize("kv_dtype", [syn.KV_FP8, syn.KV_MXFP4])
+def test_merge_in_stage1_back_to_back_calls_bitwise(mla, dev, kv_dtype):
+    """The merge reads the partials in slot order whichever split arrives last,
+    so repeated calls give bitwise-identical results. 40 calls are queued back to
+    back on one workspace (each call's counters are reset by its own last
+    arrivals before the next call starts), each writing its own output buffers;
+    a partial read before it was complete, or a counter left behind, would change
+    some bits."""
+    case = syn.make_case(48, [1024] * 40 + [300, 7, 0, 4000, 1024, 64, 1025, 2], kv_dtype, seed=92, shuffle=True)
+    t = to_dev(case, dev)
+    B = case.batch
+    f = mla.flags_for(splits=4)
+    assert mla.mla_decode_plan(B, case.total_kv, kv_dtype, f).combine == 2
+    ws = new_workspace(mla, case, dev, f)
+    outs = [torch.empty((B, 16, 512), dtype=torch.bfloat16, device=dev) for _ in range(40)]
+    lses = [torch.empty((B, 16), dtype=torch.float32, device=dev) for _ in range(40)]
+    for o, l in zip(outs, lses):
+        mla.mla_decode(t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], t["kv_indices"], o, l,
+                       total_kv=case.total_kv, kv_dtype=kv_dtype, workspace=ws, flags=f)
+    torch.cuda.synchronize()
+    for i in range(1, 40):
+        assert torch.equal(outs[i].view(torch.int16), outs[0].view(torch.int16)), f"call {i}: output bits differ"
+        assert torch.equal(lses[i].view(torch.int32), lses[0].view(torch.int32)), f"call {i}: lse bits differ"
+    assert int(torch.count_nonzero(ws[: mla.WORKSPACE_COUNTER_BYTES])) == 0

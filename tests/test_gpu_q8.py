@@ -86,8 +86,7 @@ def run_q8(mla, case, dev, mode, scale=None, flags=0, paged=None, sm_scale=0.0, 
         plan_flags = flags | (mla.FLAG_FORCE_SPLIT if ps > 1 else 0)
         need = mla.mla_decode_q8_workspace_size(B, case.total_kv, case.kv_dtype, plan_flags, mode)
         if need:
-            ws = torch.empty(need, dtype=torch.uint8, device=dev)
-            ws.view(torch.float32)[: need // 4].fill_(float("nan"))
+            ws = mla.new_workspace(need, dev, poison=True)
     mla.mla_decode_q8(t["q"], q_scale, t["kv"], t["kv_scales"], indptr, indices, out, lse, q_scale_mode=mode,
                       total_kv=case.total_kv, kv_dtype=case.kv_dtype, kv_last_page_len=last, page_size=ps,
                       sm_scale=sm_scale, workspace=ws, flags=flags)
