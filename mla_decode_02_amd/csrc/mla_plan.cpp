@@ -46,10 +46,18 @@ size_t partial_lse_offset(int num_partials) {
 //   overlaps (each split also costs a 32 KB partial written and read back);
 //   for short sequences, one workgroup per compute unit with at least one
 //   32-token step each, since latency rather than bandwidth bounds them.
+// A third rule applies when the split partials can be merged by the last-
+// arriving split (merge_ok: up to kMaxMergeSplits splits): if one workgroup
+// per compute unit fills the chip with that few splits and each split is
+// short, that plan saves the combine launch, which costs more than the second
+// workgroup per compute unit gains on short splits. Long splits keep two
+// workgroups per compute unit to stream.
 // Measured optima this reproduces (cold, MI355X): 4 x 1k: 32 splits (bf16
-// 14.8 vs 18.1 us at 8 splits); 32 x 1k fp8: 8; 64 x 1k bf16: 4; 256 x 1k
-// fp8: 2; 64 x 8k fp8: 8; 32 x 8k MXFP4: 16.
-int heuristic_splits(int batch, int64_t total_kv, int kv_dtype) {
+// 14.8 vs 18.1 us at 8 splits); 32 x 1k fp8: 8 (17.4 us, against 19.4 at 4
+// merged); 64 x 1k bf16: 4; 64 x 1k fp8: 4 merged (20.7 us, against 23.4 at
+// 8; MXFP4 equal, 23.1 both); 256 x 1k fp8: 2 (39.7 us merged, against 41.9
+// at 1); 64 x 8k fp8: 8 (66.1 us, against 79.7 at 4 merged); 32 x 8k MXFP4: 16.
+int heuristic_splits(int batch, int64_t total_kv, int kv_dtype, bool merge_ok) {
     if (batch <= 0) return 1;
     const int64_t avg = cdiv(total_kv, batch);
     auto rule = [&](int64_t wgs, int64_t min_tokens) {
@@ -60,7 +68,11 @@ int heuristic_splits(int batch, int64_t total_kv, int kv_dtype) {
     };
     const int64_t fill = rule((int64_t)kNumCUs * wgs_per_cu(kv_dtype), kMinTokensPerWg);
     const int64_t per_cu = rule(kNumCUs, kStepTokens);
-    return (int)(fill > per_cu ? fill : per_cu);
+    const int64_t s = fill > per_cu ? fill : per_cu;
+    if (merge_ok && batch <= kMaxCounterRows && s > kMaxMergeSplits && per_cu > 1 && per_cu <= kMaxMergeSplits &&
+        (int64_t)batch * per_cu >= kNumCUs && cdiv(avg, per_cu) <= kShortSplitTokens)
+        return (int)per_cu;
+    return (int)s;
 }
 
 // Persistent grid: one workgroup per compute unit, fewer when there are not
@@ -77,9 +89,9 @@ int heuristic_grid(int64_t total_kv, int kv_dtype) {
 // split grid lands on a whole number of workgroups per compute unit; the
 // persistent grid for large, uneven shapes where the split grid would leave
 // compute units idle.
-static bool prefer_persistent(int batch, int64_t total_kv, int kv_dtype) {
+static bool prefer_persistent(int batch, int64_t total_kv, int kv_dtype, bool merge_ok) {
     if (total_kv < (int64_t)kNumCUs * kPersistentMinTokensPerCU) return false;
-    int s = heuristic_splits(batch, total_kv, kv_dtype);
+    int s = heuristic_splits(batch, total_kv, kv_dtype, merge_ok);
     int64_t wgs = (int64_t)s * batch;
     return (wgs % kNumCUs) != 0;
 }
@@ -111,8 +123,9 @@ int make_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_inf
     // grid: its equal token shares balance mixed lengths, where split-K's
     // per-sequence splits leave the longest sequences on the critical path.
     const bool mixed = (flags & MLA_FLAG_MIXED_LENGTHS) != 0 && total_kv >= kNumCUs;
+    const bool merge_ok = (flags & MLA_FLAG_COMBINE_LAUNCH) == 0;
     bool persistent = force_pers || (!force_split && forced_splits == 0 &&
-                                     (mixed || prefer_persistent(batch, total_kv, kv_dtype)));
+                                     (mixed || prefer_persistent(batch, total_kv, kv_dtype, merge_ok)));
     if (persistent) {
         int g = forced_grid ? forced_grid : heuristic_grid(total_kv, kv_dtype);
         p->mode = 1;
@@ -122,7 +135,7 @@ int make_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_inf
         p->combine = 1;
         p->workspace_bytes = partial_bytes(p->num_partials);
     } else {
-        int s = forced_splits ? forced_splits : heuristic_splits(batch, total_kv, kv_dtype);
+        int s = forced_splits ? forced_splits : heuristic_splits(batch, total_kv, kv_dtype, merge_ok);
         p->mode = 0;
         p->num_splits = s;
         p->grid = s * batch;
@@ -130,8 +143,7 @@ int make_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_inf
         // The last-arriving split of a row merges the row's partials alone,
         // so that merge pays only while it reads a few of them; many splits
         // (short batches of long sequences) merge in the wide combine launch.
-        const bool merge_in_stage1 = s <= kMaxMergeSplits && batch <= kMaxCounterRows &&
-                                     (flags & MLA_FLAG_COMBINE_LAUNCH) == 0;
+        const bool merge_in_stage1 = s <= kMaxMergeSplits && batch <= kMaxCounterRows && merge_ok;
         p->combine = (s > 1) ? (merge_in_stage1 ? 2 : 1) : 0;
         p->workspace_bytes = (s > 1) ? partial_bytes(p->num_partials) : 0;
     }

@@ -23,13 +23,14 @@ constexpr int kQ8AmaxParts = 256;     // partial maxima of the dynamic fp8 query
 constexpr size_t kCounterBytes = MLA_WORKSPACE_COUNTER_BYTES;          // arrival counters ahead of the partials
 constexpr int kMaxCounterRows = (int)(kCounterBytes / sizeof(uint32_t));  // query rows with a counter
 constexpr int kMaxMergeSplits = 4;    // split-K plans merged by the last-arriving split (more: combine launch)
+constexpr int64_t kShortSplitTokens = 256;  // longest split the one-workgroup-per-CU merged plan is chosen for
 
 // Stage-1 workgroups resident per compute unit (bound by the LDS ring size:
 // bf16 one, fp8 and MXFP4 two).
 constexpr int wgs_per_cu(int kv_dtype) { return kv_dtype == MLA_KV_BF16 ? 1 : 2; }
 
 int make_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_info* p);
-int heuristic_splits(int batch, int64_t total_kv, int kv_dtype);
+int heuristic_splits(int batch, int64_t total_kv, int kv_dtype, bool merge_ok);
 int heuristic_grid(int64_t total_kv, int kv_dtype);
 size_t partial_lse_offset(int num_partials);
 // Plan for total_q query rows over `batch` sequences holding total_kv cache
