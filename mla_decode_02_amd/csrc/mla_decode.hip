@@ -537,15 +537,124 @@ __device__ __forceinline__ f32x4 qk_partial_mx(const uint8_t* step, const i32x8 
     return acc;
 }
 
+// bf16 query on the MXFP4 cache: the scores also run on the MX-scaled MFMA,
+// straight from the staged e2m1 codes, with the query split into two e4m3fn
+// code sets that carry their own e8m0 scale per 32-element block:
+//     hi = RNE(q / 2^eh),  lo = RNE((q - hi 2^eh) / 2^el),
+// eh = floor(log2 max|q|) - 7 over the block and el likewise over the
+// residuals (so every scaled value lies below 256, inside the e4m3fn range;
+// the residual q - hi 2^eh is exact in fp32). hi 2^eh + lo 2^el equals q
+// exactly for the elements within about 2^-10 of their block's largest
+// magnitude (four significant bits each, eight together) and differs from
+// q by less than 2^-20 of it for the rest, far below the rounding of the
+// softmax weights to bf16. No cache code is converted for the scores.
+// e8m0 code c of the scale 2^(floor(log2 a) - 7) for a >= 0 (1 for a < 2^-119).
+__device__ __forceinline__ int split_scale_code(float a) {
+    return max(1, (int)((__float_as_uint(a) >> 23) & 0xffu) - 7);
+}
+__device__ __forceinline__ float pow2_code(int c) { return __uint_as_float((uint32_t)c << 23); }  // 2^(c - 127)
+
+// The query row's two code sets: thread tid splits the 8-element groups tid,
+// tid + 256, ... (< kQGroups) held in g; four consecutive groups (threads 4m
+// .. 4m + 3) form one 32-element block. hi_dst / lo_dst receive the codes as
+// [16][576] bytes followed by the e8m0 codes [16][18].
+template <int PER>
+__device__ __forceinline__ void q_split_quantise(const bf16x8 (&g)[PER], int tid, uint8_t* hi_dst, uint8_t* lo_dst) {
+    constexpr int kGroups = kHeads * kDqk / 8;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int grp = tid + k * kThreads;
+        if (k * kThreads + (tid & ~63) >= kGroups) continue;  // whole waves: the block's four lanes stay together
+        float x[8], amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            x[e] = (float)g[k][e];
+            amax = fmaxf(amax, fabsf(x[e]));
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        const int ch = split_scale_code(amax);
+        const float dh = pow2_code(254 - ch), uh = pow2_code(ch);  // 2^-eh, 2^eh
+        u32x2 hc;
+        hc[0] = q8_pack2<true>(x[2] * dh, x[3] * dh, q8_pack2<false>(x[0] * dh, x[1] * dh, 0u));
+        hc[1] = q8_pack2<true>(x[6] * dh, x[7] * dh, q8_pack2<false>(x[4] * dh, x[5] * dh, 0u));
+        float hv[8];
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            hv[4 * w + 0] = __builtin_amdgcn_cvt_f32_fp8((int)hc[w], 0);
+            hv[4 * w + 1] = __builtin_amdgcn_cvt_f32_fp8((int)hc[w], 1);
+            hv[4 * w + 2] = __builtin_amdgcn_cvt_f32_fp8((int)hc[w], 2);
+            hv[4 * w + 3] = __builtin_amdgcn_cvt_f32_fp8((int)hc[w], 3);
+        }
+        float rr[8], ramax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            rr[e] = x[e] - hv[e] * uh;  // exact: hi holds the leading bits of x
+            ramax = fmaxf(ramax, fabsf(rr[e]));
+        }
+        ramax = fmaxf(ramax, __shfl_xor(ramax, 1));
+        ramax = fmaxf(ramax, __shfl_xor(ramax, 2));
+        const int cl = split_scale_code(ramax);
+        const float dl = pow2_code(254 - cl);
+        u32x2 lc;
+        lc[0] = q8_pack2<true>(rr[2] * dl, rr[3] * dl, q8_pack2<false>(rr[0] * dl, rr[1] * dl, 0u));
+        lc[1] = q8_pack2<true>(rr[6] * dl, rr[7] * dl, q8_pack2<false>(rr[4] * dl, rr[5] * dl, 0u));
+        if (grp < kGroups) {
+            *reinterpret_cast<u32x2*>(hi_dst + 8 * grp) = hc;
+            *reinterpret_cast<u32x2*>(lo_dst + 8 * grp) = lc;
+            if ((tid & 3) == 0) {
+                hi_dst[kHeads * kDqk + (grp >> 2)] = (uint8_t)ch;
+                lo_dst[kHeads * kDqk + (grp >> 2)] = (uint8_t)cl;
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ f32x4 mfma_mx2(i32x8 a, i32x8 b, int scale_a, int scale_b, f32x4 c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, scale_a, 0, scale_b);
+}
+
+// Partial scores of one wave with the split query: qm[j] / qm[3 + j] are the
+// hi / lo B operands of this wave's block j, qs[j] / qs[3 + j] their e8m0
+// codes for (head r, k block G). The two pieces accumulate in separate chains.
+template <int HF>
+__device__ __forceinline__ f32x4 qk_partial_mx2(const uint8_t* step, const i32x8 (&qm)[6], const int (&qs)[6], int t,
+                                                int lane) {
+    const uint8_t* tile = step + t * Fmt<MLA_KV_MXFP4>::kTileBytes;
+    const int G = lane >> 4, r = lane & 15;
+    f32x4 ah = {0.f, 0.f, 0.f, 0.f}, al = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < (HF ? 2 : 3); ++j) {
+        const int u = HF ? 3 + j : j;
+        i32x8 a = {0, 0, 0, 0, 0, 0, 0, 0};
+        int sc = 127;
+        if (u < 4) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(tile + 1024 * u + 16 * lane);
+            a[0] = (int)w[0]; a[1] = (int)w[1]; a[2] = (int)w[2]; a[3] = (int)w[3];
+            sc = mx_scale_code(tile, 4 * u + G, r);
+        } else if (G < 2) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(tile + Fmt<MLA_KV_MXFP4>::kRopeOff + 16 * lane);
+            a[0] = (int)w[0]; a[1] = (int)w[1]; a[2] = (int)w[2]; a[3] = (int)w[3];
+            sc = mx_scale_code(tile, 16 + G, r);
+        }
+        ah = mfma_mx2(a, qm[j], sc, qs[j], ah);
+        al = mfma_mx2(a, qm[3 + j], sc, qs[3 + j], al);
+    }
+    return ah + al;
+}
+
 // Query operand type: bf16 (also the decoded fp8 query codes, which bf16
 // holds exactly), raw e4m3fn codes when both operands are fp8, or the
-// MX-scaled MFMA's e4m3fn operand on the MXFP4 cache.
+// MX-scaled MFMA's e4m3fn operand on the MXFP4 cache (the fp8 query's codes,
+// or the two code sets a bf16 query is split into).
 template <int KV, int QF>
 struct QOperand { using T = bf16x8; };
 template <>
 struct QOperand<MLA_KV_FP8_E4M3, 1> { using T = long; };
 template <>
 struct QOperand<MLA_KV_MXFP4, 1> { using T = i32x8; };
+template <>
+struct QOperand<MLA_KV_MXFP4, 0> { using T = i32x8; };
 
 struct WaveAcc {
     f32x4 o[kWaveBlocks];  // o[j][i]: head 4G+i, column dcol(kWaveBlocks * wave + j, r)
@@ -769,13 +878,18 @@ __device__ __forceinline__ void dma_idx(const Params& P, int first, int n, int32
 }
 
 // One query row in registers, with the scales read alongside it.
-//   bf16 query: this wave's half of Q^T, straight in the score operand layout.
-//   fp8 query: thread tid holds the 8-element groups tid, tid + 256, ... of
-//   the row's 16 x 576 query, quantised once per workgroup later on.
+//   bf16 query (bf16 and fp8 caches): this wave's half of Q^T, straight in
+//   the score operand layout.
+//   fp8 query, and bf16 query on the MXFP4 cache: thread tid holds the
+//   8-element groups tid, tid + 256, ... of the row's 16 x 576 query,
+//   quantised (fp8 query) or split into two code sets (bf16 query on MXFP4)
+//   once per workgroup later on.
 template <int KV, int QF>
 struct QueryRegs {
-    typename QOperand<KV, QF>::T qB[QF && KV == MLA_KV_MXFP4 ? 3 : kHalfK];
-    bf16x8 qg[QF ? kQPer : 1];
+    static constexpr bool kSplit = KV == MLA_KV_MXFP4 && !QF;  // split query on the MX-scaled MFMA
+    typename QOperand<KV, QF>::T qB[KV == MLA_KV_MXFP4 ? (QF ? 3 : 6) : kHalfK];
+    bf16x8 qg[(QF || kSplit) ? kQPer : 1];
+    int qsc[kSplit ? 6 : 1];  // split query: e8m0 codes of qB (head r, k block G)
     float kv_scale, q_scale, q_part;
 };
 
@@ -788,14 +902,16 @@ __device__ __forceinline__ void load_query(const Params& P, int b, QueryRegs<KV,
     if constexpr (KV == MLA_KV_FP8_E4M3) q.kv_scale = *reinterpret_cast<const float*>(P.kv_scales);
     q.q_scale = 1.0f;
     q.q_part = 0.0f;
-    if constexpr (QF) {
+    if constexpr (QF || QueryRegs<KV, QF>::kSplit) {
 #pragma unroll
         for (int k = 0; k < kQPer; ++k) {
             q.qg[k] = bf16x8{};
             if (tid + k * kThreads < kQGroups) q.qg[k] = *reinterpret_cast<const bf16x8*>(qseq + 8 * (tid + k * kThreads));
         }
-        if (P.q_amax) q.q_part = tid < P.q_amax_n ? P.q_amax[tid] : 0.0f;
-        else q.q_scale = *P.q_scale;
+        if constexpr (QF) {
+            if (P.q_amax) q.q_part = tid < P.q_amax_n ? P.q_amax[tid] : 0.0f;
+            else q.q_scale = *P.q_scale;
+        }
     } else {
         const __bf16* qrow = qseq + r * kDqk;
 #pragma unroll
@@ -933,16 +1049,18 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
     int32_t iv[kPer];
     if (!idx_staged) load_idx<KV>(P, base, t0, min(kIdxWindow, t1 - t0), iv);
     using QOp = typename QOperand<KV, QF>::T;
-    constexpr bool kMx = QF && KV == MLA_KV_MXFP4;  // scores on the MX-scaled MFMA
+    constexpr bool kMx = QF && KV == MLA_KV_MXFP4;           // fp8 query: scores on the MX-scaled MFMA
+    constexpr bool kSplit = QueryRegs<KV, QF>::kSplit;      // bf16 query, MXFP4 cache: split query, same MFMA
     auto& qB = qr.qB;
     auto& qg = qr.qg;
+    auto& qsc = qr.qsc;
     const float kv_scale = qr.kv_scale, q_part = qr.q_part;
     float q_scale = qr.q_scale;
     const __bf16* qseq = P.q + (int64_t)b * kHeads * kDqk;
     // Consume Q and the scales here: the compiler's wait for these loads must
     // not land inside the token loop, where the count it waits for would also
     // drain the gathers in flight (it does not see the LDS-DMA loads).
-    if constexpr (QF) {
+    if constexpr (QF || kSplit) {
 #pragma unroll
         for (int k = 0; k < kQPer; ++k) asm volatile("" ::"v"(qg[k]));
     } else {
@@ -991,6 +1109,8 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
             if constexpr (KV == MLA_KV_MXFP4) convert_scales(st, fs_buf + (i & 1) * (L::kFsBytes / 4), tid);
             if constexpr (kMx) {
                 return hf ? qk_partial_mx<1>(st, qB, tile, lane) : qk_partial_mx<0>(st, qB, tile, lane);
+            } else if constexpr (kSplit) {
+                return hf ? qk_partial_mx2<1>(st, qB, qsc, tile, lane) : qk_partial_mx2<0>(st, qB, qsc, tile, lane);
             } else {
                 return hf ? qk_partial<KV, 1>(st, qB, tile, lane) : qk_partial<KV, 0>(st, qB, tile, lane);
             }
@@ -1003,8 +1123,18 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
         // flight. The codes ([head][576] bytes) pass through ring slot D, whose
         // step is issued only after the next two barriers.
         uint8_t* qcodes = smem + (D % R) * L::kStepBytes;
+        // split query: hi codes in ring slot D, lo codes in the score exchange
+        // and value-scale buffers (free until scores(0) and put_scores(0) write
+        // them, which every wave does only after a barrier that follows all
+        // waves' operand reads below)
+        uint8_t* qcodes_lo = smem + L::kSbufOff;
         if constexpr (QF) {
             if (w0 == t0) q8_quantise<kQPer>(qg, qseq, tid, kThreads, kQGroups, q_scale, qcodes);
+        } else if constexpr (kSplit) {
+            static_assert(L::kIdxOff - L::kSbufOff >= kHeads * kDqk + kHeads * (kDqk / 32),
+                          "the exchange and value-scale buffers hold one split-query code set");
+            static_assert(L::kStepBytes >= kHeads * kDqk + kHeads * (kDqk / 32), "a ring slot holds one code set");
+            if (w0 == t0) q_split_quantise<kQPer>(qg, tid, qcodes, qcodes_lo);
         }
         wait_own<KV>(min(D - 1, nsteps - 1), hf);
         __syncthreads();  // step 0 has landed (and the query codes are written)
@@ -1026,6 +1156,35 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
                     qB[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
                 }
+            }
+        } else if constexpr (kSplit) {
+            if (w0 == t0) {
+                // as for the fp8 query, once per code set; the e8m0 code of lane (G, r) is that of head r's
+                // 32-element block G of the 128-dim block (RoPE: blocks 16, 17, then zero padding)
+#pragma unroll
+                for (int pc = 0; pc < 2; ++pc) {
+                    const uint8_t* cs = pc ? qcodes_lo : qcodes;
+                    const uint8_t* crow = cs + r * kDqk;
+                    const uint8_t* srow = cs + kHeads * kDqk + r * (kDqk / 32);
+#pragma unroll
+                    for (int j = 0; j < 3; ++j) {
+                        const int u = hf ? 3 + j : j;
+                        u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+                        int code = 127;
+                        if (u < 4) {
+                            lo = *reinterpret_cast<const u32x4*>(crow + 128 * u + 16 * G);
+                            hi = *reinterpret_cast<const u32x4*>(crow + 128 * u + 64 + 16 * G);
+                            code = srow[4 * u + G];
+                        } else if (u == 4) {
+                            lo = *reinterpret_cast<const u32x4*>(crow + 512 + 16 * G);
+                            if (G < 2) code = srow[16 + G];
+                        }
+                        qB[3 * pc + j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                        qsc[3 * pc + j] = code;
+                    }
+                }
+                __syncthreads();  // every wave has read the lo codes before any wave writes the buffers
             }
         } else if constexpr (QF) {
             if (w0 == t0) {
