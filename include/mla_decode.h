@@ -297,7 +297,9 @@ size_t mla_decode_mtp_workspace_size(int batch, int total_q, int64_t total_kv, i
  * product (code value) * kv_scale[0]; for MXFP4 it is the e2m1 value times
  * 2^(e8m0 - 127); for bf16 the value itself.
  *   kv, kv_scales  as for mla_decode (row r of the output is physical row r)
- *   path           0: all columns through the score-operand decode;
+ *   path           0: all columns through the score-operand decode (the
+ *                     bf16 cache and fp8 scores use it; MXFP4 scores take the
+ *                     codes into the MX-scaled MFMA undecoded);
  *                  1: columns 0..511 through the value-operand decode (LDS
  *                     transpose reads), columns 512..575 as path 0
  *   out_f32        device fp32 [rows, 576]

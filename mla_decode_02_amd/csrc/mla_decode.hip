@@ -18,11 +18,13 @@
 //      64u + 16G of row r for load u: the MFMA operand layout of the scores.
 //   2. Scores S^T[16 tokens x 16 heads] = K . Q^T: wave w computes tile w % 2
 //      over half w / 2 of the score dims on v_mfma_f32_16x16x32_bf16 (Q^T in
-//      VGPRs), and each tile's two half products are summed through LDS. fp8 and
-//      MXFP4 codes are decoded exactly to bf16 with the gfx950 scaled converts
-//      (fp8: kv_scale folded into the score scale and the output). With an fp8
-//      query the scores run on fp8 x fp8 (fp8 cache) or MX-scaled fp4 x fp8
-//      (MXFP4 cache) MFMAs on the raw codes.
+//      VGPRs), and each tile's two half products are summed through LDS. fp8
+//      codes are decoded exactly to bf16 with the gfx950 scaled converts
+//      (kv_scale folded into the score scale and the output). On the MXFP4
+//      cache the scores run on the MX-scaled fp4 x fp8 MFMA on the raw codes,
+//      with the bf16 query split into two e4m3fn code sets (see
+//      q_split_quantise). With an fp8 query the scores run on fp8 x fp8 (fp8
+//      cache) or MX-scaled fp4 x fp8 (MXFP4 cache) MFMAs on the raw codes.
 //   3. Online softmax in the log2 domain with lazy rescaling (the running max
 //      only moves when a score exceeds it by 2^8). Every wave runs it on the
 //      full step and holds the same max and sum. The S^T accumulator is

@@ -504,3 +504,27 @@ def test_merge_in_stage1_back_to_back_calls_bitwise(mla, dev, kv_dtype):
         assert torch.equal(outs[i].view(torch.int16), outs[0].view(torch.int16)), f"call {i}: output bits differ"
         assert torch.equal(lses[i].view(torch.int32), lses[0].view(torch.int32)), f"call {i}: lse bits differ"
     assert int(torch.count_nonzero(ws[: mla.WORKSPACE_COUNTER_BYTES])) == 0
+
+
+def test_mxfp4_split_query_wide_range(mla, orc, dev):
+    """On the MXFP4 cache the bf16 query enters the scores as two e4m3fn code sets
+    with per-32-element e8m0 scales. Its weak spot is a block whose elements span
+    a wide range (the small ones keep fewer bits), so the query here has
+    magnitudes 2^-24 .. 2^3 inside every block, all-zero blocks, blocks with one
+    nonzero element and a block at the top of the range: the result stays within
+    the same bounds as the oracle's exact bf16 query (the acceptance band, the
+    rounding gate and lse within 1e-3)."""
+    case = syn.make_case(3, [500, 64, 1000], syn.KV_MXFP4, seed=93, shuffle=True)
+    rng = np.random.default_rng(94)
+    q = rng.standard_normal(case.q.shape).astype(np.float32)
+    q *= np.exp2(rng.integers(-24, 4, size=case.q.shape)).astype(np.float32)
+    q[0, 0, :32] = 0.0                      # an all-zero block
+    q[1, 3, 64:96] = 0.0
+    q[1, 3, 70] = 2.5                       # one nonzero element in a block
+    q[2, 15, 544:576] = 0.0                 # the last RoPE block: one tiny element
+    q[2, 15, 575] = 2.0 ** -20
+    q[2, 7, 0:32] = rng.standard_normal(32).astype(np.float32) * 60.0  # large block, scores of order 10
+    case.q = syn.f32_to_bf16_bits(q)
+    ref = oracle_ref(orc, case)
+    check(run_gpu(mla, case, dev), ref, "MXFP4, wide-range query")
+    check(run_gpu(mla, case, dev, flags=mla.flags_for(persistent=True, grid=7)), ref, "MXFP4, wide-range query, persistent")
