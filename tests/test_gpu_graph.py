@@ -44,16 +44,22 @@ def _capture(fn):
     return g
 
 
+@pytest.mark.parametrize("merge_in_stage1", [False, True])
 @pytest.mark.parametrize("kv_dtype", DTYPES)
-def test_captured_decode_replays(mla, dev, kv_dtype):
+def test_captured_decode_replays(mla, dev, kv_dtype, merge_in_stage1):
+    """A captured call replays bit-identically to eager calls, with the combine
+    launch (default plan here) and with the partials merged by the last-arriving
+    split (3 splits; its arrival counters are reset inside the kernel)."""
     case = syn.make_case(6, [1000, 3, 700, 0, 2000, 64], kv_dtype, seed=620 + kv_dtype, shuffle=True)
     t = to_dev(case, dev)
     B = case.batch
+    flags = mla.flags_for(splits=3) if merge_in_stage1 else 0
+    assert mla.mla_decode_plan(B, case.total_kv, kv_dtype, flags).combine == (2 if merge_in_stage1 else 1)
     out = torch.empty((B, 16, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, 16), dtype=torch.float32, device=dev)
-    ws = mla.new_workspace(mla.mla_decode_workspace_size(B, case.total_kv, kv_dtype), dev)
+    ws = mla.new_workspace(mla.mla_decode_workspace_size(B, case.total_kv, kv_dtype, flags), dev)
     args = (t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], t["kv_indices"], out, lse)
-    kw = dict(total_kv=case.total_kv, kv_dtype=kv_dtype, workspace=ws)
+    kw = dict(total_kv=case.total_kv, kv_dtype=kv_dtype, workspace=ws, flags=flags)
     g = _capture(lambda: mla.mla_decode(*args, **kw))
     rng = np.random.default_rng(621)
     other = syn.make_case(2, [300, 40], kv_dtype, seed=622)
@@ -61,7 +67,7 @@ def test_captured_decode_replays(mla, dev, kv_dtype):
         # eager reference on the current inputs, into separate outputs
         ro = torch.empty_like(out)
         rl = torch.empty_like(lse)
-        mla.mla_decode(args[0], *args[1:5], ro, rl, total_kv=case.total_kv, kv_dtype=kv_dtype)
+        mla.mla_decode(args[0], *args[1:5], ro, rl, total_kv=case.total_kv, kv_dtype=kv_dtype, flags=flags)
         torch.cuda.synchronize()
         out.fill_(float("nan"))
         lse.fill_(float("nan"))
