@@ -162,6 +162,30 @@ int mla_decode(const void* q, const void* kv, const void* kv_scales, const int32
                void* stream);
 
 /*
+ * mla_decode_rows: mla_decode with the number of rows the cache buffer holds
+ * (for callers that can allocate their cache contiguously per sequence, as
+ * the pages' benchmark does with kv_indices = arange; submission 593653,
+ * `custom_kernel`).
+ *   kv_rows  rows in kv (and in kv_scales for MXFP4); every kv_indices value
+ *            must be below it. 0 = unknown, which is exactly mla_decode.
+ *   all other arguments, the outputs, the errors and the results as for
+ *   mla_decode; MLA_ERR_INVALID_ARG also for kv_rows < 0.
+ * With kv_rows known and every sequence of the same length L (total_kv a
+ * multiple of batch), each stage-1 workgroup requests the first rows of its
+ * token range as a contiguous cache would place them (sequence b at rows
+ * b * L .. b * L + L - 1, clamped below kv_rows) together with its query and
+ * kv_indices reads, before kv_indices has arrived. It keeps them only when
+ * kv_indices names exactly those rows and gathers again otherwise, so the
+ * result does not depend on the cache layout; a contiguous cache saves one
+ * dependent memory round trip at start-up. The bf16 and fp8 caches do this;
+ * on the MXFP4 cache mla_decode_rows is mla_decode (its query split overlaps
+ * the first row requests instead).
+ */
+int mla_decode_rows(const void* q, const void* kv, const void* kv_scales, const int32_t* kv_indptr,
+                    const int32_t* kv_indices, void* out, float* lse, int batch, int64_t total_kv, int64_t kv_rows,
+                    int kv_dtype, float sm_scale, void* workspace, size_t workspace_bytes, int flags, void* stream);
+
+/*
  * mla_decode_paged: mla_decode over a paged cache (page_size rows per page),
  * the layout the pages' a16w8 path uses with 8-row pages for kv >= 8192
  * (submission 616673, `_run_a16w8`: the fp8 cache viewed as

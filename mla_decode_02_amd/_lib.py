@@ -24,7 +24,7 @@ WORKSPACE_COUNTER_BYTES = 65536  # leading workspace bytes that hold the arrival
 FLAG_SPLITS_SHIFT, FLAG_GRID_SHIFT = 8, 16
 Q_SCALE_STATIC, Q_SCALE_DYNAMIC = 0, 1
 
-_EXPORTS = ("mla_decode", "mla_decode_paged", "mla_decode_q8", "mla_decode_mtp", "mla_decode_plan",
+_EXPORTS = ("mla_decode", "mla_decode_rows", "mla_decode_paged", "mla_decode_q8", "mla_decode_mtp", "mla_decode_plan",
             "mla_decode_workspace_size", "mla_decode_q8_workspace_size", "mla_decode_mtp_workspace_size",
             "mla_quantize_q8_debug", "mla_dequant_debug", "mla_status_string")
 
@@ -73,6 +73,8 @@ def _load():
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
     lib.mla_decode.restype = i32
     lib.mla_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, ctypes.c_float, vp, sz, i32, vp]
+    lib.mla_decode_rows.restype = i32
+    lib.mla_decode_rows.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i64, i32, ctypes.c_float, vp, sz, i32, vp]
     lib.mla_decode_paged.restype = i32
     lib.mla_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i64, i32, ctypes.c_float, vp, sz, i32,
                                      vp]
@@ -174,12 +176,14 @@ def _check_kv(kv, kv_scales, kv_dtype):
 
 
 def mla_decode(q, kv, kv_scales, kv_indptr, kv_indices, out, lse=None, *, total_kv: int, kv_dtype: int,
-               sm_scale: float = 0.0, workspace=None, flags: int = 0):
+               sm_scale: float = 0.0, workspace=None, flags: int = 0, kv_rows: int | None = None):
     """Enqueue MLA decode on the current stream of q's device (see include/mla_decode.h).
 
     q [B,16,576] bf16, kv / kv_scales per kv_dtype, kv_indptr [B+1] int32,
     kv_indices [total_kv] int32, out [B,16,512] bf16, lse [B,16] fp32 or None.
-    total_kv is the host copy of kv_indptr[B]. Returns the workspace used.
+    total_kv is the host copy of kv_indptr[B]. kv_rows is the cache's row
+    count for mla_decode_rows (None: kv's own, 0: unknown, i.e. mla_decode).
+    Returns the workspace used.
     """
     B = int(kv_indptr.shape[0]) - 1
     _need(q.is_cuda and q.dtype == torch.bfloat16 and q.is_contiguous() and tuple(q.shape) == (B, NUM_HEADS, QK_DIM),
@@ -198,12 +202,19 @@ def mla_decode(q, kv, kv_scales, kv_indptr, kv_indices, out, lse=None, *, total_
     if workspace is None and need > 0:
         workspace = new_workspace(need, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = _lib.mla_decode(_ptr(q), _ptr(kv), _ptr(kv_scales), _ptr(kv_indptr), _ptr(kv_indices), _ptr(out),
-                         _ptr(lse), B, int(total_kv), int(kv_dtype), float(sm_scale), _ptr(workspace), ws_bytes,
-                         int(flags), _stream(q.device))
+    rows = _kv_rows(kv, kv_rows)
+    rc = _lib.mla_decode_rows(_ptr(q), _ptr(kv), _ptr(kv_scales), _ptr(kv_indptr), _ptr(kv_indices), _ptr(out),
+                              _ptr(lse), B, int(total_kv), rows, int(kv_dtype), float(sm_scale), _ptr(workspace),
+                              ws_bytes, int(flags), _stream(q.device))
     if rc != 0:
         raise MlaError(rc, "mla_decode")
     return workspace
+
+
+def _kv_rows(kv, kv_rows):
+    """The cache row count passed to mla_decode_rows: kv's leading dimension
+    unless the caller gives one (0 turns the early row requests off)."""
+    return int(kv.shape[0]) if kv_rows is None else int(kv_rows)
 
 
 def mla_decode_paged(q, kv, kv_scales, kv_indptr, kv_indices, kv_last_page_len, out, lse=None, *, page_size: int,
@@ -248,18 +259,20 @@ def mla_decode_paged(q, kv, kv_scales, kv_indptr, kv_indices, kv_last_page_len, 
 
 
 def prepare_decode(q, kv, kv_scales, kv_indptr, kv_indices, out, lse=None, *, total_kv: int, kv_dtype: int,
-                   sm_scale: float = 0.0, workspace=None, flags: int = 0):
+                   sm_scale: float = 0.0, workspace=None, flags: int = 0, kv_rows: int | None = None):
     """Check and marshal the arguments once; return a zero-argument callable that
-    enqueues the same mla_decode call on the current stream (for serving loops and
-    timing, where per-call Python checks would dominate). The tensors must stay
-    alive and in place while the callable is used."""
+    enqueues the same mla_decode call (through mla_decode_rows, kv_rows as for
+    mla_decode) on the current stream (for serving loops and timing, where
+    per-call Python checks would dominate). The tensors must stay alive and in
+    place while the callable is used."""
     ws = mla_decode(q, kv, kv_scales, kv_indptr, kv_indices, out, lse, total_kv=total_kv, kv_dtype=kv_dtype,
-                    sm_scale=sm_scale, workspace=workspace, flags=flags)
+                    sm_scale=sm_scale, workspace=workspace, flags=flags, kv_rows=kv_rows)
     B = int(kv_indptr.shape[0]) - 1
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     args = (_ptr(q), _ptr(kv), _ptr(kv_scales), _ptr(kv_indptr), _ptr(kv_indices), _ptr(out), _ptr(lse), B,
-            int(total_kv), int(kv_dtype), float(sm_scale), _ptr(ws), ws_bytes, int(flags), _stream(q.device))
-    fn = _lib.mla_decode
+            int(total_kv), _kv_rows(kv, kv_rows), int(kv_dtype), float(sm_scale), _ptr(ws), ws_bytes, int(flags),
+            _stream(q.device))
+    fn = _lib.mla_decode_rows
     keep = (q, kv, kv_scales, kv_indptr, kv_indices, out, lse, ws)
 
     def call():

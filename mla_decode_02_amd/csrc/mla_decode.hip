@@ -112,6 +112,9 @@ struct Params {
     // query row: one arrival counter per row (zero between calls); NULL when a
     // combine launch merges them.
     uint32_t* counters;
+    // Rows the cache buffer holds (0: unknown). Known, on batches of equal
+    // lengths, it bounds the rows gathered before kv_indices arrives.
+    int64_t kv_rows;
 };
 
 // ---------------------------------------------------------------------------
@@ -879,6 +882,32 @@ __device__ __forceinline__ void dma_idx(const Params& P, int first, int n, int32
         dma4(P.indices + first + min(tid + k * kThreads, n - 1), lds_addr(idx + k * kThreads + wave0));
 }
 
+// Row of prologue token j (< n) of this wave's tile half: the row a
+// contiguous cache holds (first + j, tokens past n repeat the last one, as
+// issue_step does), clamped below the cache size.
+__device__ __forceinline__ int64_t early_row(const Params& P, int64_t first, int j, int n) {
+    return min(first + min(j, n - 1), P.kv_rows - 1);
+}
+
+// Equal lengths and a known cache size: the gathers of the first D steps of
+// a range whose kv_indices entries are guessed to be first, first + 1, ...
+// (the rows a contiguous cache gives the sequence), issued with the query and
+// index requests so that the first rows arrive in the same memory round trip.
+// run_wg keeps them only where kv_indices confirms every row.
+template <int KV>
+__device__ __forceinline__ void issue_early(const Params& P, uint8_t* smem, int64_t first, int n) {
+    using L = Layout<KV>;
+    constexpr int R = Fmt<KV>::kRing, D = R - 1;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r = lane & 15;
+    const int tile = wave & 1, hf = wave >> 1;
+    const int nsteps = (n + kStepTokens - 1) / kStepTokens;
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        if (d < nsteps)
+            issue_half<KV>(P, early_row(P, first, d * kStepTokens + kTile * tile + r, n),
+                           smem + (d % R) * L::kStepBytes + tile * Fmt<KV>::kTileBytes, lane, hf);
+}
+
 // One query row in registers, with the scales read alongside it.
 //   bf16 query (bf16 and fp8 caches): this wave's half of Q^T, straight in
 //   the score operand layout.
@@ -1031,7 +1060,8 @@ __device__ void merge_if_last(const Params& P, int row, uint8_t* smem) {
 // publish a dynamic scale.
 template <int KV, int QF, bool MG = false>
 __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, int t1, bool final, int slot,
-                       bool scale_out, QueryRegs<KV, QF>& qr, bool idx_dma, bool idx_staged) {
+                       bool scale_out, QueryRegs<KV, QF>& qr, bool idx_dma, bool idx_staged,
+                       int64_t early_first = -1) {
     using L = Layout<KV>;
     constexpr int R = Fmt<KV>::kRing;
     constexpr int D = R - 1;  // steps issued ahead of the one computed
@@ -1071,7 +1101,8 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
     }
     asm volatile("" ::"v"(kv_scale), "v"(q_part), "v"(q_scale));
     // The caller's index DMA, kept or not, has landed before anything else
-    // touches the index window (no gathers are in flight yet).
+    // touches the index window (so have the caller's early gathers, issued
+    // after it: no gathers are in flight past this point).
     if (idx_dma) wait_vmcnt<0>();
     if constexpr (QF) {
         if (P.q_amax) {
@@ -1118,9 +1149,24 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
             }
         };
         auto put_scores = [&](int i, f32x4 part) { sbuf[(i & 1) * (kWaves * 64) + wave * 64 + lane] = part; };
+        // The caller's early gathers of the first D steps (already landed) stand
+        // when the guessed range was the true one and kv_indices names exactly
+        // the rows this wave fetched; else this wave gathers its steps again.
+        bool keep = w0 == t0 && early_first >= 0 && idx_staged;
+        if (keep) {
 #pragma unroll
-        for (int d = 0; d < D; ++d)
-            if (d < nsteps) issue_step(d);
+            for (int d = 0; d < D; ++d)
+                if (d < nsteps) {
+                    const int j = d * kStepTokens + kTile * tile + r;
+                    keep = keep && (int64_t)idx[min(j, n - 1)] == early_row(P, early_first, j, n);
+                }
+            keep = __all(keep);
+        }
+        if (!keep) {
+#pragma unroll
+            for (int d = 0; d < D; ++d)
+                if (d < nsteps) issue_step(d);
+        }
         // fp8 query, first window: quantise while the first gathers are in
         // flight. The codes ([head][576] bytes) pass through ring slot D, whose
         // step is issued only after the next two barriers.
@@ -1341,6 +1387,14 @@ void split_kernel(STAGE1_ARGS) {
     if (idx_dma)
         dma_idx<KV>(P, row * Lu + t0u, min(Fmt<KV>::kIdxWindow, t1u - t0u),
                     reinterpret_cast<int32_t*>(smem + Layout<KV>::kIdxOff));
+    // With the cache size known, the first steps' rows of a contiguous cache
+    // are requested as well (kept by run_wg where kv_indices agrees). Not on
+    // the MXFP4 cache: the wait for the query registers also drains LDS-DMA
+    // loads issued before it, which would put the query split behind the
+    // first rows instead of beside them.
+    const int64_t early_first =
+        (KV != MLA_KV_MXFP4 && idx_dma && P.kv_rows > 0) ? (int64_t)row * Lu + t0u : -1;
+    if (early_first >= 0) issue_early<KV>(P, smem, early_first, min(Fmt<KV>::kIdxWindow, t1u - t0u));
     // the sequence of this query row, and the cache tokens the causal reading hides from it
     int b = row, hide = 0;
     if (P.uni_q > 0 || P.qo_indptr) {
@@ -1366,7 +1420,7 @@ void split_kernel(STAGE1_ARGS) {
     const int t1 = min(L, t0 + chunk);
     const bool staged = idx_dma && base == row * Lu && L == Lu;  // then t0, t1 are t0u, t1u
     run_wg<KV, QF, MG>(P, smem, row, base, t0, t1, P.nsplit == 1, row * P.nsplit + s, blockIdx.x == 0, qr, idx_dma,
-                   staged);
+                       staged, early_first);
 }
 
 // Largest p whose share [floor(p T / G), floor((p+1) T / G)) starts at or before t.
@@ -1766,7 +1820,7 @@ static int decode_impl(const void* q, const void* kv, const void* kv_scales, con
                        const int32_t* kv_indices, const int32_t* kv_last_page_len, int page_size, void* out,
                        float* lse, int batch, int64_t total_kv, int kv_dtype, float sm_scale, void* workspace,
                        size_t workspace_bytes, int flags, void* stream, int q_mode = -1, float* q_scale = nullptr,
-                       const MtpArgs* mtp = nullptr) {
+                       const MtpArgs* mtp = nullptr, int64_t kv_rows = 0) {
     mla_plan_info plan;
     const int rows = mtp ? mtp->total_q : batch;
     int rc = mtp ? mtp_plan(batch, mtp->total_q, total_kv, kv_dtype, flags, &plan)
@@ -1778,7 +1832,7 @@ static int decode_impl(const void* q, const void* kv, const void* kv_scales, con
     if (batch == 0 || rows == 0) return MLA_OK;
     if (q_mode >= 0 && (!q_scale || !aligned(q_scale, 4))) return MLA_ERR_INVALID_ARG;
     if (mtp && mtp->uni_q == 0 && (!mtp->qo_indptr || !aligned(mtp->qo_indptr, 4))) return MLA_ERR_INVALID_ARG;
-    if (!q || !kv || !kv_indptr || !out) return MLA_ERR_INVALID_ARG;
+    if (!q || !kv || !kv_indptr || !out || kv_rows < 0) return MLA_ERR_INVALID_ARG;
     if (total_kv > 0 && !kv_indices) return MLA_ERR_INVALID_ARG;
     if (kv_dtype != MLA_KV_BF16 && !kv_scales) return MLA_ERR_INVALID_ARG;
     if (page_size > 1 && (!kv_last_page_len || !aligned(kv_last_page_len, 4))) return MLA_ERR_INVALID_ARG;
@@ -1810,6 +1864,7 @@ static int decode_impl(const void* q, const void* kv, const void* kv_scales, con
                                                              partial_lse_offset(plan.num_partials))
                                    : nullptr;
     P.counters = plan.combine == 2 ? reinterpret_cast<uint32_t*>(workspace) : nullptr;
+    P.kv_rows = kv_rows;
     P.batch = batch;
     P.nsplit = plan.num_splits;
     P.grid = plan.grid;
@@ -1855,6 +1910,14 @@ extern "C" int mla_decode(const void* q, const void* kv, const void* kv_scales, 
                           void* stream) {
     return mla::decode_impl(q, kv, kv_scales, kv_indptr, kv_indices, nullptr, 1, out, lse, batch, total_kv, kv_dtype,
                             sm_scale, workspace, workspace_bytes, flags, stream);
+}
+
+extern "C" int mla_decode_rows(const void* q, const void* kv, const void* kv_scales, const int32_t* kv_indptr,
+                               const int32_t* kv_indices, void* out, float* lse, int batch, int64_t total_kv,
+                               int64_t kv_rows, int kv_dtype, float sm_scale, void* workspace, size_t workspace_bytes,
+                               int flags, void* stream) {
+    return mla::decode_impl(q, kv, kv_scales, kv_indptr, kv_indices, nullptr, 1, out, lse, batch, total_kv, kv_dtype,
+                            sm_scale, workspace, workspace_bytes, flags, stream, -1, nullptr, nullptr, kv_rows);
 }
 
 extern "C" int mla_decode_paged(const void* q, const void* kv, const void* kv_scales, const int32_t* kv_indptr,

@@ -35,7 +35,7 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("mla_decode", "mla_decode_paged", "mla_decode_q8", "mla_decode_mtp", "mla_decode_plan",
+    for n in ("mla_decode", "mla_decode_rows", "mla_decode_paged", "mla_decode_q8", "mla_decode_mtp", "mla_decode_plan",
               "mla_decode_workspace_size", "mla_decode_q8_workspace_size", "mla_decode_mtp_workspace_size",
               "mla_quantize_q8_debug", "mla_dequant_debug", "mla_status_string"):
         assert n in names
@@ -370,3 +370,14 @@ def test_plan_merge_rule(mla):
     # several query tokens: the rows are the query tokens
     assert mla.mla_decode_mtp_workspace_size(4, 16, 4 * 1024, 1, mla.flags_for(splits=3)) == \
         mla.mla_decode_workspace_size(16, 16 * 1024, 1, mla.flags_for(splits=3))
+
+
+def test_rows_validation(raw_lib):
+    """mla_decode_rows rejects a negative cache row count on the host, before any launch."""
+    f = raw_lib.mla_decode_rows
+    f.restype = ctypes.c_int
+    vp = ctypes.c_void_p
+    f.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                  ctypes.c_float, vp, ctypes.c_size_t, ctypes.c_int, vp]
+    assert f(A, A, A, A, A, A, None, 2, 64, -1, 1, 0.0, None, 0, 0, None) == -1
+    assert f(A, A, A, A, A, A, None, 0, 0, -1, 1, 0.0, None, 0, 0, None) == 0   # batch 0: a no-op, as mla_decode

@@ -528,3 +528,73 @@ def test_mxfp4_split_query_wide_range(mla, orc, dev):
     ref = oracle_ref(orc, case)
     check(run_gpu(mla, case, dev), ref, "MXFP4, wide-range query")
     check(run_gpu(mla, case, dev, flags=mla.flags_for(persistent=True, grid=7)), ref, "MXFP4, wide-range query, persistent")
+
+
+# ---------------------------------------------------------------------------
+# Early gathers of the rows a contiguous cache would hold (mla_decode_rows)
+# ---------------------------------------------------------------------------
+def _run_rows(mla, case, dev, kv_rows, flags=0):
+    t = to_dev(case, dev)
+    B = case.batch
+    out = torch.full((B, 16, 512), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((B, 16), float("nan"), dtype=torch.float32, device=dev)
+    mla.mla_decode(t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], t["kv_indices"], out, lse,
+                   total_kv=case.total_kv, kv_dtype=case.kv_dtype, flags=flags, kv_rows=kv_rows)
+    torch.cuda.synchronize()
+    return out.view(torch.int16).cpu().numpy(), lse.view(torch.int32).cpu().numpy()
+
+
+def _with_indices(case, indices, rows=None):
+    """The case with kv_indices replaced (and the cache cut to `rows` rows)."""
+    import dataclasses
+    kv, sc = case.kv, case.kv_scales
+    if rows is not None:
+        kv = kv[:rows]
+        if case.kv_dtype == syn.KV_MXFP4:
+            sc = sc[:rows]
+    return dataclasses.replace(case, kv=np.ascontiguousarray(kv), kv_scales=sc,
+                               kv_indices=np.ascontiguousarray(indices, dtype=np.int32))
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+def test_early_gathers_match_the_plain_call(mla, orc, dev, kv_dtype):
+    """With equal lengths and the cache size known, stage 1 requests the rows a
+    contiguous cache holds before kv_indices arrives, and keeps them only where
+    kv_indices agrees. Whatever the indices, the result is bit-identical to the
+    call without early requests (kv_rows = 0), and within the oracle's bounds:
+    contiguous indices (all kept), shuffled (all gathered again), contiguous
+    but for a few entries in the first steps of some ranges (only those waves
+    gather again), and a cache with fewer rows than tokens (indices repeat;
+    guessed rows beyond the cache are clamped below it)."""
+    B, L = 6, 700
+    base = syn.make_case(B, [L] * B, kv_dtype, seed=95)
+    T = base.total_kv
+    rng = np.random.default_rng(96)
+    contiguous = np.arange(T, dtype=np.int32)
+    shuffled = rng.permutation(T).astype(np.int32)
+    patched = contiguous.copy()
+    for pos in (0, 5, 33, 700 + 17, 3 * 700 + 64, 5 * 700 + 2):
+        patched[pos] = int(rng.integers(0, T))
+    small = 1000
+    repeating = (np.arange(T) % small).astype(np.int32)
+    cases = [("contiguous", _with_indices(base, contiguous)), ("shuffled", _with_indices(base, shuffled)),
+             ("patched", _with_indices(base, patched)), ("repeating", _with_indices(base, repeating, rows=small))]
+    for name, case in cases:
+        ref = oracle_ref(orc, case)
+        for flags in (0, mla.flags_for(splits=3), mla.flags_for(splits=1)):
+            early = _run_rows(mla, case, dev, None, flags)
+            plain = _run_rows(mla, case, dev, 0, flags)
+            assert np.array_equal(early[0], plain[0]), f"{name} flags={flags:#x}: out differs from the plain call"
+            assert np.array_equal(early[1], plain[1]), f"{name} flags={flags:#x}: lse differs from the plain call"
+        check(run_gpu(mla, case, dev), ref, f"early gathers, {name}")
+
+
+def test_early_gathers_unequal_lengths(mla, orc, dev):
+    """Lengths that differ (the guessed range is rejected once kv_indptr arrives):
+    the early requests are dropped and the result equals the plain call's."""
+    case = syn.make_case(5, [700, 700, 0, 2000, 33], syn.KV_FP8, seed=97)
+    case = _with_indices(case, np.arange(case.total_kv, dtype=np.int32))
+    a = _run_rows(mla, case, dev, None)
+    b = _run_rows(mla, case, dev, 0)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    check(run_gpu(mla, case, dev), oracle_ref(orc, case), "early gathers, unequal lengths")
