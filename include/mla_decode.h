@@ -78,9 +78,12 @@ extern "C" {
 /*
  * Workspace layout. When a plan has split partials (workspace_bytes > 0), the
  * first MLA_WORKSPACE_COUNTER_BYTES bytes of the workspace hold one 32-bit
- * arrival counter per query row, used by plans with combine = 2: each split
- * workgroup counts itself in after writing its partial, and the one that
- * arrives last merges the row's partials and sets the counter back to zero.
+ * arrival counter per query row, used by plans with combine = 2 (split-K with
+ * 2 to 4 splits over at most 16384 query rows, unless MLA_FLAG_COMBINE_LAUNCH
+ * is set): each split workgroup counts itself in after writing its partial,
+ * and the one that arrives last merges the row's partials (the log-sum-exp
+ * merge of flash-decoding split partials; submission 593653,
+ * `_flash_fp8_split_s2`) and sets the counter back to zero.
  * That region must be all zero when a call starts: zero the workspace (at
  * least its first MLA_WORKSPACE_COUNTER_BYTES bytes) once after allocating
  * it. Every call leaves the region all zero again, whatever its plan, so a
