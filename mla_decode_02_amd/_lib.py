@@ -213,8 +213,12 @@ def mla_decode(q, kv, kv_scales, kv_indptr, kv_indices, out, lse=None, *, total_
 
 def _kv_rows(kv, kv_rows):
     """The cache row count passed to mla_decode_rows: kv's leading dimension
-    unless the caller gives one (0 turns the early row requests off)."""
-    return int(kv.shape[0]) if kv_rows is None else int(kv_rows)
+    unless the caller gives one (0 turns the early row requests off; more rows
+    than kv holds are refused, since the kernels may read below that bound)."""
+    if kv_rows is None:
+        return int(kv.shape[0])
+    _need(0 <= int(kv_rows) <= int(kv.shape[0]), "kv_rows must lie in [0, kv.shape[0]]")
+    return int(kv_rows)
 
 
 def mla_decode_paged(q, kv, kv_scales, kv_indptr, kv_indices, kv_last_page_len, out, lse=None, *, page_size: int,

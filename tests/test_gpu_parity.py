@@ -598,3 +598,5 @@ def test_early_gathers_unequal_lengths(mla, orc, dev):
     b = _run_rows(mla, case, dev, 0)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
     check(run_gpu(mla, case, dev), oracle_ref(orc, case), "early gathers, unequal lengths")
+    with pytest.raises(ValueError):  # a bound beyond the cache tensor is refused before any launch
+        _run_rows(mla, case, dev, int(case.kv.shape[0]) + 1)
