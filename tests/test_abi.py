@@ -381,3 +381,20 @@ def test_rows_validation(raw_lib):
                   ctypes.c_float, vp, ctypes.c_size_t, ctypes.c_int, vp]
     assert f(A, A, A, A, A, A, None, 2, 64, -1, 1, 0.0, None, 0, 0, None) == -1
     assert f(A, A, A, A, A, A, None, 0, 0, -1, 1, 0.0, None, 0, 0, None) == 0   # batch 0: a no-op, as mla_decode
+
+
+def test_short_splits_take_one_workgroup_per_cu_merged(mla):
+    """Short splits on a batch that fills the chip at one workgroup per CU with at
+    most 4 splits take that plan, merged by the last-arriving split (fp8 64 x 1k:
+    4 merged splits); the rule needs the merge (MLA_FLAG_COMBINE_LAUNCH keeps the
+    8-split plan), leaves long splits at two workgroups per CU (64 x 8k: 8) and
+    leaves batches that one workgroup per CU cannot fill within 4 splits (32 x 1k: 8)."""
+    p = mla.mla_decode_plan(64, 64 * 1024, 1)
+    assert (p.num_splits, p.combine) == (4, 2)
+    p = mla.mla_decode_plan(64, 64 * 1024, 1, mla.FLAG_COMBINE_LAUNCH)
+    assert (p.num_splits, p.combine) == (8, 1)
+    assert mla.mla_decode_plan(64, 64 * 8192, 1).num_splits == 8
+    p = mla.mla_decode_plan(32, 32 * 1024, 1)
+    assert (p.num_splits, p.combine) == (8, 1)
+    p = mla.mla_decode_plan(256, 256 * 1024, 1)
+    assert (p.num_splits, p.combine) == (2, 2)
