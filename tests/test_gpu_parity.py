@@ -600,3 +600,40 @@ def test_early_gathers_unequal_lengths(mla, orc, dev):
     check(run_gpu(mla, case, dev), oracle_ref(orc, case), "early gathers, unequal lengths")
     with pytest.raises(ValueError):  # a bound beyond the cache tensor is refused before any launch
         _run_rows(mla, case, dev, int(case.kv.shape[0]) + 1)
+
+
+def test_merge_in_stage1_two_streams(mla, dev):
+    """Two streams run merged-split calls at the same time, each on its own
+    workspace (the C ABI orders calls that share one): every result equals the
+    same call run alone, bit for bit, so concurrent kernels do not disturb each
+    other's arrival counters or coherent partials."""
+    cases = [syn.make_case(24, [1024] * 20 + [77, 0, 900, 3000], syn.KV_FP8, seed=98, shuffle=True),
+             syn.make_case(16, [512] * 16, syn.KV_MXFP4, seed=99)]
+    flags = mla.flags_for(splits=3)
+    setups = []
+    for c in cases:
+        t = to_dev(c, dev)
+        assert mla.mla_decode_plan(c.batch, c.total_kv, c.kv_dtype, flags).combine == 2
+        ws = new_workspace(mla, c, dev, flags)
+        ref_o = torch.empty((c.batch, 16, 512), dtype=torch.bfloat16, device=dev)
+        ref_l = torch.empty((c.batch, 16), dtype=torch.float32, device=dev)
+        mla.mla_decode(t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], t["kv_indices"], ref_o, ref_l,
+                       total_kv=c.total_kv, kv_dtype=c.kv_dtype, workspace=ws, flags=flags)
+        setups.append((c, t, ws, ref_o, ref_l))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
+    outs = [[], []]
+    for _ in range(15):
+        for k, (c, t, ws, _, _) in enumerate(setups):
+            with torch.cuda.stream(streams[k]):
+                o = torch.empty((c.batch, 16, 512), dtype=torch.bfloat16, device=dev)
+                l = torch.empty((c.batch, 16), dtype=torch.float32, device=dev)
+                mla.mla_decode(t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], t["kv_indices"], o, l,
+                               total_kv=c.total_kv, kv_dtype=c.kv_dtype, workspace=ws, flags=flags)
+                outs[k].append((o, l))
+    torch.cuda.synchronize()
+    for k, (c, _, ws, ref_o, ref_l) in enumerate(setups):
+        for i, (o, l) in enumerate(outs[k]):
+            assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16)), f"stream {k} call {i}: out differs"
+            assert torch.equal(l.view(torch.int32), ref_l.view(torch.int32)), f"stream {k} call {i}: lse differs"
+        assert int(torch.count_nonzero(ws[: mla.WORKSPACE_COUNTER_BYTES])) == 0
