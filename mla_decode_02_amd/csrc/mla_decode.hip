@@ -1436,6 +1436,7 @@ __device__ __forceinline__ int64_t share_start(int64_t p, int64_t T, int64_t G) 
 template <int KV, int QF>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Fmt<KV>::kWgsPerCU, Fmt<KV>::kWgsPerCU)))
 void persistent_kernel(STAGE1_ARGS) {
+    if (blockIdx.x >= kNumCUs) __builtin_amdgcn_s_setprio(2);  // as in split_kernel (MXFP4 mixed lengths 46.0 -> 45.6 us)
     const Params P = stage1_params(q_arg, indices_arg, kv_scales_arg, nsplit_arg, uni_len_arg, uni_chunk_arg, P_arg);
     __shared__ __attribute__((aligned(16))) uint8_t smem[Layout<KV>::kBytes];
     const int64_t T = P.total, Gn = P.grid;
