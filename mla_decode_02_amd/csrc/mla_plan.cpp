@@ -33,7 +33,14 @@ static size_t partial_bytes(int num_partials) {
     return kCounterBytes + ((o + 255) / 256) * 256 + ((l + 255) / 256) * 256;
 }
 
-size_t q8_amax_offset(size_t plan_bytes) { return (plan_bytes + 255) & ~(size_t)255; }
+// The partial maxima of the dynamic fp8 query scale follow the plan's bytes,
+// and never start inside the arrival-counter region: a plan without split
+// partials needs no workspace of its own, but the region must stay zero for
+// later calls that reuse the buffer with a merging plan.
+size_t q8_amax_offset(size_t plan_bytes) {
+    const size_t o = (plan_bytes + 255) & ~(size_t)255;
+    return o < kCounterBytes ? kCounterBytes : o;
+}
 
 size_t partial_lse_offset(int num_partials) {
     size_t o = (size_t)num_partials * kHeads * kDv * sizeof(float);

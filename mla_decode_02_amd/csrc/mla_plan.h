@@ -37,7 +37,8 @@ size_t partial_lse_offset(int num_partials);
 // tokens (several query tokens per sequence): always split-K, made as for
 // total_q sequences of the average length.
 int mtp_plan(int batch, int total_q, int64_t total_kv, int kv_dtype, int flags, mla_plan_info* p);
-// Offset of the dynamic fp8 query scale's partial maxima: after the plan's bytes.
+// Offset of the dynamic fp8 query scale's partial maxima: after the plan's
+// bytes and never inside the arrival-counter region.
 size_t q8_amax_offset(size_t plan_bytes);
 
 }  // namespace mla

@@ -37,13 +37,24 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("mla_decode", "mla_decode_rows", "mla_decode_paged", "mla_decode_q8", "mla_decode_mtp", "mla_decode_plan",
               "mla_decode_workspace_size", "mla_decode_q8_workspace_size", "mla_decode_mtp_workspace_size",
-              "mla_quantize_q8_debug", "mla_dequant_debug", "mla_status_string"):
+              "mla_quantize_q8_debug", "mla_dequant_debug", "mla_hbm_read_probe", "mla_status_string"):
         assert n in names
 
 
 def test_library_exports_every_declared_symbol(raw_lib):
     for name in _declared_functions():
         assert hasattr(raw_lib, name), name
+
+
+def test_hbm_read_probe_validation(raw_lib):
+    """The streaming-read measurement aid checks its arguments on the host (no launch)."""
+    f = raw_lib.mla_hbm_read_probe
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert f(None, 0, None) == 0           # nothing to read
+    assert f(None, 64, None) == -1         # null buffer
+    assert f(ctypes.c_void_p(24), 64, None) == -1   # misaligned
+    assert f(ctypes.c_void_p(256), 40, None) == -1  # not a multiple of 16
 
 
 def test_status_strings(mla):
@@ -232,8 +243,20 @@ def test_q8_workspace_size(mla):
         base = mla.mla_decode_workspace_size(32, 32 * 1024, 1, flags)
         assert mla.mla_decode_q8_workspace_size(32, 32 * 1024, 1, flags, mla.Q_SCALE_STATIC) == base
         dyn = mla.mla_decode_q8_workspace_size(32, 32 * 1024, 1, flags, mla.Q_SCALE_DYNAMIC)
-        assert dyn >= base + 1024 and dyn - 1024 == (base + 255) // 256 * 256
+        # the partial maxima follow the plan's bytes and never start inside the counter region
+        assert dyn - 1024 == max((base + 255) // 256 * 256, mla.WORKSPACE_COUNTER_BYTES)
     assert mla.mla_decode_q8_workspace_size(32, 1024, 1, 0, 7) == 0
+
+
+def test_q8_dynamic_maxima_stay_out_of_the_counter_region(mla):
+    """A plan without split partials needs no workspace of its own; the dynamic scale's
+    1 KiB of partial maxima then lies right after the arrival-counter region, so a later
+    merging call on the same buffer still finds every counter zero."""
+    one = mla.flags_for(splits=1)
+    assert mla.mla_decode_workspace_size(4, 4 * 300, 1, one) == 0
+    assert mla.mla_decode_q8_workspace_size(4, 4 * 300, 1, one, mla.Q_SCALE_DYNAMIC) == \
+        mla.WORKSPACE_COUNTER_BYTES + 1024
+    assert mla.mla_decode_q8_workspace_size(4, 4 * 300, 1, one, mla.Q_SCALE_STATIC) == 0
 
 
 def test_quantize_q8_debug_validation(raw_lib):

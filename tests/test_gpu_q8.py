@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import synthetic as syn
-from test_gpu_parity import DTYPES, check, to_dev
+from test_gpu_parity import DTYPES, check, oracle_tokens, to_dev
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -178,7 +178,7 @@ def test_q8_persistent(mla, orc, dev, kv_dtype, grid):
 def test_q8_paged(mla, orc, dev, kv_dtype):
     lens = [1, 0, 8, 25, 1030]
     case, paged = syn.make_paged_case(len(lens), lens, kv_dtype, 8, seed=440 + kv_dtype, extra_pages=3)
-    ref, _ = q8_ref(orc, case, scale=STATIC_SCALE)
+    ref, _ = q8_ref(orc, oracle_tokens(orc, case, paged), scale=STATIC_SCALE)  # the oracle expands the pages
     go, gl, _ = run_q8(mla, case, dev, 0, scale=STATIC_SCALE, paged=paged)
     check((go, gl), ref, "q8 paged")
 
@@ -249,3 +249,23 @@ def test_prepared_q8_call_matches_direct_call(mla, dev, kv_dtype):
         outs.append((out.float().cpu().numpy(), lse.cpu().numpy(), qs.item()))
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
     assert outs[0][2] == outs[1][2]
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+def test_q8_dynamic_single_split_then_merged_call_on_one_workspace(mla, orc, dev, kv_dtype):
+    """A dynamic-scale call whose plan has one split (no partials) writes its partial
+    maxima after the arrival-counter region: a merging call (3 splits) on the same
+    workspace afterwards finds every counter zero, merges, and leaves them zero."""
+    case = syn.make_case(4, [300, 45, 0, 260], kv_dtype, seed=470 + kv_dtype, shuffle=True)
+    one, three = mla.flags_for(splits=1), mla.flags_for(splits=3)
+    assert mla.mla_decode_plan(4, case.total_kv, kv_dtype, three).combine == 2
+    need = max(mla.mla_decode_q8_workspace_size(4, case.total_kv, kv_dtype, f, mla.Q_SCALE_DYNAMIC)
+               for f in (one, three))
+    ws = mla.new_workspace(need, dev, poison=True)
+    ref, (_, rsc) = q8_ref(orc, case)
+    for flags in (one, three, one, three):
+        go, gl, gsc = run_q8(mla, case, dev, 1, flags=flags, ws=ws)
+        check((go, gl), ref, f"q8 dynamic flags={flags:#x}")
+        assert gsc[0] == rsc[0]
+        counters = ws[:mla.WORKSPACE_COUNTER_BYTES].view(torch.int32)
+        assert int(torch.count_nonzero(counters)) == 0, "arrival counters left non-zero"
