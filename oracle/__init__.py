@@ -93,6 +93,15 @@ def _load():
     lib.oracle_quantize_q_fp8.restype = ctypes.c_int
     lib.oracle_quantize_q_fp8.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                                           ctypes.c_void_p]
+    lib.oracle_expand_pages.restype = ctypes.c_int
+    lib.oracle_expand_pages.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
+    lib.oracle_mla_decode_paged.restype = ctypes.c_int
+    lib.oracle_mla_decode_paged.argtypes = [
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_void_p,
+    ]
     lib.oracle_max_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -221,6 +230,52 @@ def mla_decode_mtp(q: np.ndarray, qo_indptr: np.ndarray, causal: bool, kv_dtype:
     )
     if rc != 0:
         raise ValueError("oracle_mla_decode_mtp: invalid argument")
+    return out, lse
+
+
+def expand_pages(page_indptr: np.ndarray, page_ids: np.ndarray, last_page_len: np.ndarray | None, page_size: int):
+    """Token-level tables of a paged cache (oracle_expand_pages): returns
+    (tok_indptr int32 [B+1], tok_rows int32 [T]) with the cache row of every
+    token, sequence by sequence, in token order."""
+    page_indptr = np.ascontiguousarray(page_indptr, dtype=np.int32)
+    page_ids = np.ascontiguousarray(page_ids, dtype=np.int32)
+    last = None if last_page_len is None else np.ascontiguousarray(last_page_len, dtype=np.int32)
+    batch = page_indptr.shape[0] - 1
+    cap = int(page_indptr[batch]) * int(page_size)
+    tok_indptr = np.zeros(batch + 1, dtype=np.int32)
+    tok_rows = np.zeros(max(cap, 1), dtype=np.int32)
+    rc = _load().oracle_expand_pages(_ptr(page_indptr), _ptr(page_ids) if page_ids.size else None, _ptr(last),
+                                     int(page_size), batch, _ptr(tok_indptr), _ptr(tok_rows), cap)
+    if rc != 0:
+        raise ValueError("oracle_expand_pages: invalid argument")
+    return tok_indptr, tok_rows[:int(tok_indptr[batch])].copy()
+
+
+def mla_decode_paged(q_bits: np.ndarray, kv_dtype: int, kv: np.ndarray, scales: np.ndarray | None,
+                     page_indptr: np.ndarray, page_ids: np.ndarray, last_page_len: np.ndarray | None,
+                     page_size: int, sm_scale: float = SM_SCALE, batches=None, nthreads: int = 0):
+    """Reference MLA decode over a paged cache (oracle_mla_decode_paged): the
+    oracle expands the pages itself. Returns (out [n,16,512] f64, lse [n,16] f64)."""
+    q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    kv = np.ascontiguousarray(kv)
+    scales = None if scales is None else np.ascontiguousarray(scales)
+    page_indptr = np.ascontiguousarray(page_indptr, dtype=np.int32)
+    page_ids = np.ascontiguousarray(page_ids, dtype=np.int32)
+    last = None if last_page_len is None else np.ascontiguousarray(last_page_len, dtype=np.int32)
+    batch = page_indptr.shape[0] - 1
+    if batches is None:
+        blist, n = None, batch
+    else:
+        blist = np.ascontiguousarray(np.asarray(batches, dtype=np.int32))
+        n = blist.shape[0]
+    out = np.zeros((n, NUM_HEADS, DV), dtype=np.float64)
+    lse = np.zeros((n, NUM_HEADS), dtype=np.float64)
+    rc = _load().oracle_mla_decode_paged(
+        _ptr(q_bits), kv_dtype, _ptr(kv), _ptr(scales), _ptr(page_indptr), _ptr(page_ids) if page_ids.size else None,
+        _ptr(last), int(page_size), batch, float(sm_scale), _ptr(blist), n, nthreads, _ptr(out), _ptr(lse),
+    )
+    if rc != 0:
+        raise ValueError("oracle_mla_decode_paged: invalid argument")
     return out, lse
 
 

@@ -547,6 +547,82 @@ int oracle_quantize_q_fp8(const uint16_t* q, int64_t n, int mode, float* scale, 
     return 0;
 }
 
+/*
+ * Paged cache (more than one row per page). The convention is that of the
+ * pages' a16w8 path (submission 616673, `_run_a16w8`: the cache viewed as
+ * [pages, page_size, 1, 576], the page table given by kv_indptr / kv_indices
+ * counted in pages, and kv_last_page_lens) and of the page tables passed to
+ * `mla_decode_fwd` (submission 593653):
+ *   - sequence b owns the pages page_ids[page_indptr[b]] ..
+ *     page_ids[page_indptr[b+1] - 1], in that order;
+ *   - page p holds cache rows p * page_size .. p * page_size + page_size - 1;
+ *   - every page of a sequence but its last contributes all page_size rows,
+ *     in row order; the last one contributes its first last_page_len[b] rows
+ *     (1 .. page_size). With page_size 1 every page is one row and
+ *     last_page_len is not read.
+ * oracle_expand_pages writes the token-level tables of that convention:
+ * tok_indptr [batch + 1] and tok_rows (cache row of every token, in order;
+ * room for cap entries). Returns 0, or -1 on an invalid argument.
+ */
+int oracle_expand_pages(const int32_t* page_indptr, const int32_t* page_ids, const int32_t* last_page_len,
+                        int page_size, int batch, int32_t* tok_indptr, int32_t* tok_rows, int64_t cap) {
+    int64_t n = 0;
+    int b;
+    if (!page_indptr || !tok_indptr || batch < 0 || page_size < 1) return -1;
+    tok_indptr[0] = 0;
+    for (b = 0; b < batch; ++b) {
+        int32_t first = page_indptr[b], end = page_indptr[b + 1], k;
+        if (end < first) return -1;
+        if (end > first && !page_ids) return -1;
+        for (k = first; k < end; ++k) {
+            int64_t rows_in_page = page_size, i;
+            if (k == end - 1 && page_size > 1) {  /* the sequence's last page */
+                if (!last_page_len) return -1;
+                rows_in_page = last_page_len[b];
+                if (rows_in_page < 1 || rows_in_page > page_size) return -1;
+            }
+            for (i = 0; i < rows_in_page; ++i) {
+                int64_t row = (int64_t)page_ids[k] * page_size + i;
+                if (n >= cap || row > INT32_MAX) return -1;
+                tok_rows[n++] = (int32_t)row;
+            }
+        }
+        if (n > INT32_MAX) return -1;
+        tok_indptr[b + 1] = (int32_t)n;
+    }
+    return 0;
+}
+
+/*
+ * MLA decode over a paged cache: the pages of each sequence are expanded into
+ * its token rows (oracle_expand_pages), then the attention of
+ * oracle_mla_decode (route 0) runs over those tokens. Arguments as
+ * oracle_mla_decode, with the page table in place of kv_indptr / kv_indices.
+ */
+int oracle_mla_decode_paged(const uint16_t* q, int kv_dtype, const void* kv, const void* scales,
+                            const int32_t* page_indptr, const int32_t* page_ids, const int32_t* last_page_len,
+                            int page_size, int batch, double sm_scale, const int32_t* batches, int n_list,
+                            int nthreads, double* out, double* lse) {
+    int32_t* tok_indptr;
+    int32_t* tok_rows;
+    int64_t cap;
+    int rc;
+    if (!page_indptr || batch < 0 || page_size < 1) return -1;
+    cap = (int64_t)page_indptr[batch] * page_size;
+    if (cap < 0) return -1;
+    tok_indptr = (int32_t*)malloc(((size_t)batch + 1) * sizeof(int32_t));
+    tok_rows = (int32_t*)malloc((size_t)(cap > 0 ? cap : 1) * sizeof(int32_t));
+    rc = (tok_indptr && tok_rows) ? 0 : -1;
+    if (rc == 0)
+        rc = oracle_expand_pages(page_indptr, page_ids, last_page_len, page_size, batch, tok_indptr, tok_rows, cap);
+    if (rc == 0)
+        rc = decode_any(0, q, 1.0f, kv_dtype, kv, scales, tok_indptr, tok_rows, batch, sm_scale, batches, n_list, 0, 1,
+                        0, nthreads, out, lse);
+    free(tok_indptr);
+    free(tok_rows);
+    return rc;
+}
+
 /* Threads the OpenMP runtime will use (1 without OpenMP). */
 int oracle_max_threads(void) {
 #ifdef _OPENMP

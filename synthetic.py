@@ -124,9 +124,12 @@ class Case:
         return T * per_tok + (4 if self.kv_dtype == KV_FP8 else 0)
 
     def total_bytes(self) -> int:
-        """KV + scales + kv_indices + kv_indptr + q + out (bf16) + lse (fp32)."""
+        """KV + scales + kv_indices + kv_indptr + q + out (bf16) + lse (fp32); a paged
+        cache reads one kv_indices entry per page plus kv_last_page_len."""
         B, T = self.batch, self.total_kv
-        return (self.kv_bytes() + 4 * T + 4 * (B + 1) + 2 * B * NUM_HEADS * DQK
+        paged = self.meta.get("paged")
+        index_bytes = 4 * T if paged is None else 4 * (int(paged["kv_indptr"][-1]) + B)
+        return (self.kv_bytes() + index_bytes + 4 * (B + 1) + 2 * B * NUM_HEADS * DQK
                 + 2 * B * NUM_HEADS * DV + 4 * B * NUM_HEADS)
 
 
@@ -193,11 +196,14 @@ def make_mtp_query(q_lens, seed: int):
 def make_paged_case(batch: int, kv_lens, kv_dtype: int, page_size: int, seed: int, shuffle: bool = True,
                     extra_pages: int = 0):
     """A seeded workload over a paged cache: each sequence's tokens fill whole
-    pages of `page_size` rows except the last one; physical pages are a
-    seeded permutation (or the identity). Returns (case, paged), where `case`
-    is the same workload with one kv_indices entry per token (token j of
-    sequence b at row page * page_size + j % page_size) and `paged` holds the
-    page-level kv_indptr, kv_indices (page ids) and kv_last_page_len."""
+    pages of `page_size` rows except the last one; the physical pages are a
+    seeded permutation (or the identity). Returns (case, paged): `paged` holds
+    the page table (page-level kv_indptr, kv_indices = page ids, and
+    kv_last_page_len); `case` carries the query, the cache of every physical
+    page, and the token-level kv_indptr (prefix sums of the lengths). Which
+    cache row a token reads is the method's paging rule, so it is not written
+    here: case.kv_indices is empty, and the oracle expands the page table
+    itself (oracle.expand_pages)."""
     if np.isscalar(kv_lens):
         lens = np.full(batch, int(kv_lens), dtype=np.int64)
     else:
@@ -213,17 +219,12 @@ def make_paged_case(batch: int, kv_lens, kv_dtype: int, page_size: int, seed: in
     page_ids = (rng.permutation(phys_pages)[:total_pages] if shuffle else np.arange(total_pages)).astype(np.int64)
     tok_indptr = np.zeros(batch + 1, dtype=np.int64)
     tok_indptr[1:] = np.cumsum(lens)
-    rows = []
-    for b in range(batch):
-        j = np.arange(lens[b])
-        rows.append(page_ids[page_indptr[b] + j // page_size] * page_size + j % page_size)
-    tok_indices = np.concatenate(rows) if rows else np.zeros(0, dtype=np.int64)
     last = np.where(npages > 0, lens - (npages - 1) * page_size, 0)
-    case = Case(kv_dtype, base.q, base.kv, base.kv_scales, tok_indptr.astype(np.int32),
-                tok_indices.astype(np.int32),
-                meta={"batch": batch, "seed": seed, "page_size": page_size, "kv_dtype": KV_NAMES[kv_dtype]})
     paged = {"page_size": page_size, "kv_indptr": page_indptr.astype(np.int32),
              "kv_indices": page_ids.astype(np.int32), "kv_last_page_len": last.astype(np.int32)}
+    case = Case(kv_dtype, base.q, base.kv, base.kv_scales, tok_indptr.astype(np.int32), np.zeros(0, np.int32),
+                meta={"batch": batch, "seed": seed, "page_size": page_size, "kv_dtype": KV_NAMES[kv_dtype],
+                      "paged": paged})
     return case, paged
 
 
@@ -274,8 +275,7 @@ RAGGED = {
 def make_workload(name: str) -> Case:
     """A named workload; for the paged ones the page-level arrays are in meta['paged']."""
     if name in PAGED:
-        c, paged = make_paged_case(**PAGED[name])
-        c.meta["paged"] = paged
+        c, _ = make_paged_case(**PAGED[name])
     elif name in RAGGED:
         c = make_case(**RAGGED[name])
     else:

@@ -34,6 +34,13 @@ MUTANTS = {
     "quant_multiplies": ("oracle_bf16_value(q[i]) / s;", "oracle_bf16_value(q[i]) * s;"),
     "mtp_causal_off_by_one": ("L = L - n + 1 + t;", "L = L - n + t;"),
     "mtp_token_order": ("t = r - qo_indptr[b];", "t = n - 1 - (r - qo_indptr[b]);"),
+    "paged_last_page_full": ("rows_in_page = last_page_len[b];", "rows_in_page = page_size; (void)last_page_len;"),
+    "paged_row_of_page": ("int64_t row = (int64_t)page_ids[k] * page_size + i;",
+                          "int64_t row = (int64_t)page_ids[k] + i;"),
+    "paged_page_order": ("int64_t row = (int64_t)page_ids[k] * page_size + i;",
+                         "int64_t row = (int64_t)page_ids[first + end - 1 - k] * page_size + i;"),
+    "paged_rows_reversed": ("int64_t row = (int64_t)page_ids[k] * page_size + i;",
+                            "int64_t row = (int64_t)page_ids[k] * page_size + (rows_in_page - 1 - i);"),
     "mtp_query_row": ("decode_query(0, q, 1.0f, (int64_t)r * OR_HEADS + h, qh);",
                       "decode_query(0, q, 1.0f, (int64_t)b * OR_HEADS + h, qh);"),
 }

@@ -481,3 +481,84 @@ def test_mtp_row_subset(oracle_mod):
     sub = oracle_mod.mla_decode_mtp(q, qo, True, syn.KV_MXFP4, case.kv, case.kv_scales, case.kv_indptr,
                                     case.kv_indices, rows=[5, 0, 3])
     assert np.array_equal(sub[0], full[0][[5, 0, 3]]) and np.array_equal(sub[1], full[1][[5, 0, 3]])
+
+
+# --------------------------------------------------------------------------- paged cache
+
+
+def _read_paged_example():
+    """tests/golden/paged_example.txt: (page_size, page_indptr, page_ids, last_page_len, expected rows per sequence)."""
+    ps, pages, last, rows = None, [], [], []
+    with open(os.path.join(GOLDEN, "paged_example.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line.startswith("page_size"):
+                ps = int(line.split()[1])
+                continue
+            assert line.startswith("seq")
+            a, b, c = line[3:].split("|")
+            pages.append([int(x) for x in a.split()])
+            last.append(int(b))
+            rows.append([int(x) for x in c.split()])
+    indptr = np.zeros(len(pages) + 1, dtype=np.int32)
+    indptr[1:] = np.cumsum([len(p) for p in pages])
+    ids = np.array([x for p in pages for x in p], dtype=np.int32)
+    return ps, indptr, ids, np.array(last, dtype=np.int32), rows
+
+
+def test_paged_expansion_worked_example(oracle_mod):
+    """The oracle's page expansion reproduces the hand-worked token rows (a partial last
+    page, an empty sequence, a page shared by two sequences)."""
+    ps, indptr, ids, last, rows = _read_paged_example()
+    tok_indptr, tok_rows = oracle_mod.expand_pages(indptr, ids, last, ps)
+    assert tok_indptr.tolist() == [0] + np.cumsum([len(r) for r in rows]).tolist()
+    assert tok_rows.tolist() == [x for r in rows for x in r]
+
+
+@pytest.mark.parametrize("kv_dtype", [syn.KV_BF16, syn.KV_FP8, syn.KV_MXFP4])
+def test_paged_decode_worked_example(oracle_mod, kv_dtype):
+    """The paged route on the worked example equals the plain route over the hand-written
+    token rows, bit for bit."""
+    ps, indptr, ids, last, rows = _read_paged_example()
+    B = len(rows)
+    case = syn.make_case(B, 0, kv_dtype, seed=61, extra_rows=6 * ps)
+    tok_indptr = np.zeros(B + 1, dtype=np.int32)
+    tok_indptr[1:] = np.cumsum([len(r) for r in rows])
+    tok_rows = np.array([x for r in rows for x in r], dtype=np.int32)
+    o1, l1 = oracle_mod.mla_decode_paged(case.q, kv_dtype, case.kv, case.kv_scales, indptr, ids, last, ps)
+    o2, l2 = oracle_mod.mla_decode(case.q, kv_dtype, case.kv, case.kv_scales, tok_indptr, tok_rows)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    assert np.isneginf(l1[1]).all() and not o1[1].any()  # the empty sequence
+
+
+@pytest.mark.parametrize("kv_dtype", [syn.KV_FP8, syn.KV_MXFP4])
+def test_paged_page_size_one_is_the_plain_route(oracle_mod, kv_dtype):
+    """With one row per page the page table is the token table: the paged route equals
+    oracle_mla_decode on the same arrays (kv_last_page_len is not read)."""
+    case = syn.make_case(4, [7, 0, 30, 1], kv_dtype, seed=62, shuffle=True, extra_rows=5)
+    o1, l1 = oracle_mod.mla_decode_paged(case.q, kv_dtype, case.kv, case.kv_scales, case.kv_indptr,
+                                         case.kv_indices, None, 1)
+    o2, l2 = oracle_mod.mla_decode(case.q, kv_dtype, case.kv, case.kv_scales, case.kv_indptr, case.kv_indices)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_paged_expansion_counts_and_rejects(oracle_mod):
+    """Token count = (pages - 1) * page_size + last_page_len per non-empty sequence; a last
+    page length outside 1..page_size is refused."""
+    rng = np.random.default_rng(63)
+    ps = 16
+    npages = rng.integers(0, 6, size=9)
+    last = np.where(npages > 0, rng.integers(1, ps + 1, size=9), 0).astype(np.int32)
+    indptr = np.zeros(10, dtype=np.int32)
+    indptr[1:] = np.cumsum(npages)
+    ids = rng.permutation(200)[:indptr[-1]].astype(np.int32)
+    tok_indptr, tok_rows = oracle_mod.expand_pages(indptr, ids, last, ps)
+    want = np.where(npages > 0, (npages - 1) * ps + last, 0)
+    assert np.diff(tok_indptr).tolist() == want.tolist()
+    assert all(r // ps in set(ids.tolist()) for r in tok_rows.tolist())
+    bad = last.copy()
+    bad[np.argmax(npages > 0)] = ps + 1
+    with pytest.raises(ValueError):
+        oracle_mod.expand_pages(indptr, ids, bad, ps)

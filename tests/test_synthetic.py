@@ -103,22 +103,24 @@ def test_workload_bytes():
 
 
 @pytest.mark.parametrize("page_size", [1, 2, 8, 13])
-def test_paged_case_follows_the_page_rule(page_size):
+def test_paged_case_page_table(page_size):
+    """The page table of a paged workload: whole pages but the last, a last-page
+    length in 1..page_size, each physical page used once; the generator writes
+    no token-to-row expansion (the oracle expands the pages itself)."""
     lens = [0, 1, page_size, 2 * page_size + 1, 37]
     case, pg = syn.make_paged_case(len(lens), lens, syn.KV_FP8, page_size, seed=9, extra_pages=3)
     assert list(np.diff(case.kv_indptr)) == lens
+    assert case.kv_indices.size == 0 and case.meta["paged"] is pg
     assert case.kv.shape[0] % page_size == 0
     ids = pg["kv_indices"]
     assert len(set(ids.tolist())) == len(ids)  # each physical page used once
+    assert ids.max() < case.kv.shape[0] // page_size
     for b, L in enumerate(lens):
         np_b = pg["kv_indptr"][b + 1] - pg["kv_indptr"][b]
         assert np_b == -(-L // page_size)
         if L:
             assert 1 <= pg["kv_last_page_len"][b] <= page_size
             assert (np_b - 1) * page_size + pg["kv_last_page_len"][b] == L
-        for j in range(L):
-            row = case.kv_indices[case.kv_indptr[b] + j]
-            assert row == ids[pg["kv_indptr"][b] + j // page_size] * page_size + j % page_size
 
 
 def test_mtp_query_layout():
