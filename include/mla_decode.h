@@ -253,9 +253,12 @@ int mla_decode_q8(const void* q, float* q_scale, int q_scale_mode, const void* k
 /*
  * mla_decode_q8_workspace_size: bytes of workspace mla_decode_q8 needs: the
  * split partials of mla_decode_workspace_size(batch, total_kv, kv_dtype,
- * flags), plus 1 KiB of partial maxima for the dynamic scale. For a paged
- * call (page_size > 1) pass flags with MLA_FLAG_FORCE_SPLIT set. Returns 0
- * for invalid arguments (mla_decode_q8 reports them).
+ * flags), plus, for the dynamic scale, 1 KiB of partial maxima placed after
+ * them and never inside the first MLA_WORKSPACE_COUNTER_BYTES bytes (so a
+ * dynamic-scale call whose plan has no split partials still needs
+ * MLA_WORKSPACE_COUNTER_BYTES + 1 KiB, and leaves the counter region zero).
+ * For a paged call (page_size > 1) pass flags with MLA_FLAG_FORCE_SPLIT set.
+ * Returns 0 for invalid arguments (mla_decode_q8 reports them).
  */
 size_t mla_decode_q8_workspace_size(int batch, int64_t total_kv, int kv_dtype, int flags, int q_scale_mode);
 
@@ -334,6 +337,18 @@ size_t mla_decode_mtp_workspace_size(int batch, int total_q, int64_t total_kv, i
  */
 int mla_dequant_debug(int kv_dtype, const void* kv, const void* kv_scales, int64_t rows, int path,
                       float* out_f32, void* stream);
+
+/*
+ * mla_hbm_read_probe: measurement aid, not part of the decode. Streams `bytes`
+ * bytes of device memory at `buf` into LDS with the same LDS-DMA loads (and
+ * cache hint) that gather the cache rows, two workgroups per compute unit,
+ * each reading one contiguous share; nothing is written. Its run time is the
+ * practical HBM read ceiling the decode's effective bandwidth is compared with.
+ *   buf    device memory, 16-byte aligned, caller-owned
+ *   bytes  a multiple of 16 (0 is a no-op)
+ * Returns MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED or MLA_ERR_HIP.
+ */
+int mla_hbm_read_probe(const void* buf, size_t bytes, void* stream);
 
 /* mla_status_string: static, human-readable text for a status code. */
 const char* mla_status_string(int status);

@@ -35,6 +35,7 @@ from ._lib import (  # noqa: F401
     mla_decode_q8_workspace_size,
     mla_decode_workspace_size,
     mla_dequant_debug,
+    mla_hbm_read_probe,
     mla_quantize_q8_debug,
     mla_status_string,
     new_workspace,

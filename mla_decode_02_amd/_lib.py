@@ -26,7 +26,7 @@ Q_SCALE_STATIC, Q_SCALE_DYNAMIC = 0, 1
 
 _EXPORTS = ("mla_decode", "mla_decode_rows", "mla_decode_paged", "mla_decode_q8", "mla_decode_mtp", "mla_decode_plan",
             "mla_decode_workspace_size", "mla_decode_q8_workspace_size", "mla_decode_mtp_workspace_size",
-            "mla_quantize_q8_debug", "mla_dequant_debug", "mla_status_string")
+            "mla_quantize_q8_debug", "mla_dequant_debug", "mla_hbm_read_probe", "mla_status_string")
 
 
 class MlaError(RuntimeError):
@@ -96,6 +96,8 @@ def _load():
     lib.mla_decode_workspace_size.argtypes = [i32, i64, i32, i32]
     lib.mla_dequant_debug.restype = i32
     lib.mla_dequant_debug.argtypes = [i32, vp, vp, i64, i32, vp, vp]
+    lib.mla_hbm_read_probe.restype = i32
+    lib.mla_hbm_read_probe.argtypes = [vp, sz, vp]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_status_string.argtypes = [i32]
     return lib
@@ -497,3 +499,13 @@ def prepare_decode_mtp(q, qo_indptr, kv, kv_scales, kv_indptr, kv_indices, out, 
         return keep
 
     return call
+
+
+def mla_hbm_read_probe(buf):
+    """Enqueue the library's streaming read of a device tensor (measurement aid; see
+    include/mla_decode.h). Its size in bytes must be a multiple of 16."""
+    _need(buf.is_cuda and buf.is_contiguous(), "buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    rc = _lib.mla_hbm_read_probe(_ptr(buf), nbytes, _stream(buf.device))
+    if rc != 0:
+        raise MlaError(rc, "mla_hbm_read_probe")

@@ -1689,6 +1689,25 @@ __global__ __launch_bounds__(64) void dequant_kernel(Params P, int64_t rows, int
     }
 }
 
+// Streaming read of a buffer through the attention kernels' LDS-DMA loads
+// (measurement aid for the practical HBM read ceiling): workgroup w reads the
+// 16-byte vectors [w n / G, (w + 1) n / G) into an LDS ring, each wave one
+// 1 KiB contiguous piece per load, kStreamInFlight loads in flight per wave,
+// with the non-temporal hint the cache-row gathers use. Nothing is written.
+constexpr int kStreamInFlight = 8;
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t* p, int64_t n16) {
+    __shared__ __attribute__((aligned(16))) uint8_t ring[kStreamInFlight * 4096];
+    const int64_t b0 = (int64_t)blockIdx.x * n16 / gridDim.x, b1 = (int64_t)(blockIdx.x + 1) * n16 / gridDim.x;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int it = 0;
+    for (int64_t base = b0; base < b1; base += 256, ++it) {
+        const int64_t k = min(base + (int64_t)threadIdx.x, b1 - 1);
+        dma16(p + 16 * k, lds_addr(ring + (it % kStreamInFlight) * 4096 + 1024 * wave));
+        wait_vmcnt<kStreamInFlight - 1>();
+    }
+    wait_vmcnt<0>();
+}
+
 // Dynamic fp8 query scale, first step: part[i] = max |q| over the query rows
 // of sequences [i B / n, (i + 1) B / n), n = gridDim.x (at most 256). The
 // magnitude of a bf16 value orders like its low 15 bits, so the maximum is
@@ -2002,6 +2021,19 @@ extern "C" int mla_quantize_q8_debug(const void* q, int batch, float* q_scale, i
         if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
     }
     hipLaunchKernelGGL(q8_debug_kernel, dim3(batch), dim3(256), 0, s, P, codes);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+extern "C" int mla_hbm_read_probe(const void* buf, size_t bytes, void* stream) {
+    using namespace mla;
+    if (bytes == 0) return MLA_OK;
+    if (!buf || !aligned(buf, 16) || bytes % 16 != 0) return MLA_ERR_INVALID_ARG;
+    int rc = check_device();
+    if (rc != MLA_OK) return rc;
+    const int64_t n16 = (int64_t)(bytes / 16);
+    const int grid = n16 < 2 * kNumCUs ? (int)n16 : 2 * kNumCUs;  // two workgroups per compute unit
+    hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                       reinterpret_cast<const uint8_t*>(buf), n16);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

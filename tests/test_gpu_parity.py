@@ -135,6 +135,26 @@ def oracle_ref(orc, case, batches=None, sm_scale=1.0 / 24.0):
     return o, l, weighted_abs_v(orc, case, blist, l, sm_scale)
 
 
+def oracle_tokens(orc, case, paged):
+    """The paged workload with the token tables of the oracle's own page expansion
+    (oracle.expand_pages); the input generator writes none."""
+    import dataclasses
+
+    ti, tr = orc.expand_pages(paged["kv_indptr"], paged["kv_indices"], paged["kv_last_page_len"], paged["page_size"])
+    assert np.array_equal(ti, case.kv_indptr), "page table and sequence lengths disagree"
+    return dataclasses.replace(case, kv_indptr=ti, kv_indices=tr)
+
+
+def oracle_ref_paged(orc, case, paged, batches=None, sm_scale=1.0 / 24.0):
+    """Oracle outputs and lse of a paged workload through the oracle's paged route (which
+    expands the pages itself), with the rounding-bound term over the same tokens."""
+    o, l = orc.mla_decode_paged(case.q, case.kv_dtype, case.kv, case.kv_scales, paged["kv_indptr"],
+                                paged["kv_indices"], paged["kv_last_page_len"], paged["page_size"],
+                                sm_scale=sm_scale, batches=batches)
+    blist = list(range(case.batch)) if batches is None else list(batches)
+    return o, l, weighted_abs_v(orc, oracle_tokens(orc, case, paged), blist, l, sm_scale)
+
+
 DTYPES = [syn.KV_BF16, syn.KV_FP8, syn.KV_MXFP4]
 
 
@@ -354,30 +374,34 @@ def test_large_scores_rescale_path(mla, orc, dev):
 # ------------------------------------------------------------------ full-size workloads, sampled
 
 @pytest.mark.parametrize("name", list(syn.WORKLOADS))
-def test_full_size_workload_sampled(mla, orc, dev, name):
-    """Full-size workloads in the benchmark's launch configuration (default plan);
-    the oracle computes a sample of sequences."""
+def test_full_size_workload(mla, orc, dev, name):
+    """Full-size workloads in the benchmark's launch configuration (default plan), every
+    sequence compared with the oracle."""
     case = syn.make_workload(name)
-    got_o, got_l = run_gpu(mla, case, dev)
-    B = case.batch
-    sample = sorted({0, B - 1, B // 2, (7 * B) // 11})
-    check((got_o[sample], got_l[sample]), oracle_ref(orc, case, batches=sample), name)
+    print(f"{name}: plan {mla.mla_decode_plan(case.batch, case.total_kv, case.kv_dtype, 0)}", flush=True)
+    check(run_gpu(mla, case, dev), oracle_ref(orc, case), name)
 
 
-# The rest of the pages' shape grid (batch x kv_len x format), at full size and in the
-# default plan; caches beyond 64K rows repeat a seeded 64K-row pool. The oracle computes
-# a sample of sequences.
-SWEEP_SAMPLE = ["bf16_b256_kv8192", "fp8_b256_kv8192", "mxfp4_b256_kv1024", "mxfp4_b4_kv8192",
-                "bf16_b32_kv8192", "fp8_b256_kv1024"]
+# The pages' whole shape grid (batch {4, 32, 64, 256} x kv_len {1024, 8192} x format), at
+# full size and in the default plan; caches beyond 64K rows repeat a seeded 64K-row pool.
+# Every sequence is compared, except on the 256 x 8192 shapes (2M tokens), where 32
+# sequences spread over the batch are.
+def _sweep_sample(B, L):
+    if B * L <= 256 * 1024:
+        return None
+    return sorted({int(x) for x in np.linspace(0, B - 1, 32)})
 
 
-@pytest.mark.parametrize("name", SWEEP_SAMPLE)
-def test_sweep_shape_sampled(mla, orc, dev, name):
+@pytest.mark.parametrize("name", list(syn.SWEEP))
+def test_sweep_shape(mla, orc, dev, name):
     case = syn.make_workload(name)
+    print(f"{name}: plan {mla.mla_decode_plan(case.batch, case.total_kv, case.kv_dtype, 0)}", flush=True)
     got_o, got_l = run_gpu(mla, case, dev, nan_workspace=False)
-    B = case.batch
-    sample = sorted({0, 1, B - 1, B // 2, (5 * B) // 7})
-    check((got_o[sample], got_l[sample]), oracle_ref(orc, case, batches=sample), name)
+    sample = _sweep_sample(case.batch, int(case.kv_indptr[1]))
+    if sample is None:
+        check((got_o, got_l), oracle_ref(orc, case), name)
+    else:
+        check((got_o[sample], got_l[sample]), oracle_ref(orc, case, batches=sample), name)
 
 
 @pytest.mark.parametrize("name", list(syn.RAGGED))
@@ -387,10 +411,7 @@ def test_mixed_length_workload_sampled(mla, orc, dev, name, hint):
     case = syn.make_workload(name)
     flags = mla.FLAG_MIXED_LENGTHS if hint else 0
     assert mla.mla_decode_plan(case.batch, case.total_kv, case.kv_dtype, flags).mode == (1 if hint else 0)
-    got_o, got_l = run_gpu(mla, case, dev, flags=flags, nan_workspace=False)
-    B = case.batch
-    sample = sorted({0, 1, B // 3, B // 2, B - 1})
-    check((got_o[sample], got_l[sample]), oracle_ref(orc, case, batches=sample), f"{name} hint={hint}")
+    check(run_gpu(mla, case, dev, flags=flags, nan_workspace=False), oracle_ref(orc, case), f"{name} hint={hint}")
 
 
 # ------------------------------------------------------------------ paged cache
@@ -420,15 +441,15 @@ def test_paged_cache(mla, orc, dev, kv_dtype, page_size):
     """Ragged lengths with partial last pages, an empty sequence, shuffled physical pages."""
     lens = [1, 0, page_size, 3 * page_size + 1, 333, 1030]
     case, paged = syn.make_paged_case(len(lens), lens, kv_dtype, page_size, seed=70 + page_size, extra_pages=5)
-    check(run_gpu_paged(mla, case, paged, dev), oracle_ref(orc, case), f"page_size={page_size}")
+    check(run_gpu_paged(mla, case, paged, dev), oracle_ref_paged(orc, case, paged), f"page_size={page_size}")
 
 
 @pytest.mark.parametrize("splits", [1, 5])
 def test_paged_cache_forced_splits(mla, orc, dev, splits):
     lens = [300, 7, 1030]
     case, paged = syn.make_paged_case(3, lens, syn.KV_FP8, 8, seed=80 + splits)
-    check(run_gpu_paged(mla, case, paged, dev, flags=mla.flags_for(splits=splits)), oracle_ref(orc, case),
-          f"splits={splits}")
+    check(run_gpu_paged(mla, case, paged, dev, flags=mla.flags_for(splits=splits)),
+          oracle_ref_paged(orc, case, paged), f"splits={splits}")
 
 
 @pytest.mark.parametrize("kv_dtype", DTYPES)
@@ -442,13 +463,14 @@ def test_page_size_one_is_mla_decode(mla, dev, kv_dtype):
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-@pytest.mark.parametrize("kv_dtype,batch", [(syn.KV_FP8, 64), (syn.KV_MXFP4, 32)])
-def test_paged_full_size_page8_sampled(mla, orc, dev, kv_dtype, batch):
-    """The pages' paged configuration for kv >= 8192: 8-row pages, full size, default split plan."""
-    case, paged = syn.make_paged_case(batch, 8192, kv_dtype, 8, seed=90 + kv_dtype)
-    got_o, got_l = run_gpu_paged(mla, case, paged, dev)
-    sample = sorted({0, batch - 1, batch // 2})
-    check((got_o[sample], got_l[sample]), oracle_ref(orc, case, batches=sample), f"paged {batch}x8192")
+@pytest.mark.parametrize("name", list(syn.PAGED))
+def test_paged_full_size_page8(mla, orc, dev, name):
+    """The pages' paged configuration for kv >= 8192: 8-row pages over shuffled physical
+    pages, full size, default split plan, every sequence compared with the oracle's paged
+    route."""
+    case = syn.make_workload(name)
+    paged = case.meta["paged"]
+    check(run_gpu_paged(mla, case, paged, dev), oracle_ref_paged(orc, case, paged), name)
 
 
 # ---------------------------------------------------------------------------
@@ -637,3 +659,40 @@ def test_merge_in_stage1_two_streams(mla, dev):
             assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16)), f"stream {k} call {i}: out differs"
             assert torch.equal(l.view(torch.int32), ref_l.view(torch.int32)), f"stream {k} call {i}: lse differs"
         assert int(torch.count_nonzero(ws[: mla.WORKSPACE_COUNTER_BYTES])) == 0
+
+
+# ---------------------------------------------------------------------------
+# The mla_decode export itself (the Python binding calls mla_decode_rows)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+@pytest.mark.parametrize("flags_kind", ["default", "one", "merged3", "combine8", "persistent"])
+def test_mla_decode_export_through_ctypes(mla, orc, dev, kv_dtype, flags_kind):
+    """mla_decode called through ctypes with raw device pointers, in every merge form,
+    against the oracle and bit for bit against the binding's call (mla_decode_rows)."""
+    import ctypes
+
+    flags = {"default": 0, "one": mla.flags_for(splits=1), "merged3": mla.flags_for(splits=3),
+             "combine8": mla.flags_for(splits=8),
+             "persistent": mla.flags_for(persistent=True, grid=40)}[flags_kind]
+    case = syn.make_case(5, [640, 1, 0, 333, 2048], kv_dtype, seed=620 + kv_dtype, shuffle=True, extra_rows=9)
+    t = to_dev(case, dev)
+    B = case.batch
+    out = torch.full((B, 16, 512), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((B, 16), float("nan"), dtype=torch.float32, device=dev)
+    ws = new_workspace(mla, case, dev, flags)
+    p = lambda x: None if x is None else ctypes.c_void_p(x.data_ptr())  # noqa: E731
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    lib = ctypes.CDLL(mla.LIB_PATH)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.mla_decode.restype = i32
+    lib.mla_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, ctypes.c_int64, i32, ctypes.c_float, vp,
+                               ctypes.c_size_t, i32, vp]
+    rc = lib.mla_decode(p(t["q"]), p(t["kv"]), p(t["kv_scales"]), p(t["kv_indptr"]), p(t["kv_indices"]), p(out),
+                             p(lse), B, case.total_kv, kv_dtype, ctypes.c_float(0.0), p(ws),
+                             0 if ws is None else ws.numel(), flags, stream)
+    assert rc == 0, mla.mla_status_string(rc)
+    torch.cuda.synchronize()
+    got = (out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64))
+    check(got, oracle_ref(orc, case), f"mla_decode export {flags_kind}")
+    again = run_gpu(mla, case, dev, flags=flags)
+    assert np.array_equal(got[0], again[0]) and np.array_equal(got[1], again[1])
