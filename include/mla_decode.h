@@ -165,6 +165,29 @@ int mla_decode(const void* q, const void* kv, const void* kv_scales, const int32
                void* stream);
 
 /*
+ * mla_decode_noalloc: mla_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). It takes no workspace: the arrival counters and split
+ * partials of its plan live in a fixed device array inside the library,
+ * MLA_NOALLOC_SCRATCH_BYTES bytes per device, which each device holds from its
+ * first such call until the process ends. The call itself allocates and frees
+ * nothing. The first call on a device looks the array up and enqueues one small
+ * fill kernel that zeroes its counter region.
+ *   arguments, outputs, results and errors as for mla_decode (without
+ *   workspace / workspace_bytes); additionally MLA_ERR_WORKSPACE_TOO_SMALL when
+ *   the plan's workspace (mla_decode_workspace_size) exceeds
+ *   MLA_NOALLOC_SCRATCH_BYTES, checked on the host before any device call.
+ * Every call on one device shares that device's array and leaves the last
+ * call's partials in it (its counters zero): calls that may overlap on one
+ * device -- two streams, or two host threads -- race and must be ordered by the
+ * caller (one stream, or events).
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (32u << 20) /* 32 MiB: 64 KiB of counters and up to 1020 partial slots */
+int mla_decode_noalloc(const void* q, const void* kv, const void* kv_scales, const int32_t* kv_indptr,
+                       const int32_t* kv_indices, void* out, float* lse, int batch, int64_t total_kv, int kv_dtype,
+                       float sm_scale, int flags, void* stream);
+
+/*
  * mla_decode_rows: mla_decode with the number of rows the cache buffer holds
  * (for callers that can allocate their cache contiguously per sequence, as
  * the pages' benchmark does with kv_indices = arange; submission 593653,

@@ -28,6 +28,7 @@ from ._lib import (  # noqa: F401
     flags_for,
     mla_decode,
     mla_decode_mtp,
+    mla_decode_noalloc,
     mla_decode_mtp_workspace_size,
     mla_decode_paged,
     mla_decode_plan,

@@ -24,7 +24,7 @@ WORKSPACE_COUNTER_BYTES = 65536  # leading workspace bytes that hold the arrival
 FLAG_SPLITS_SHIFT, FLAG_GRID_SHIFT = 8, 16
 Q_SCALE_STATIC, Q_SCALE_DYNAMIC = 0, 1
 
-_EXPORTS = ("mla_decode", "mla_decode_rows", "mla_decode_paged", "mla_decode_q8", "mla_decode_mtp", "mla_decode_plan",
+_EXPORTS = ("mla_decode", "mla_decode_rows", "mla_decode_noalloc", "mla_decode_paged", "mla_decode_q8", "mla_decode_mtp", "mla_decode_plan",
             "mla_decode_workspace_size", "mla_decode_q8_workspace_size", "mla_decode_mtp_workspace_size",
             "mla_quantize_q8_debug", "mla_dequant_debug", "mla_hbm_read_probe", "mla_status_string")
 
@@ -73,6 +73,8 @@ def _load():
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
     lib.mla_decode.restype = i32
     lib.mla_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, ctypes.c_float, vp, sz, i32, vp]
+    lib.mla_decode_noalloc.restype = i32
+    lib.mla_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, ctypes.c_float, i32, vp]
     lib.mla_decode_rows.restype = i32
     lib.mla_decode_rows.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i64, i32, ctypes.c_float, vp, sz, i32, vp]
     lib.mla_decode_paged.restype = i32
@@ -211,6 +213,31 @@ def mla_decode(q, kv, kv_scales, kv_indptr, kv_indices, out, lse=None, *, total_
     if rc != 0:
         raise MlaError(rc, "mla_decode")
     return workspace
+
+
+def mla_decode_noalloc(q, kv, kv_scales, kv_indptr, kv_indices, out, lse=None, *, total_kv: int, kv_dtype: int,
+                       sm_scale: float = 0.0, flags: int = 0):
+    """Enqueue mla_decode_noalloc (see include/mla_decode.h): mla_decode without a
+    workspace, its partials in the library's fixed per-device scratch array. Nothing is
+    allocated, here or in the library. Calls that may overlap on one device race."""
+    B = int(kv_indptr.shape[0]) - 1
+    _need(q.is_cuda and q.dtype == torch.bfloat16 and q.is_contiguous() and tuple(q.shape) == (B, NUM_HEADS, QK_DIM),
+          "q must be contiguous bf16 [batch, 16, 576]")
+    _check_kv(kv, kv_scales, kv_dtype)
+    _need(kv_indptr.is_cuda and kv_indptr.dtype == torch.int32 and kv_indptr.is_contiguous(),
+          "kv_indptr must be a contiguous device int32 tensor")
+    _need(kv_indices.is_cuda and kv_indices.dtype == torch.int32 and kv_indices.is_contiguous()
+          and kv_indices.numel() >= total_kv, "kv_indices must be a contiguous device int32 tensor of >= total_kv")
+    _need(out.is_cuda and out.dtype == torch.bfloat16 and out.is_contiguous() and tuple(out.shape) == (B, NUM_HEADS, V_DIM),
+          "out must be contiguous bf16 [batch, 16, 512]")
+    if lse is not None:
+        _need(lse.is_cuda and lse.dtype == torch.float32 and lse.is_contiguous() and tuple(lse.shape) == (B, NUM_HEADS),
+              "lse must be contiguous fp32 [batch, 16]")
+    rc = _lib.mla_decode_noalloc(_ptr(q), _ptr(kv), _ptr(kv_scales), _ptr(kv_indptr), _ptr(kv_indices), _ptr(out),
+                                 _ptr(lse), B, int(total_kv), int(kv_dtype), float(sm_scale), int(flags),
+                                 _stream(q.device))
+    if rc != 0:
+        raise MlaError(rc, "mla_decode_noalloc")
 
 
 def _kv_rows(kv, kv_rows):

@@ -44,6 +44,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "mla_decode.h"
 #include "mla_plan.h"
@@ -1831,6 +1832,51 @@ static int launch(const mla_plan_info& plan, const Params& P, hipStream_t stream
 
 namespace mla {
 
+// ---------------------------------------------------------------------------
+// Scratch for mla_decode_noalloc: the arrival counters and split partials of
+// its plans live in this file-scope device array instead of a caller
+// workspace. Each device the library runs on holds its own copy (zero when
+// the code object loads) until the process ends. In host code the array's
+// name only stands in for the symbol: its device address is taken once per
+// device with hipGetSymbolAddress (that device current) and cached, and only
+// that address is ever passed to kernels.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0 && kScratchBytes > kCounterBytes, "scratch holds the counters and partials");
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex scratch_mu;
+static void* scratch_ptr[kMaxDevices];  // device address of `scratch` per device (nullptr: not set up yet)
+
+__global__ __launch_bounds__(256) void clear_u32_kernel(uint32_t* p, int n) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
+// The current device's scratch address. The first call on a device looks the
+// symbol up and clears the arrival-counter region with a fill kernel on
+// `stream` (the array starts zero; this makes that explicit, and every call
+// leaves the region zero again). Returns MLA_OK or MLA_ERR_HIP.
+static int scratch_for_current_device(hipStream_t stream, void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLA_ERR_HIP;
+        hipLaunchKernelGGL(clear_u32_kernel, dim3(16), dim3(256), 0, stream, reinterpret_cast<uint32_t*>(p),
+                           (int)(kCounterBytes / sizeof(uint32_t)));
+        if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return MLA_OK;
+}
+
+}  // namespace mla
+
+namespace mla {
+
 // Shared body of mla_decode (page size 1), mla_decode_paged and mla_decode_q8
 // (q_mode < 0: bf16 query; else MLA_Q_SCALE_*, with q_scale).
 // Several query tokens per sequence (mla_decode_mtp): qo_indptr / uni_q /
@@ -1936,6 +1982,25 @@ extern "C" int mla_decode(const void* q, const void* kv, const void* kv_scales, 
                           void* stream) {
     return mla::decode_impl(q, kv, kv_scales, kv_indptr, kv_indices, nullptr, 1, out, lse, batch, total_kv, kv_dtype,
                             sm_scale, workspace, workspace_bytes, flags, stream);
+}
+
+extern "C" int mla_decode_noalloc(const void* q, const void* kv, const void* kv_scales, const int32_t* kv_indptr,
+                                  const int32_t* kv_indices, void* out, float* lse, int batch, int64_t total_kv,
+                                  int kv_dtype, float sm_scale, int flags, void* stream) {
+    using namespace mla;
+    mla_plan_info plan;
+    int rc = make_plan(batch, total_kv, kv_dtype, flags, &plan);
+    if (rc != MLA_OK) return rc;
+    if (plan.workspace_bytes > kScratchBytes) return MLA_ERR_WORKSPACE_TOO_SMALL;  // before any device call
+    void* ws = nullptr;
+    if (plan.workspace_bytes > 0 && batch > 0) {
+        rc = check_device();
+        if (rc != MLA_OK) return rc;
+        rc = scratch_for_current_device(reinterpret_cast<hipStream_t>(stream), &ws);
+        if (rc != MLA_OK) return rc;
+    }
+    return decode_impl(q, kv, kv_scales, kv_indptr, kv_indices, nullptr, 1, out, lse, batch, total_kv, kv_dtype,
+                       sm_scale, ws, ws ? kScratchBytes : 0, flags, stream);
 }
 
 extern "C" int mla_decode_rows(const void* q, const void* kv, const void* kv_scales, const int32_t* kv_indptr,

@@ -37,7 +37,8 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("mla_decode", "mla_decode_rows", "mla_decode_paged", "mla_decode_q8", "mla_decode_mtp", "mla_decode_plan",
               "mla_decode_workspace_size", "mla_decode_q8_workspace_size", "mla_decode_mtp_workspace_size",
-              "mla_quantize_q8_debug", "mla_dequant_debug", "mla_hbm_read_probe", "mla_status_string"):
+              "mla_quantize_q8_debug", "mla_dequant_debug", "mla_hbm_read_probe", "mla_decode_noalloc",
+              "mla_status_string"):
         assert n in names
 
 
@@ -55,6 +56,23 @@ def test_hbm_read_probe_validation(raw_lib):
     assert f(None, 64, None) == -1         # null buffer
     assert f(ctypes.c_void_p(24), 64, None) == -1   # misaligned
     assert f(ctypes.c_void_p(256), 40, None) == -1  # not a multiple of 16
+
+
+def test_noalloc_refuses_plans_beyond_its_scratch(raw_lib, mla):
+    """mla_decode_noalloc refuses a plan whose workspace exceeds its fixed scratch before any
+    device call (so this runs without a GPU)."""
+    f = raw_lib.mla_decode_noalloc
+    f.restype = ctypes.c_int
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    f.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, ctypes.c_int64, i32, ctypes.c_float, i32, vp]
+    A = ctypes.c_void_p(256)
+    limit = 32 << 20
+    flags = mla.flags_for(splits=2)
+    assert mla.mla_decode_workspace_size(1100, 1100 * 2048, 1, flags) > limit
+    assert f(A, A, A, A, A, A, None, 1100, 1100 * 2048, 1, 0.0, flags, None) == -3
+    assert mla.mla_decode_workspace_size(500, 500 * 2048, 1, flags) <= limit
+    assert f(A, A, A, A, A, A, None, 0, 0, 1, 0.0, 0, None) == 0        # empty batch: a no-op
+    assert f(A, A, A, A, A, A, None, -1, 0, 1, 0.0, 0, None) == -1      # invalid sizes
 
 
 def test_status_strings(mla):
