@@ -120,19 +120,40 @@ struct Params {
 
 // ---------------------------------------------------------------------------
 // Cache formats: staging layout of one 16-row tile in LDS. The gather of a
-// tile is split in two halves (hi = 0, 1), each issued by one wave; every
-// lane of a half fetches parts of the row of token r = lane % 16, so the
-// issuing wave reads one row index per step.
-//   codes: load u (0 <= u < kCodeLoads) is one 16-byte DMA per lane; lane
-//          (G, r) = (lane / 16, lane % 16) brings bytes 64u + 16G .. +15 of
-//          tile row r to tile + 1024u + 16 lane. Half hi issues u = hi, hi+2, ...
-//   MXFP4: the 32 RoPE bytes of each row (bytes 256..287) are one 16-byte DMA
-//          on lanes 0..31 (lane (c, r) brings bytes 256 + 16c .. +15 of row r
-//          to tile + kRopeOff + 16 lane); the 18 e8m0 codes of each row are
-//          two-byte DMAs, load v bringing codes 2p, 2p+1, p = 4v + G, of row
-//          r into the low half of the dword at tile + kScaleOff + 256 v + 4 lane
-//          (load 2 on lanes 0..15 only). Half 0 issues codes 0, 2 and scale
-//          loads 0, 2; half 1 codes 1, 3, the RoPE load and scale load 1.
+// tile is split in two halves (hf = 0, 1), each issued by one wave; every
+// LDS-DMA load writes 64 consecutive 16-byte slots of the tile, lane L of load
+// v at slot 64 v + L. Chunk c of tile row r (bytes 16 c .. 16 c + 15 of that
+// cache row) sits in slot slot(r, c).
+//   bf16 and fp8: each group of 8 lanes of a load fetches one whole 128-byte
+//     run of cache memory, so the HBM requests of every load are whole lines
+//     (a row gather that reads 64-byte pieces of 16 rows per load streams
+//     about a third slower); within its run a row's chunks are permuted by an
+//     XOR with a function of the row, and the runs are placed so that the 16
+//     rows of any chunk lie in 16 different 16-byte bank groups modulo 256
+//     bytes (8 different ones in each half of 8 rows): the score operand reads
+//     (one chunk of 16 rows) and the transposed value reads stay free of bank
+//     conflicts.
+//     bf16 (72 chunks per row: 9 runs, the 9 lines of a 1152-byte row): load
+//       v = 2k + h brings run k of rows 8h .. 8h + 7, row 8h + (m ^ h) on
+//       lanes 8m .. 8m + 7; half hf issues the loads with h = hf, so each lane
+//       fetches from one row.
+//       slot(r, c) = 64 (2 (c / 8) + r / 8) + 8 ((r % 8) ^ (r / 8)) + ((c % 8) ^ (r % 8))
+//     fp8 (36 chunks per row): rows 2p and 2p + 1 form a pair of 72 chunks,
+//       pair chunk q = c + 36 (r % 2), i.e. 9 runs that are whole lines when
+//       the pair's first row has an even index in a contiguous cache. Load v
+//       brings run v of all 8 pairs, pair p on lanes 8 sigma(p) ..,
+//       sigma(p) = 2 (p % 4) + p / 4; half hf issues the loads v = hf, hf + 2,
+//       .., and each lane fetches from the two rows of its pair.
+//       slot(r, c) = 64 (q / 8) + 8 sigma(p) + ((q % 8) ^ (p % 4)),  p = r / 2
+//   MXFP4: lane (G, r) = (lane / 16, lane % 16) of code load u (0 <= u < 4)
+//     brings bytes 64u + 16G .. +15 of tile row r to tile + 1024u + 16 lane;
+//     the 32 RoPE bytes of each row (bytes 256..287) are one 16-byte DMA
+//     on lanes 0..31 (lane (c, r) brings bytes 256 + 16c .. +15 of row r
+//     to tile + kRopeOff + 16 lane); the 18 e8m0 codes of each row are
+//     two-byte DMAs, load v bringing codes 2p, 2p+1, p = 4v + G, of row
+//     r into the low half of the dword at tile + kScaleOff + 256 v + 4 lane
+//     (load 2 on lanes 0..15 only). Half 0 issues codes 0, 2 and scale
+//     loads 0, 2; half 1 codes 1, 3, the RoPE load and scale load 1.
 // ---------------------------------------------------------------------------
 template <int KV>
 struct Fmt;
@@ -219,6 +240,19 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
                  : "=&s"(save) : "v"(g), "s"(lds) : "memory");
 }
+// The same from g + OFF (an immediate, 0 <= OFF < 4096) with the
+// non-temporal hint (nt): cache rows are read once per call, so they are
+// streamed through the caches rather than kept. The instruction offset of an
+// LDS-DMA load moves its LDS destination as well as its global address
+// (checked on gfx950), so m0 is set OFF below the destination; every caller's
+// destination lies at least OFF bytes into LDS.
+template <int OFF>
+__device__ __forceinline__ void dma16nt(const void* g, uint32_t lds) {
+    static_assert(OFF >= 0 && OFF < 4096, "global load offsets are 12-bit");
+    uint32_t save;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off offset:%3 nt\n\ts_mov_b32 m0, %0"
+                 : "=&s"(save) : "v"(g), "s"(lds - (uint32_t)OFF), "n"(OFF) : "memory");
+}
 __device__ __forceinline__ void dma2(const void* g, uint32_t lds) {
     uint32_t save;
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_ushort %1, off\n\ts_mov_b32 m0, %0"
@@ -240,17 +274,65 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
-// The LDS-DMA loads of half `hi` of one tile (layout above). `row` is the
-// cache row of token lane % 16 of the tile; `tile` its LDS staging area.
-template <int KV, int HI>
-__device__ __forceinline__ void issue_half(const Params& P, int64_t row, uint8_t* tile, int lane) {
-    constexpr int RB = Fmt<KV>::kRowBytes;
-    const int G = lane >> 4;
-    const uint8_t* src = P.kv + row * RB + 16 * G;
-    if constexpr (KV != MLA_KV_MXFP4) {
-#pragma unroll
-        for (int u = HI; u < Fmt<KV>::kCodeLoads; u += 2) dma16(src + 64 * u, lds_addr(tile + 1024 * u));
+// Tile rows whose cache rows lane `lane` fetches when issuing half hf of a
+// tile: (first, second) -- the two rows of its pair (fp8), or its one row
+// twice (bf16, MXFP4).
+template <int KV>
+__device__ __forceinline__ int2 lane_tile_rows(int lane, int hf) {
+    if constexpr (KV == MLA_KV_BF16) {
+        const int r = 8 * hf + ((lane >> 3) ^ hf);
+        return make_int2(r, r);
+    } else if constexpr (KV == MLA_KV_FP8_E4M3) {
+        const int m = lane >> 3, p = (m >> 1) + 4 * (m & 1);
+        return make_int2(2 * p, 2 * p + 1);
     } else {
+        return make_int2(lane & 15, lane & 15);
+    }
+}
+
+// The LDS-DMA loads of half HI of one tile (layout above). ra / rb are the
+// cache rows of this lane's tile rows lane_tile_rows(lane, HI); `tile` is
+// the tile's LDS staging area.
+template <int KV, int HI>
+__device__ __forceinline__ void issue_half(const Params& P, int64_t ra, int64_t rb, uint8_t* tile, int lane) {
+    if constexpr (KV == MLA_KV_BF16) {
+        // load 2k + HI: run k (bytes 128k ..) of the lane's row, its chunk 8k + jj
+        const int r = 8 * HI + ((lane >> 3) ^ HI), jj = (lane & 7) ^ (r & 7);
+        const uint8_t* src = P.kv + ra * Fmt<KV>::kRowBytes + 16 * jj;
+        dma16nt<0>(src, lds_addr(tile + 1024 * (0 + HI)));
+        dma16nt<128>(src, lds_addr(tile + 1024 * (2 + HI)));
+        dma16nt<256>(src, lds_addr(tile + 1024 * (4 + HI)));
+        dma16nt<384>(src, lds_addr(tile + 1024 * (6 + HI)));
+        dma16nt<512>(src, lds_addr(tile + 1024 * (8 + HI)));
+        dma16nt<640>(src, lds_addr(tile + 1024 * (10 + HI)));
+        dma16nt<768>(src, lds_addr(tile + 1024 * (12 + HI)));
+        dma16nt<896>(src, lds_addr(tile + 1024 * (14 + HI)));
+        dma16nt<1024>(src, lds_addr(tile + 1024 * (16 + HI)));
+    } else if constexpr (KV == MLA_KV_FP8_E4M3) {
+        // load v: pair chunks 8v + jj; below 36 they are chunks of the pair's
+        // first row, from 36 on chunks q - 36 of its second row
+        const int m = lane >> 3, p = (m >> 1) + 4 * (m & 1), jj = (lane & 7) ^ (p & 3);
+        const uint8_t* a = P.kv + ra * Fmt<KV>::kRowBytes + 16 * jj;
+        const uint8_t* b = P.kv + rb * Fmt<KV>::kRowBytes + 16 * jj;
+        if constexpr (HI == 0) {
+            dma16nt<0>(a, lds_addr(tile + 1024 * 0));    // first row, chunk jj
+            dma16nt<256>(a, lds_addr(tile + 1024 * 2));  // first row, chunk 16 + jj
+            // pair chunk 32 + jj: first row chunk 32 + jj (jj < 4), second row chunk jj - 4 (jj >= 4;
+            // jj >= 4 exactly when lane bit 2 is set, the XOR touching only bits 0-1)
+            dma16nt<0>((lane & 4) ? b - 64 : a + 512, lds_addr(tile + 1024 * 4));
+            dma16nt<192>(b, lds_addr(tile + 1024 * 6));  // second row, chunk 12 + jj
+            dma16nt<448>(b, lds_addr(tile + 1024 * 8));  // second row, chunk 28 + jj
+        } else {
+            dma16nt<128>(a, lds_addr(tile + 1024 * 1));  // first row, chunk 8 + jj
+            dma16nt<384>(a, lds_addr(tile + 1024 * 3));  // first row, chunk 24 + jj
+            dma16nt<64>(b, lds_addr(tile + 1024 * 5));   // second row, chunk 4 + jj
+            dma16nt<320>(b, lds_addr(tile + 1024 * 7));  // second row, chunk 20 + jj
+        }
+    } else {
+        constexpr int RB = Fmt<KV>::kRowBytes;
+        const int G = lane >> 4;
+        const int64_t row = ra;
+        const uint8_t* src = P.kv + row * RB + 16 * G;
         dma16(src + 64 * HI, lds_addr(tile + 1024 * HI));
         dma16(src + 64 * (HI + 2), lds_addr(tile + 1024 * (HI + 2)));
         const uint8_t* sc = reinterpret_cast<const uint8_t*>(P.kv_scales) + row * MLA_MX_SCALES_PER_ROW + 2 * G;
@@ -265,9 +347,20 @@ __device__ __forceinline__ void issue_half(const Params& P, int64_t row, uint8_t
 }
 
 template <int KV>
-__device__ __forceinline__ void issue_half(const Params& P, int64_t row, uint8_t* tile, int lane, int hi) {
-    if (hi) issue_half<KV, 1>(P, row, tile, lane);
-    else issue_half<KV, 0>(P, row, tile, lane);
+__device__ __forceinline__ void issue_half(const Params& P, int64_t ra, int64_t rb, uint8_t* tile, int lane, int hi) {
+    if (hi) issue_half<KV, 1>(P, ra, rb, tile, lane);
+    else issue_half<KV, 0>(P, ra, rb, tile, lane);
+}
+
+// Byte offset, within a tile, of chunk c of tile row r (bf16, fp8; layout above).
+template <int KV>
+__device__ __forceinline__ int chunk_offset(int r, int c) {
+    if constexpr (KV == MLA_KV_BF16) {
+        return 16 * (64 * (2 * (c >> 3) + (r >> 3)) + 8 * ((r & 7) ^ (r >> 3)) + ((c & 7) ^ (r & 7)));
+    } else {
+        const int p = r >> 1, q = c + 36 * (r & 1);
+        return 16 * (64 * (q >> 3) + 8 * (2 * (p & 3) + (p >> 2)) + ((q & 7) ^ (p & 3)));
+    }
 }
 
 // e8m0 code in bits sh..sh+7 of w -> fp32 scale operand of the scaled
@@ -302,9 +395,12 @@ template <int KV>
 __device__ __forceinline__ bf16x8 qk_operand(const uint8_t* step, int t, int ks, int lane) {
     const uint8_t* tile = step + t * Fmt<KV>::kTileBytes;
     if constexpr (KV == MLA_KV_BF16) {
-        return *reinterpret_cast<const bf16x8*>(tile + 1024 * ks + 16 * lane);
+        // dims 8c .. 8c + 7 are chunk c = 4 ks + G of row r
+        return *reinterpret_cast<const bf16x8*>(tile + chunk_offset<KV>(lane & 15, 4 * ks + (lane >> 4)));
     } else if constexpr (KV == MLA_KV_FP8_E4M3) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(tile + 1024 * (ks >> 1) + 16 * lane);
+        // dims 16c + 8 (ks % 2) .. +7 are half ks % 2 of chunk c = 4 (ks / 2) + G of row r
+        const u32x4 w =
+            *reinterpret_cast<const u32x4*>(tile + chunk_offset<KV>(lane & 15, 4 * (ks >> 1) + (lane >> 4)));
         return (ks & 1) ? fp8x8_to_bf16(w[2], w[3]) : fp8x8_to_bf16(w[0], w[1]);
     } else {
         // e8m0 block k of row r is byte k & 1 of the dword at scale index 16 (k / 2) + r
@@ -484,8 +580,8 @@ __device__ __forceinline__ f32x4 qk_partial(const uint8_t* step, const QOp (&qB)
         QOp k;
         if constexpr (__is_same(QOp, long)) {
             static_assert(KV == MLA_KV_FP8_E4M3, "fp8 score operands need the fp8 cache");
-            k = *reinterpret_cast<const long*>(step + t * Fmt<KV>::kTileBytes + 1024 * (ks >> 1) + 16 * lane +
-                                               8 * (ks & 1));
+            k = *reinterpret_cast<const long*>(step + t * Fmt<KV>::kTileBytes +
+                                               chunk_offset<KV>(lane & 15, 4 * (ks >> 1) + (lane >> 4)) + 8 * (ks & 1));
         } else {
             k = qk_operand<KV>(step, t, ks, lane);
         }
@@ -686,55 +782,61 @@ struct PvRaw<MLA_KV_MXFP4> {
     f32x4 s0[kWaveBlocks / 2], s1[kWaveBlocks / 2];
 };
 
-// Per-lane byte offset (within a staged step) of this wave's value reads; the
-// per-block part is a compile-time constant added in pv_load, so the LDS reads
-// take it as an immediate offset.
+// Per-lane byte offsets (within a staged step) of this wave's value reads,
+// taken once per workgroup; pv_load adds the step base and a compile-time
+// per-block part, which the LDS reads take as an immediate offset.
 //   fp8 / MXFP4 (ds_read_b64_tr_b8): row i of the transposed 8 x 16-byte block
 //     is token tau(G, i); lanes 2i and 2i+1 supply its bytes 0-7 and 8-15.
-//     Block c's 16 (fp8) or 32 (MXFP4, two codes a byte) columns are bytes
-//     16 (c % 4) .. +15 of code load c / 4.
+//     Block c's 16 (fp8) or 32 (MXFP4, two codes a byte) columns are chunk c
+//     of the token's row: fp8 a[j] for block 8 wave + j (the row's XOR and
+//     pair placement make these 8 separate offsets); MXFP4 a[0] + 256 j.
 //   bf16 (ds_read_b64_tr_b16, two reads): row i of each transposed 4 x 16
-//     block is token tau(G, i) (first read) or tau(G, 4 + i) (second read);
-//     lanes 4i..4i+3 supply its 32 bytes.
+//     block is token tau(G, i) (first read, tile 0) or tau(G, 4 + i) (second
+//     read, the same row of tile 1); lanes 4i..4i+3 supply its 32 bytes, the
+//     chunks 2c and 2c + 1 of block c = 8 wave + j: a[j % 4] + 2048 (j / 4).
 template <int KV>
-__device__ __forceinline__ int pv_lane_offset(int lane, int wave) {
+struct PvOff {
+    int a[KV == MLA_KV_FP8_E4M3 ? 8 : KV == MLA_KV_BF16 ? 4 : 1];
+};
+
+template <int KV>
+__device__ __forceinline__ PvOff<KV> pv_lane_offsets(int lane, int wave) {
     const int G = lane >> 4, j = lane & 15;
+    PvOff<KV> o;
     if constexpr (KV == MLA_KV_FP8_E4M3) {
-        const int tk = tau(G, j >> 1);
-        return (tk >> 4) * Fmt<KV>::kTileBytes + 16 * (tk & 15) + 8 * (j & 1) + 2048 * wave;
+        const int tk = tau(G, j >> 1), t = tk >> 4, r = tk & 15;
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+            o.a[b] = t * Fmt<KV>::kTileBytes + chunk_offset<KV>(r, 8 * wave + b) + 8 * (j & 1);
     } else if constexpr (KV == MLA_KV_BF16) {
-        const int i = j >> 2, q = j & 3;
-        const int t0 = tau(G, i);
-        return (t0 >> 4) * Fmt<KV>::kTileBytes + 16 * (t0 & 15) + 256 * (q >> 1) + 8 * (q & 1) + 4096 * wave;
+        const int i = j >> 2, q = j & 3, r = 4 * G + i;
+        // chunk 2 (8 wave + b) + q / 2 of row r: 2048 (b / 4) apart for b and b + 4
+#pragma unroll
+        for (int b = 0; b < 4; ++b) o.a[b] = chunk_offset<KV>(r, 2 * (8 * wave + b) + (q >> 1)) + 8 * (q & 1);
     } else {
         const int tk = tau(G, j >> 1);
-        return (tk >> 4) * Fmt<KV>::kTileBytes + 16 * (tk & 15) + 8 * (j & 1) + 1024 * wave;
+        o.a[0] = (tk >> 4) * Fmt<KV>::kTileBytes + 16 * (tk & 15) + 8 * (j & 1) + 1024 * wave;
     }
+    return o;
 }
 
 template <int KV>
-__device__ __forceinline__ void pv_load(const uint8_t* step, const float* fs, int lane_off, int lane, int wave,
-                                        PvRaw<KV>& v) {
-    const uint8_t* vb = step + lane_off;
+__device__ __forceinline__ void pv_load(const uint8_t* step, const float* fs, const PvOff<KV>& off, int lane,
+                                        int wave, PvRaw<KV>& v) {
     if constexpr (KV == MLA_KV_FP8_E4M3) {
-        // block 8 wave + j: + 1024 (j / 4) + 256 (j % 4)
 #pragma unroll
         for (int j = 0; j < kWaveBlocks; ++j)
-            v.w[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vb + 1024 * (j >> 2) + 256 * (j & 3)));
+            v.w[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(step + off.a[j]));
     } else if constexpr (KV == MLA_KV_BF16) {
-        // block 8 wave + j: + 1024 (j / 2) + 512 (j % 2); the second read covers tokens tau(G, 4 + i),
-        // 16 tokens (one tile) or 12 rows further on
-        const int G = lane >> 4, i = (lane & 15) >> 2;
-        const int t0 = tau(G, i), t1 = tau(G, 4 + i);
-        const int d1 = ((t1 >> 4) - (t0 >> 4)) * Fmt<KV>::kTileBytes + 16 * ((t1 & 15) - (t0 & 15));
 #pragma unroll
         for (int j = 0; j < kWaveBlocks; ++j) {
-            const uint8_t* a0 = vb + 1024 * (j >> 1) + 512 * (j & 1);
+            const uint8_t* a0 = step + off.a[j & 3] + 2048 * (j >> 2);
             v.lo[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0);
-            v.hi[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + d1));
+            v.hi[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + Fmt<KV>::kTileBytes));
         }
     } else {
         // MX block b = 4 wave + j: codes + 256 j; scales fs[t][b][4G..4G+3] (as f32x4: 4 (16 t + b) + G)
+        const uint8_t* vb = step + off.a[0];
         const int G = lane >> 4;
         const f32x4* f = reinterpret_cast<const f32x4*>(fs) + 16 * wave + G;
 #pragma unroll
@@ -899,13 +1001,15 @@ template <int KV>
 __device__ __forceinline__ void issue_early(const Params& P, uint8_t* smem, int64_t first, int n) {
     using L = Layout<KV>;
     constexpr int R = Fmt<KV>::kRing, D = R - 1;
-    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r = lane & 15;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int tile = wave & 1, hf = wave >> 1;
+    const int2 tr = lane_tile_rows<KV>(lane, hf);
     const int nsteps = (n + kStepTokens - 1) / kStepTokens;
 #pragma unroll
     for (int d = 0; d < D; ++d)
         if (d < nsteps)
-            issue_half<KV>(P, early_row(P, first, d * kStepTokens + kTile * tile + r, n),
+            issue_half<KV>(P, early_row(P, first, d * kStepTokens + kTile * tile + tr.x, n),
+                           early_row(P, first, d * kStepTokens + kTile * tile + tr.y, n),
                            smem + (d % R) * L::kStepBytes + tile * Fmt<KV>::kTileBytes, lane, hf);
 }
 
@@ -1073,7 +1177,8 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
     int32_t* idx = reinterpret_cast<int32_t*>(smem + L::kIdxOff);
     f32x4* sbuf = reinterpret_cast<f32x4*>(smem + L::kSbufOff);
     float* fs_buf = reinterpret_cast<float*>(smem + L::kFsOff);
-    const int pv_off = pv_lane_offset<KV>(lane, wave);
+    const PvOff<KV> pv_off = pv_lane_offsets<KV>(lane, wave);
+    const int2 trows = lane_tile_rows<KV>(lane, hf);  // this lane's tile rows when it issues its half
 
     // The first index window (unless the caller's LDS-DMA of a guessed window
     // already holds it) and the query are in flight together here.
@@ -1133,8 +1238,10 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
         // This wave's half of tile `tile` of step i into ring slot i % R; tokens
         // at or beyond n re-read the last valid row (always in bounds).
         auto issue_step = [&](int i) {
-            const int64_t row = idx[min(i * kStepTokens + kTile * tile + r, n - 1)];
-            issue_half<KV>(P, row, smem + (i % R) * L::kStepBytes + tile * Fmt<KV>::kTileBytes, lane, hf);
+            const int j0 = i * kStepTokens + kTile * tile;
+            const int64_t ra = idx[min(j0 + trows.x, n - 1)];
+            const int64_t rb = trows.y == trows.x ? ra : (int64_t)idx[min(j0 + trows.y, n - 1)];
+            issue_half<KV>(P, ra, rb, smem + (i % R) * L::kStepBytes + tile * Fmt<KV>::kTileBytes, lane, hf);
         };
         // This wave's partial scores of step i, for exchange buffer i % 2.
         // (MXFP4: also converts the step's value-block scales into buffer i % 2.)
@@ -1158,8 +1265,10 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
 #pragma unroll
             for (int d = 0; d < D; ++d)
                 if (d < nsteps) {
-                    const int j = d * kStepTokens + kTile * tile + r;
-                    keep = keep && (int64_t)idx[min(j, n - 1)] == early_row(P, early_first, j, n);
+                    const int ja = d * kStepTokens + kTile * tile + trows.x;
+                    const int jb = d * kStepTokens + kTile * tile + trows.y;
+                    keep = keep && (int64_t)idx[min(ja, n - 1)] == early_row(P, early_first, ja, n) &&
+                           (int64_t)idx[min(jb, n - 1)] == early_row(P, early_first, jb, n);
                 }
             keep = __all(keep);
         }
@@ -1634,9 +1743,13 @@ __global__ __launch_bounds__(64) void dequant_kernel(Params P, int64_t rows, int
     const int n = (int)min<int64_t>(kStepTokens, rows - row0);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        const int64_t row = row0 + min(kTile * t + r, n - 1);
-        issue_half<KV, 0>(P, row, step + t * Fmt<KV>::kTileBytes, lane);
-        issue_half<KV, 1>(P, row, step + t * Fmt<KV>::kTileBytes, lane);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int2 tr = lane_tile_rows<KV>(lane, hf);
+            const int64_t ra = row0 + min(kTile * t + tr.x, n - 1), rb = row0 + min(kTile * t + tr.y, n - 1);
+            if (hf) issue_half<KV, 1>(P, ra, rb, step + t * Fmt<KV>::kTileBytes, lane);
+            else issue_half<KV, 0>(P, ra, rb, step + t * Fmt<KV>::kTileBytes, lane);
+        }
     }
     wait_vmcnt<0>();
     __syncthreads();
@@ -1666,7 +1779,7 @@ __global__ __launch_bounds__(64) void dequant_kernel(Params P, int64_t rows, int
         // lane (G, n) holds column n of block c for tokens tau(G, 0..7).
         for (int w = 0; w < kWaves; ++w) {
             PvRaw<KV> v;
-            pv_load<KV>(step, fs, pv_lane_offset<KV>(lane, w), lane, w, v);
+            pv_load<KV>(step, fs, pv_lane_offsets<KV>(lane, w), lane, w, v);
 #pragma unroll
             for (int j = 0; j < (KV == MLA_KV_MXFP4 ? kWaveBlocks / 2 : kWaveBlocks); ++j) {
                 const int c = (KV == MLA_KV_MXFP4 ? kWaveBlocks / 2 : kWaveBlocks) * w + j;
@@ -1703,7 +1816,7 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t* p, int6
     int it = 0;
     for (int64_t base = b0; base < b1; base += 256, ++it) {
         const int64_t k = min(base + (int64_t)threadIdx.x, b1 - 1);
-        dma16(p + 16 * k, lds_addr(ring + (it % kStreamInFlight) * 4096 + 1024 * wave));
+        dma16nt<0>(p + 16 * k, lds_addr(ring + (it % kStreamInFlight) * 4096 + 1024 * wave));
         wait_vmcnt<kStreamInFlight - 1>();
     }
     wait_vmcnt<0>();
