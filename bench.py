@@ -584,6 +584,7 @@ def main():
         "sweep": sweep,
         "legs": legs,
         "kernel_source_hash": source_hash(),
+        "argv": " ".join(sys.argv[1:]),
         "host": platform.node(),
     }
     print(json.dumps(line), flush=True)
@@ -659,7 +660,7 @@ def _summarise_trace(d, h):
     out = ["# MLA decode kernels: durations under a bench run\n",
            "Command (one MI355X, from the repository root):\n",
            f"    cd /tmp && export TMPDIR=/tmp && cd <repo> && rocprofv3 --kernel-trace --stats --output-format csv "
-           f"-d DIR/trace -o run -- python3 bench.py {bench.get('_argv', '')}".rstrip() + " > DIR/trace.log",
+           f"-d DIR/trace -o run -- python3 bench.py {bench.get('argv', '')}".rstrip() + " > DIR/trace.log",
            "    python3 bench.py --summarise DIR\n",
            f"Kernel source sha256[:16] = `{h}`. Each leg: one checked call, {warm} warm-up calls, its cold calls (each",
            "after a 1 GiB read flush), then as many back-to-back warm calls. Durations are rocprofv3 kernel-dispatch",

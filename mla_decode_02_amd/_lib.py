@@ -2,9 +2,11 @@
 
 Argument marshalling only: shape / dtype / device checks that the C side
 cannot make (it only sees pointers), pointer extraction, the current HIP
-stream, and -- when the caller passes none -- a workspace tensor of the size
-the library asks for, with its arrival-counter region zeroed as the C ABI
-requires. No arithmetic of the operation happens here.
+stream, and -- when the caller passes none -- a workspace of the size the
+library asks for, with its arrival-counter region zeroed as the C ABI requires
+(kept per device and stream and reused by that stream's later calls, so a call
+without a workspace allocates only when it needs a larger one). No arithmetic
+of the operation happens here.
 """
 from __future__ import annotations
 
@@ -58,6 +60,22 @@ def new_workspace(nbytes: int, device, poison: bool = False):
     ws = torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device)
     if poison and ws.numel() > WORKSPACE_COUNTER_BYTES:
         ws[WORKSPACE_COUNTER_BYTES:].view(torch.float32).fill_(float("nan"))
+    return ws
+
+
+# Workspaces of the calls made without one, one per (device, stream): calls on a
+# stream run in order and each leaves the arrival-counter region zero, so a
+# stream's workspace is reused by its next call; it grows when a call needs more.
+_STREAM_WORKSPACES = {}
+
+
+def _stream_workspace(nbytes: int, device):
+    key = (device.index if device.index is not None else torch.cuda.current_device(),
+           torch.cuda.current_stream(device).cuda_stream)
+    ws = _STREAM_WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = new_workspace(nbytes, device)
+        _STREAM_WORKSPACES[key] = ws
     return ws
 
 
@@ -204,7 +222,7 @@ def mla_decode(q, kv, kv_scales, kv_indptr, kv_indices, out, lse=None, *, total_
               "lse must be contiguous fp32 [batch, 16]")
     need = mla_decode_workspace_size(B, total_kv, kv_dtype, flags)
     if workspace is None and need > 0:
-        workspace = new_workspace(need, q.device)
+        workspace = _stream_workspace(need, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rows = _kv_rows(kv, kv_rows)
     rc = _lib.mla_decode_rows(_ptr(q), _ptr(kv), _ptr(kv_scales), _ptr(kv_indptr), _ptr(kv_indices), _ptr(out),
@@ -280,7 +298,7 @@ def mla_decode_paged(q, kv, kv_scales, kv_indptr, kv_indices, kv_last_page_len, 
     plan_flags = flags | (FLAG_FORCE_SPLIT if page_size > 1 else 0)
     need = mla_decode_workspace_size(B, total_kv, kv_dtype, plan_flags)
     if workspace is None and need > 0:
-        workspace = new_workspace(need, q.device)
+        workspace = _stream_workspace(need, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = _lib.mla_decode_paged(_ptr(q), _ptr(kv), _ptr(kv_scales), _ptr(kv_indptr), _ptr(kv_indices),
                                _ptr(kv_last_page_len), int(page_size), _ptr(out), _ptr(lse), B, int(total_kv),
@@ -399,7 +417,7 @@ def mla_decode_q8(q, q_scale, kv, kv_scales, kv_indptr, kv_indices, out, lse=Non
     plan_flags = flags | (FLAG_FORCE_SPLIT if page_size > 1 else 0)
     need = mla_decode_q8_workspace_size(B, total_kv, kv_dtype, plan_flags, q_scale_mode)
     if workspace is None and need > 0:
-        workspace = new_workspace(need, q.device)
+        workspace = _stream_workspace(need, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = _lib.mla_decode_q8(_ptr(q), _ptr(q_scale), int(q_scale_mode), _ptr(kv), _ptr(kv_scales), _ptr(kv_indptr),
                             _ptr(kv_indices), _ptr(kv_last_page_len), int(page_size), _ptr(out), _ptr(lse), B,
@@ -484,7 +502,7 @@ def _mtp_args(q, qo_indptr, kv, kv_scales, kv_indptr, kv_indices, kv_last_page_l
               and tuple(lse.shape) == (total_q, NUM_HEADS), "lse must be contiguous fp32 [total_q, 16]")
     need = mla_decode_mtp_workspace_size(B, total_q, total_kv, kv_dtype, flags)
     if workspace is None and need > 0:
-        workspace = new_workspace(need, q.device)
+        workspace = _stream_workspace(need, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_ptr(q), _ptr(qo_indptr), int(total_q), int(uni_q_len), int(bool(causal)), _ptr(kv), _ptr(kv_scales),
             _ptr(kv_indptr), _ptr(kv_indices), _ptr(kv_last_page_len), int(page_size), _ptr(out), _ptr(lse), B,
