@@ -32,7 +32,6 @@ os.environ.setdefault("HIP_FORCE_DEV_KERNARG", "1")
 
 import argparse  # noqa: E402
 import csv  # noqa: E402
-import hashlib  # noqa: E402
 import json  # noqa: E402
 import platform  # noqa: E402
 import statistics  # noqa: E402
@@ -46,7 +45,6 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0
 HEADLINE = "fp8_b64_kv8192"
 FLUSH_BYTES = 1 << 30
-KERNEL_SOURCE = os.path.join(ROOT, "mla_decode_02_amd", "csrc", "mla_decode.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic.json")
 KERNEL_TIMES_FILE = os.path.join(PROFILES, "kernel_times.json")
@@ -86,8 +84,11 @@ def parse_args():
 
 
 def source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Digest of the sources the loaded library was built from; importing the
+    package has already checked that it is the digest of the tree's sources."""
+    import mla_decode_02_amd as mla
+
+    return mla.mla_source_digest()
 
 
 def log(msg):

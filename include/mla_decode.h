@@ -373,6 +373,16 @@ int mla_dequant_debug(int kv_dtype, const void* kv, const void* kv_scales, int64
  */
 int mla_hbm_read_probe(const void* buf, size_t bytes, void* stream);
 
+/*
+ * mla_source_digest: identifies the sources this library was compiled from:
+ * the first 16 hex digits of SHA-256 over the kernel, planner and this
+ * header, as the build computed them ("unrecorded" when built without it).
+ * A caller compares it with the digest of the sources it expects, so timings
+ * and test results are never attributed to a library left over from other
+ * sources. Pure host function; the string is static and owned by the library.
+ */
+const char* mla_source_digest(void);
+
 /* mla_status_string: static, human-readable text for a status code. */
 const char* mla_status_string(int status);
 

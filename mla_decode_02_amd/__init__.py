@@ -38,6 +38,7 @@ from ._lib import (  # noqa: F401
     mla_dequant_debug,
     mla_hbm_read_probe,
     mla_quantize_q8_debug,
+    mla_source_digest,
     mla_status_string,
     new_workspace,
     prepare_decode,

@@ -16,6 +16,8 @@ from dataclasses import dataclass
 
 import torch
 
+from . import build as _build
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmla_decode.so")
 
@@ -28,7 +30,8 @@ Q_SCALE_STATIC, Q_SCALE_DYNAMIC = 0, 1
 
 _EXPORTS = ("mla_decode", "mla_decode_rows", "mla_decode_noalloc", "mla_decode_paged", "mla_decode_q8", "mla_decode_mtp", "mla_decode_plan",
             "mla_decode_workspace_size", "mla_decode_q8_workspace_size", "mla_decode_mtp_workspace_size",
-            "mla_quantize_q8_debug", "mla_dequant_debug", "mla_hbm_read_probe", "mla_status_string")
+            "mla_quantize_q8_debug", "mla_dequant_debug", "mla_hbm_read_probe", "mla_status_string",
+            "mla_source_digest")
 
 
 class MlaError(RuntimeError):
@@ -120,6 +123,17 @@ def _load():
     lib.mla_hbm_read_probe.argtypes = [vp, sz, vp]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_status_string.argtypes = [i32]
+    lib.mla_source_digest.restype = ctypes.c_char_p
+    lib.mla_source_digest.argtypes = []
+    # A library built from other sources than the ones beside it (an edit not
+    # followed by a build) would run kernels that are not the tree's: refuse it.
+    built = lib.mla_source_digest().decode()
+    if all(os.path.exists(p) for p in _build.SOURCES):
+        tree = _build.source_digest()
+        if built != tree:
+            raise ImportError(
+                f"{LIB_PATH} was built from sources with digest {built}, the tree's are {tree}: "
+                "rebuild it with `python mla_decode_02_amd/build.py`")
     return lib
 
 
@@ -128,6 +142,11 @@ _lib = _load()
 
 def mla_status_string(status: int) -> str:
     return _lib.mla_status_string(int(status)).decode()
+
+
+def mla_source_digest() -> str:
+    """Digest of the sources the loaded library was compiled from."""
+    return _lib.mla_source_digest().decode()
 
 
 def flags_for(splits: int | None = None, persistent: bool | None = None, grid: int | None = None) -> int:

@@ -4,6 +4,7 @@
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -25,6 +26,23 @@ HIP_FLAGS = [
 ]
 
 
+# The files the library is compiled from, in the order the digest reads them.
+SOURCES = [os.path.join(CSRC, "mla_decode.hip"), os.path.join(CSRC, "mla_plan.cpp"),
+           os.path.join(CSRC, "mla_plan.h"), os.path.join(INCLUDE, "mla_decode.h")]
+
+
+def source_digest() -> str:
+    """First 16 hex digits of SHA-256 over the library's source files. The build
+    stores it in the library (mla_source_digest), so a library left over from
+    other sources can be told apart from one built from the tree as it stands."""
+    h = hashlib.sha256()
+    for path in SOURCES:
+        with open(path, "rb") as f:
+            data = f.read()
+        h.update(os.path.basename(path).encode() + b"\0" + len(data).to_bytes(8, "little") + data)
+    return h.hexdigest()[:16]
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -37,7 +55,8 @@ def build(verbose: bool = False) -> str:
     os.makedirs(obj_dir, exist_ok=True)
     plan_o = os.path.join(obj_dir, "mla_plan.o")
     hip_o = os.path.join(obj_dir, "mla_decode.o")
-    _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-c",
+    _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f'-DMLA_SOURCE_DIGEST="{source_digest()}"',
+          "-I", INCLUDE, "-c",
           os.path.join(CSRC, "mla_plan.cpp"), "-o", plan_o], verbose)
     _run(["hipcc", *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "mla_decode.hip"),
           "-o", hip_o], verbose)

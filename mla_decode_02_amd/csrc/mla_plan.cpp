@@ -204,3 +204,9 @@ extern "C" const char* mla_status_string(int status) {
         default: return "unknown status";
     }
 }
+
+#ifndef MLA_SOURCE_DIGEST
+#define MLA_SOURCE_DIGEST "unrecorded"
+#endif
+
+extern "C" const char* mla_source_digest(void) { return MLA_SOURCE_DIGEST; }

@@ -38,8 +38,42 @@ def test_header_declares_the_entry_points():
     for n in ("mla_decode", "mla_decode_rows", "mla_decode_paged", "mla_decode_q8", "mla_decode_mtp", "mla_decode_plan",
               "mla_decode_workspace_size", "mla_decode_q8_workspace_size", "mla_decode_mtp_workspace_size",
               "mla_quantize_q8_debug", "mla_dequant_debug", "mla_hbm_read_probe", "mla_decode_noalloc",
-              "mla_status_string"):
+              "mla_status_string", "mla_source_digest"):
         assert n in names
+
+
+def test_library_is_built_from_the_tree_sources(mla, raw_lib):
+    """The library records the digest of the sources it was compiled from; the
+    loaded one must be the tree's (importing the package refuses any other)."""
+    import mla_decode_02_amd.build as build
+
+    f = raw_lib.mla_source_digest
+    f.restype = ctypes.c_char_p
+    f.argtypes = []
+    assert f().decode() == build.source_digest() == mla.mla_source_digest()
+
+
+def test_source_digest_follows_every_source_file(tmp_path, monkeypatch):
+    """A change to any one source file (kernel, planner, planner header, C ABI
+    header) changes the digest."""
+    import mla_decode_02_amd.build as build
+
+    copies = []
+    for i, src in enumerate(build.SOURCES):
+        dst = tmp_path / f"{i}_{os.path.basename(src)}"
+        dst.write_bytes(open(src, "rb").read())
+        copies.append(str(dst))
+    monkeypatch.setattr(build, "SOURCES", copies)
+    base = build.source_digest()
+    assert base == build.source_digest()
+    for path in copies:
+        data = open(path, "rb").read()
+        with open(path, "wb") as f:
+            f.write(data + b" ")
+        assert build.source_digest() != base, path
+        with open(path, "wb") as f:
+            f.write(data)
+    assert build.source_digest() == base
 
 
 def test_library_exports_every_declared_symbol(raw_lib):
