@@ -163,8 +163,8 @@ def mtp_query(case, mtp, dev):
 def plan_of(mla, case, flags, mtp=0):
     paged = case.meta.get("paged")
     plan_flags = flags | (mla.FLAG_FORCE_SPLIT if (paged and paged["page_size"] > 1) or mtp else 0)
-    if mtp:  # the plan runs over the query rows, each seeing its sequence
-        return mla.mla_decode_plan(case.batch * mtp, min(case.total_kv * mtp, 2**31 - 1), case.kv_dtype, plan_flags)
+    if mtp:  # split-K over the query rows (or, on the bf16 cache, row pairs), each seeing its sequence
+        return mla.mla_decode_mtp_plan(case.batch, case.batch * mtp, case.total_kv, case.kv_dtype, plan_flags, mtp)
     return mla.mla_decode_plan(case.batch, case.total_kv, case.kv_dtype, plan_flags)
 
 
@@ -236,7 +236,8 @@ def measure(name, args, dev, flush, q8=None, mtp=0, steps=None):
         "kv_len": int(case.kv_indptr[1] - case.kv_indptr[0]),
         "plan": {"mode": "split" if plan.mode == 0 else "persistent", "splits": plan.num_splits,
                  "grid": plan.grid, "combine_launch": plan.combine == 1,
-                 "merge": ("none", "combine launch", "last-arriving split workgroup")[plan.combine]},
+                 "merge": ("none", "combine launch", "last-arriving split workgroup")[plan.combine],
+                 "rows_per_wg": plan.rows_per_wg},
         "launches": launches(plan, q8),
         "steps": steps,
         "calls": 1 + args.warmup + 2 * steps,  # the prepared call's checked first call, warm-up, cold, warm
@@ -492,20 +493,29 @@ def main():
                     f"({r['pct_hbm_peak_kv']:.1f}% of 8 TB/s), plan {r['plan']}")
         args.flags = base_flags
         torch.cuda.empty_cache()
-    # Several causal query tokens per sequence (mla_decode_mtp): 2 and 4 tokens on fp8 32 x 1k and
-    # on fp8 64 x 8k. Effective GB/s counts the cache once.
+    # Several causal query tokens per sequence (mla_decode_mtp): 2 and 4 tokens on fp8 32 x 1k,
+    # fp8 64 x 8k and bf16 64 x 8k. On the bf16 cache the default plan carries two query rows per
+    # workgroup; its "rows" legs force one row per workgroup, and "q1" is the one-token mla_decode
+    # call on the same cache. Effective GB/s counts the cache once.
     grid_mtp = None
     if not args.no_mtp_grid:
         grid_mtp = {}
-        for n in dict.fromkeys(["fp8_b32_kv1024", "fp8_b64_kv8192"]):
-            for k in (2, 4):
-                r = measure(n, args, dev, flush, mtp=k)
-                r.pop("_case", None)
-                grid_mtp[f"{n}/q{k}"] = r
-                legs.append({"label": f"mtp {n}/q{k}", "calls": r["calls"], "launches": r["launches"],
-                             "steps": r["steps"]})
-                log(f"# mtp q{k} {n}: cold {r['cold_us_median']:.2f} us, warm {r['warm_us']:.2f} us, "
-                    f"{r['effective_kv_GBps']:.0f} GB/s KV counted once ({r['pct_hbm_peak_kv']:.1f}% of 8 TB/s)")
+        base_flags = args.flags
+        mtp_legs = [("fp8_b32_kv1024", k, "") for k in (2, 4)] + [("fp8_b64_kv8192", k, "") for k in (2, 4)] + \
+            [("bf16_b64_kv8192", 1, ""), ("bf16_b64_kv8192", 2, ""), ("bf16_b64_kv8192", 4, ""),
+             ("bf16_b64_kv8192", 2, "rows"), ("bf16_b64_kv8192", 4, "rows")]
+        for n, k, variant in mtp_legs:
+            args.flags = base_flags | (mla.FLAG_ROW_PER_WG if variant == "rows" else 0)
+            r = measure(n, args, dev, flush, mtp=k if k > 1 else 0)
+            r.pop("_case", None)
+            key = f"{n}/q{k}" + (f"/{variant}" if variant else "")
+            grid_mtp[key] = r
+            legs.append({"label": f"mtp {key}", "calls": r["calls"], "launches": r["launches"],
+                         "steps": r["steps"]})
+            log(f"# mtp {key}: cold {r['cold_us_median']:.2f} us, warm {r['warm_us']:.2f} us, "
+                f"{r['effective_kv_GBps']:.0f} GB/s KV counted once ({r['pct_hbm_peak_kv']:.1f}% of 8 TB/s), "
+                f"plan {r['plan']}")
+        args.flags = base_flags
     graph = None
     if not args.no_graph and args.workload not in syn.PAGED:  # the graph leg replays mla_decode (page size 1)
         graph = measure_graph(args.workload, args, dev, flush)

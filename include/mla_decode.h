@@ -72,6 +72,10 @@ extern "C" {
 #define MLA_FLAG_COMBINE_LAUNCH 0x8    /* split-K: merge the split partials in a separate
                                           combine launch instead of in the last-arriving
                                           split workgroup of each sequence               */
+#define MLA_FLAG_ROW_PER_WG 0x10       /* several-query-token calls: one query row per
+                                          workgroup even where the plan would carry two
+                                          (bf16 cache, uniform query count); ignored by the
+                                          single-token calls                             */
 #define MLA_FLAG_SPLITS_SHIFT 8        /* bits 8..15: split count for split-K (1..255)   */
 #define MLA_FLAG_GRID_SHIFT 16         /* bits 16..27: workgroups for persistent (1..4095)*/
 
@@ -102,7 +106,10 @@ typedef struct mla_plan_info {
     int combine;            /* how the split partials are merged: 0 none (one split),
                                1 a combine launch after stage 1, 2 inside stage 1 by
                                the last-arriving split workgroup of each sequence  */
-    int reserved;
+    int rows_per_wg;        /* query rows each stage-1 workgroup carries: 1, or 2 for
+                               mla_decode_mtp on the bf16 cache with a uniform query
+                               count of at least 2 (the workgroup gathers the cache
+                               once for both rows)                                  */
     size_t workspace_bytes; /* bytes of workspace this plan needs (0 when none)          */
 } mla_plan_info;
 
@@ -325,9 +332,9 @@ int mla_quantize_q8_debug(const void* q, int batch, float* q_scale, int q_scale_
  *              as mla_decode_paged (page_size 1: the layout of mla_decode)
  *   workspace  at least mla_decode_mtp_workspace_size(...) bytes, 16-byte
  *              aligned (NULL allowed when that size is 0)
- *   flags      MLA_FLAG_FORCE_SPLIT with a split count, or 0 (heuristic); the
- *              plan is always split-K over the query rows, and
- *              MLA_FLAG_FORCE_PERSISTENT is rejected
+ *   flags      MLA_FLAG_FORCE_SPLIT with a split count, or 0 (heuristic);
+ *              MLA_FLAG_ROW_PER_WG; the plan (mla_decode_mtp_plan) is always
+ *              split-K, and MLA_FLAG_FORCE_PERSISTENT is rejected
  * Returns as mla_decode_paged; MLA_ERR_INVALID_ARG also for a bad causal,
  * total_q or uni_q_len, or a NULL / misaligned qo_indptr when uni_q_len = 0.
  */
@@ -337,11 +344,27 @@ int mla_decode_mtp(const void* q, const int32_t* qo_indptr, int total_q, int uni
                    int kv_dtype, float sm_scale, void* workspace, size_t workspace_bytes, int flags, void* stream);
 
 /*
- * mla_decode_mtp_workspace_size: bytes of workspace mla_decode_mtp needs
- * (the split partials of its plan over total_q query rows). Pure host
- * function; 0 for invalid arguments.
+ * mla_decode_mtp_plan: the launch plan of mla_decode_mtp for these sizes
+ * (pure host function). The plan is split-K. On the bf16 cache with a
+ * uniform query count n = uni_q_len >= 2 (and without MLA_FLAG_ROW_PER_WG),
+ * each workgroup carries two consecutive query rows of one sequence (the
+ * last of an odd n alone): grid = splits x batch x ceil(n / 2), and
+ * rows_per_wg = 2; both rows' scores run on the rows the workgroup gathers
+ * once. Otherwise each workgroup carries one query row: grid = splits x
+ * total_q, rows_per_wg = 1. Partials are per query row (num_partials =
+ * splits x total_q when splits > 1), merged as for mla_decode.
+ * Returns MLA_OK or MLA_ERR_INVALID_ARG.
  */
-size_t mla_decode_mtp_workspace_size(int batch, int total_q, int64_t total_kv, int kv_dtype, int flags);
+int mla_decode_mtp_plan(int batch, int total_q, int uni_q_len, int64_t total_kv, int kv_dtype, int flags,
+                        mla_plan_info* plan);
+
+/*
+ * mla_decode_mtp_workspace_size: bytes of workspace mla_decode_mtp needs
+ * (the split partials of mla_decode_mtp_plan's plan). Pure host function; 0
+ * for invalid arguments.
+ */
+size_t mla_decode_mtp_workspace_size(int batch, int total_q, int uni_q_len, int64_t total_kv, int kv_dtype,
+                                     int flags);
 
 /*
  * mla_dequant_debug: decode `rows` physical cache rows to fp32 [rows, 576]

@@ -24,11 +24,13 @@ LIB_PATH = os.path.join(_HERE, "libmla_decode.so")
 NUM_HEADS, QK_DIM, V_DIM = 16, 576, 512
 KV_BF16, KV_FP8_E4M3, KV_MXFP4 = 0, 1, 2
 FLAG_FORCE_SPLIT, FLAG_FORCE_PERSISTENT, FLAG_MIXED_LENGTHS, FLAG_COMBINE_LAUNCH = 0x1, 0x2, 0x4, 0x8
+FLAG_ROW_PER_WG = 0x10  # several-query-token calls: one query row per workgroup
 WORKSPACE_COUNTER_BYTES = 65536  # leading workspace bytes that hold the arrival counters (zero between calls)
 FLAG_SPLITS_SHIFT, FLAG_GRID_SHIFT = 8, 16
 Q_SCALE_STATIC, Q_SCALE_DYNAMIC = 0, 1
 
 _EXPORTS = ("mla_decode", "mla_decode_rows", "mla_decode_noalloc", "mla_decode_paged", "mla_decode_q8", "mla_decode_mtp", "mla_decode_plan",
+            "mla_decode_mtp_plan",
             "mla_decode_workspace_size", "mla_decode_q8_workspace_size", "mla_decode_mtp_workspace_size",
             "mla_quantize_q8_debug", "mla_dequant_debug", "mla_hbm_read_probe", "mla_status_string",
             "mla_source_digest")
@@ -42,7 +44,7 @@ class MlaError(RuntimeError):
 
 class _Plan(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int), ("num_splits", ctypes.c_int), ("grid", ctypes.c_int),
-                ("num_partials", ctypes.c_int), ("combine", ctypes.c_int), ("reserved", ctypes.c_int),
+                ("num_partials", ctypes.c_int), ("combine", ctypes.c_int), ("rows_per_wg", ctypes.c_int),
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -54,6 +56,7 @@ class PlanInfo:
     num_partials: int
     combine: int         # 0 none, 1 combine launch, 2 merged by the last-arriving split workgroup
     workspace_bytes: int
+    rows_per_wg: int = 1  # query rows each stage-1 workgroup carries
 
 
 def new_workspace(nbytes: int, device, poison: bool = False):
@@ -112,7 +115,9 @@ def _load():
     lib.mla_decode_mtp.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, i32, i64, i32,
                                    ctypes.c_float, vp, sz, i32, vp]
     lib.mla_decode_mtp_workspace_size.restype = sz
-    lib.mla_decode_mtp_workspace_size.argtypes = [i32, i32, i64, i32, i32]
+    lib.mla_decode_mtp_workspace_size.argtypes = [i32, i32, i32, i64, i32, i32]
+    lib.mla_decode_mtp_plan.restype = i32
+    lib.mla_decode_mtp_plan.argtypes = [i32, i32, i32, i64, i32, i32, ctypes.POINTER(_Plan)]
     lib.mla_decode_plan.restype = i32
     lib.mla_decode_plan.argtypes = [i32, i64, i32, i32, ctypes.POINTER(_Plan)]
     lib.mla_decode_workspace_size.restype = sz
@@ -166,7 +171,18 @@ def mla_decode_plan(batch: int, total_kv: int, kv_dtype: int, flags: int = 0) ->
     rc = _lib.mla_decode_plan(int(batch), int(total_kv), int(kv_dtype), int(flags), ctypes.byref(p))
     if rc != 0:
         raise MlaError(rc, "mla_decode_plan")
-    return PlanInfo(p.mode, p.num_splits, p.grid, p.num_partials, p.combine, p.workspace_bytes)
+    return PlanInfo(p.mode, p.num_splits, p.grid, p.num_partials, p.combine, p.workspace_bytes, p.rows_per_wg)
+
+
+def mla_decode_mtp_plan(batch: int, total_q: int, total_kv: int, kv_dtype: int, flags: int = 0,
+                        uni_q_len: int = 0) -> PlanInfo:
+    """The launch plan of mla_decode_mtp (include/mla_decode.h, mla_decode_mtp_plan)."""
+    p = _Plan()
+    rc = _lib.mla_decode_mtp_plan(int(batch), int(total_q), int(uni_q_len), int(total_kv), int(kv_dtype), int(flags),
+                                  ctypes.byref(p))
+    if rc != 0:
+        raise MlaError(rc, "mla_decode_mtp_plan")
+    return PlanInfo(p.mode, p.num_splits, p.grid, p.num_partials, p.combine, p.workspace_bytes, p.rows_per_wg)
 
 
 def mla_decode_workspace_size(batch: int, total_kv: int, kv_dtype: int, flags: int = 0) -> int:
@@ -179,9 +195,10 @@ def mla_decode_q8_workspace_size(batch: int, total_kv: int, kv_dtype: int, flags
                                                  int(q_scale_mode)))
 
 
-def mla_decode_mtp_workspace_size(batch: int, total_q: int, total_kv: int, kv_dtype: int, flags: int = 0) -> int:
-    return int(_lib.mla_decode_mtp_workspace_size(int(batch), int(total_q), int(total_kv), int(kv_dtype),
-                                                  int(flags)))
+def mla_decode_mtp_workspace_size(batch: int, total_q: int, total_kv: int, kv_dtype: int, flags: int = 0,
+                                  uni_q_len: int = 0) -> int:
+    return int(_lib.mla_decode_mtp_workspace_size(int(batch), int(total_q), int(uni_q_len), int(total_kv),
+                                                  int(kv_dtype), int(flags)))
 
 
 def _ptr(t):
@@ -519,7 +536,7 @@ def _mtp_args(q, qo_indptr, kv, kv_scales, kv_indptr, kv_indices, kv_last_page_l
     if lse is not None:
         _need(lse.is_cuda and lse.dtype == torch.float32 and lse.is_contiguous()
               and tuple(lse.shape) == (total_q, NUM_HEADS), "lse must be contiguous fp32 [total_q, 16]")
-    need = mla_decode_mtp_workspace_size(B, total_q, total_kv, kv_dtype, flags)
+    need = mla_decode_mtp_workspace_size(B, total_q, total_kv, kv_dtype, flags, uni_q_len)
     if workspace is None and need > 0:
         workspace = _stream_workspace(need, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -758,11 +758,16 @@ struct QOperand<MLA_KV_MXFP4, 1> { using T = i32x8; };
 template <>
 struct QOperand<MLA_KV_MXFP4, 0> { using T = i32x8; };
 
-struct WaveAcc {
-    f32x4 o[kWaveBlocks];  // o[j][i]: head 4G+i, column dcol(kWaveBlocks * wave + j, r)
-    float m;               // running max of head r (log2 units), the same in every lane and wave
-    float l;               // this lane's share of head r's softmax denominator
+// NB output blocks of 16 columns: o[j][i] is head 4G+i of block j's column
+// r (the wave's blocks: kWaveBlocks * wave + j with one query row per
+// workgroup, 2 kWaveBlocks * (wave % 2) + j with two).
+template <int NB = kWaveBlocks>
+struct WaveAccT {
+    f32x4 o[NB];
+    float m;  // running max of head r (log2 units), the same in every lane (and wave of the row)
+    float l;  // this lane's share of head r's softmax denominator
 };
+using WaveAcc = WaveAccT<>;
 
 // This wave's value-operand data of one staged step, read from LDS ahead of
 // the softmax so that the read latency overlaps it (converted afterwards).
@@ -894,8 +899,9 @@ __device__ __forceinline__ void pv_mma(const PvRaw<KV>& v, bf16x8 pa, WaveAcc& a
 // layout of the P . V product. s[t]: full scores of tile t (the same in all
 // four waves, so every wave takes the same rescale decisions and keeps the
 // same m and l).
+template <int NB = kWaveBlocks>
 __device__ __forceinline__ bf16x8 softmax_step(const f32x4 (&s)[2], float qk_scale, int nvalid, int lane,
-                                               WaveAcc& a) {
+                                               WaveAccT<NB>& a) {
     const int G = lane >> 4;
     float x[8];  // raw scores; scaled below inside the exponent
 #pragma unroll
@@ -916,7 +922,7 @@ __device__ __forceinline__ bf16x8 softmax_step(const f32x4 (&s)[2], float qk_sca
 #pragma unroll
         for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * G + i);
 #pragma unroll
-        for (int j = 0; j < kWaveBlocks; ++j)
+        for (int j = 0; j < NB; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) a.o[j][i] *= al[i];
     }
@@ -1020,10 +1026,15 @@ __device__ __forceinline__ void issue_early(const Params& P, uint8_t* smem, int6
 //   8-element groups tid, tid + 256, ... of the row's 16 x 576 query,
 //   quantised (fp8 query) or split into two code sets (bf16 query on MXFP4)
 //   once per workgroup later on.
-template <int KV, int QF>
+// NT = 2 (two query rows per workgroup, bf16 cache and query): wave w holds
+// the Q^T operands of row w / 2 over all 18 score k-steps, qB2[h][j] those of
+// k-step kHalfK h + j.
+template <int KV, int QF, int NT = 1>
 struct QueryRegs {
+    static_assert(NT == 1 || (NT == 2 && KV == MLA_KV_BF16 && !QF), "two rows per workgroup: bf16 only");
     static constexpr bool kSplit = KV == MLA_KV_MXFP4 && !QF;  // split query on the MX-scaled MFMA
-    typename QOperand<KV, QF>::T qB[KV == MLA_KV_MXFP4 ? (QF ? 3 : 6) : kHalfK];
+    typename QOperand<KV, QF>::T qB[NT == 2 ? 1 : KV == MLA_KV_MXFP4 ? (QF ? 3 : 6) : kHalfK];
+    bf16x8 qB2[NT == 2 ? 2 : 1][NT == 2 ? kHalfK : 1];
     bf16x8 qg[(QF || kSplit) ? kQPer : 1];
     int qsc[kSplit ? 6 : 1];  // split query: e8m0 codes of qB (head r, k block G)
     float kv_scale, q_scale, q_part;
@@ -1054,6 +1065,21 @@ __device__ __forceinline__ void load_query(const Params& P, int b, QueryRegs<KV,
         for (int j = 0; j < kHalfK; ++j)
             q.qB[j] = *reinterpret_cast<const bf16x8*>(qrow + dbase<KV>(kHalfK * hf + j, G));
     }
+}
+
+// Two query rows per workgroup: this wave's row is `row` (wave / 2 picks
+// which of the pair the caller passes); all 18 k-steps of its Q^T.
+__device__ __forceinline__ void load_query_pair(const Params& P, int row, QueryRegs<MLA_KV_BF16, 0, 2>& q) {
+    const int lane = threadIdx.x & 63, G = lane >> 4, r = lane & 15;
+    const __bf16* qrow = P.q + ((int64_t)row * kHeads + r) * kDqk;
+    q.kv_scale = 1.0f;
+    q.q_scale = 1.0f;
+    q.q_part = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < kHalfK; ++j)
+            q.qB2[h][j] = *reinterpret_cast<const bf16x8*>(qrow + dbase<MLA_KV_BF16>(kHalfK * h + j, G));
 }
 
 // Buffer resource of `bytes` bytes at p for the raw buffer loads of the
@@ -1163,10 +1189,18 @@ __device__ void merge_if_last(const Params& P, int row, uint8_t* smem) {
 // QF = 1: fp8 query. Q is quantised here (static scale read, or the dynamic
 // scale reduced from the partial maxima); `scale_out` makes this workgroup
 // publish a dynamic scale.
-template <int KV, int QF, bool MG = false>
+// Two query rows per workgroup (NT = 2): row t of the pair sees the sequence's
+// positions [0, lim_t); has1 is false when the pair has no second row (the
+// last row of an odd count).
+struct RowPair {
+    int lim0 = 0, lim1 = 0;
+    bool has1 = false;
+};
+
+template <int KV, int QF, bool MG = false, int NT = 1>
 __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, int t1, bool final, int slot,
-                       bool scale_out, QueryRegs<KV, QF>& qr, bool idx_dma, bool idx_staged,
-                       int64_t early_first = -1) {
+                       bool scale_out, QueryRegs<KV, QF, NT>& qr, bool idx_dma, bool idx_staged,
+                       int64_t early_first = -1, RowPair pr = RowPair{}) {
     using L = Layout<KV>;
     constexpr int R = Fmt<KV>::kRing;
     constexpr int D = R - 1;  // steps issued ahead of the one computed
@@ -1177,7 +1211,11 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
     int32_t* idx = reinterpret_cast<int32_t*>(smem + L::kIdxOff);
     f32x4* sbuf = reinterpret_cast<f32x4*>(smem + L::kSbufOff);
     float* fs_buf = reinterpret_cast<float*>(smem + L::kFsOff);
-    const PvOff<KV> pv_off = pv_lane_offsets<KV>(lane, wave);
+    // One query row per workgroup: the wave's value reads are those of its 8
+    // output blocks. Two rows (NT = 2): wave w runs row w / 2 alone, with the
+    // 16 blocks of the two block groups 2 (w % 2) and 2 (w % 2) + 1.
+    const PvOff<KV> pv_off = pv_lane_offsets<KV>(lane, NT == 2 ? 2 * tile : wave);
+    const PvOff<KV> pv_off1 = pv_lane_offsets<KV>(lane, NT == 2 ? 2 * tile + 1 : wave);
     const int2 trows = lane_tile_rows<KV>(lane, hf);  // this lane's tile rows when it issues its half
 
     // The first index window (unless the caller's LDS-DMA of a guessed window
@@ -1188,7 +1226,7 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
     if (!idx_staged) load_idx<KV>(P, base, t0, min(kIdxWindow, t1 - t0), iv);
     using QOp = typename QOperand<KV, QF>::T;
     constexpr bool kMx = QF && KV == MLA_KV_MXFP4;           // fp8 query: scores on the MX-scaled MFMA
-    constexpr bool kSplit = QueryRegs<KV, QF>::kSplit;      // bf16 query, MXFP4 cache: split query, same MFMA
+    constexpr bool kSplit = QueryRegs<KV, QF, NT>::kSplit;  // bf16 query, MXFP4 cache: split query, same MFMA
     auto& qB = qr.qB;
     auto& qg = qr.qg;
     auto& qsc = qr.qsc;
@@ -1198,7 +1236,12 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
     // Consume Q and the scales here: the compiler's wait for these loads must
     // not land inside the token loop, where the count it waits for would also
     // drain the gathers in flight (it does not see the LDS-DMA loads).
-    if constexpr (QF || kSplit) {
+    if constexpr (NT == 2) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < kHalfK; ++j) asm volatile("" ::"v"(qr.qB2[h][j]));
+    } else if constexpr (QF || kSplit) {
 #pragma unroll
         for (int k = 0; k < kQPer; ++k) asm volatile("" ::"v"(qg[k]));
     } else {
@@ -1218,11 +1261,11 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
     }
     const float qk_scale = P.sm_scale * kv_scale * q_scale * kLog2e;
 
-    WaveAcc a;
+    WaveAccT<kWaveBlocks * NT> acc;
 #pragma unroll
-    for (int j = 0; j < kWaveBlocks; ++j) a.o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    a.m = -INFINITY;
-    a.l = 0.f;
+    for (int j = 0; j < kWaveBlocks * NT; ++j) acc.o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc.m = -INFINITY;
+    acc.l = 0.f;
 
     for (int w0 = t0; w0 < t1; w0 += kIdxWindow) {
         const int n = min(kIdxWindow, t1 - w0);
@@ -1245,10 +1288,13 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
         };
         // This wave's partial scores of step i, for exchange buffer i % 2.
         // (MXFP4: also converts the step's value-block scales into buffer i % 2.)
+        // Two rows per workgroup: the full scores of tile `tile` for row hf.
         auto scores = [&](int i) -> f32x4 {
             const uint8_t* st = smem + (i % R) * L::kStepBytes;
             if constexpr (KV == MLA_KV_MXFP4) convert_scales(st, fs_buf + (i & 1) * (L::kFsBytes / 4), tid);
-            if constexpr (kMx) {
+            if constexpr (NT == 2) {
+                return qk_partial<KV, 0>(st, qr.qB2[0], tile, lane) + qk_partial<KV, 1>(st, qr.qB2[1], tile, lane);
+            } else if constexpr (kMx) {
                 return hf ? qk_partial_mx<1>(st, qB, tile, lane) : qk_partial_mx<0>(st, qB, tile, lane);
             } else if constexpr (kSplit) {
                 return hf ? qk_partial_mx2<1>(st, qB, qsc, tile, lane) : qk_partial_mx2<0>(st, qB, qsc, tile, lane);
@@ -1368,62 +1414,99 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
             if (s + D < nsteps) issue_step(s + D);  // into the slot of step s - 1
             const f32x4* sb = sbuf + (s & 1) * (kWaves * 64);
             f32x4 sc[2];
-            sc[0] = sb[0 * 64 + lane] + sb[2 * 64 + lane];
-            sc[1] = sb[1 * 64 + lane] + sb[3 * 64 + lane];
+            if constexpr (NT == 2) {  // wave 2 t + u: tile u of row t; this wave's row is hf
+                sc[0] = sb[(2 * hf) * 64 + lane];
+                sc[1] = sb[(2 * hf + 1) * 64 + lane];
+            } else {  // wave 2 h + u: half h of tile u
+                sc[0] = sb[0 * 64 + lane] + sb[2 * 64 + lane];
+                sc[1] = sb[1 * 64 + lane] + sb[3 * 64 + lane];
+            }
             // Program order keeps every long latency behind independent work:
             // the value reads of step s and the score MFMAs of step s + 1 are
             // issued before the softmax, and the scores are stored after P . V.
-            PvRaw<KV> v;
+            PvRaw<KV> v, v1;
             pv_load<KV>(smem + (s % R) * L::kStepBytes, fs_buf + (s & 1) * (L::kFsBytes / 4), pv_off, lane, wave, v);
+            if constexpr (NT == 2)
+                pv_load<KV>(smem + (s % R) * L::kStepBytes, fs_buf, pv_off1, lane, wave, v1);
             f32x4 next = {0.f, 0.f, 0.f, 0.f};
             if (s + 1 < nsteps) next = scores(s + 1);
-            const bf16x8 pa = softmax_step(sc, qk_scale, n - s * kStepTokens, lane, a);
-            pv_mma<KV>(v, pa, a);
+            if constexpr (NT == 2) {
+                // this wave's row: its valid tokens of the step, none once past
+                // its visible prefix (uniform in the wave; no barrier inside)
+                const int lim = hf ? (pr.has1 ? pr.lim1 : w0) : pr.lim0;
+                const int nv = min(n, lim - w0) - s * kStepTokens;
+                if (nv > 0) {
+                    const bf16x8 pa = softmax_step(sc, qk_scale, nv, lane, acc);
+#pragma unroll
+                    for (int j = 0; j < kWaveBlocks; ++j) acc.o[j] = mfma32(pa, pv_convert<KV>(v, j), acc.o[j]);
+#pragma unroll
+                    for (int j = 0; j < kWaveBlocks; ++j)
+                        acc.o[kWaveBlocks + j] = mfma32(pa, pv_convert<KV>(v1, j), acc.o[kWaveBlocks + j]);
+                }
+            } else {
+                const bf16x8 pa = softmax_step(sc, qk_scale, n - s * kStepTokens, lane, acc);
+                pv_mma<KV>(v, pa, acc);
+            }
             if (s + 1 < nsteps) put_scores(s + 1, next);
         }
     }
 
-    // ---- epilogue: every wave holds the same m and l; it writes its own columns ----
-    const float lt = group_sum4(a.l);
-    const float inv_r = (lt > 0.f) ? kv_scale / lt : 0.f;  // head r
-    const float lse_r = (lt > 0.f) ? (a.m + log2f(lt)) * kLn2 : -INFINITY;
-    float inv[4];
+    // ---- epilogue: every wave of a row holds the same m and l; it writes its own columns ----
+    // One row: query row b, the wave's blocks kWaveBlocks * wave + j. Two rows
+    // (NT = 2): wave w writes row b + w / 2 (absent: nothing), blocks
+    // 2 kWaveBlocks (w % 2) + j; the row's partial slot is slot + (w / 2) nsplit
+    // (slots are row-major over the splits).
+    const int row = b + (NT == 2 ? hf : 0);
+    const bool live = NT == 1 || hf == 0 || pr.has1;
+    const int64_t sl = (int64_t)slot + (NT == 2 ? (int64_t)hf * P.nsplit : 0);
+    const int vb = NT == 2 ? 2 * kWaveBlocks * tile : kWaveBlocks * wave;  // first output block of this wave
+    const bool lse_wave = NT == 2 ? tile == 0 : wave == 0;
+    if (live) {
+        const float lt = group_sum4(acc.l);
+        const float inv_r = (lt > 0.f) ? kv_scale / lt : 0.f;  // head r
+        const float lse_r = (lt > 0.f) ? (acc.m + log2f(lt)) * kLn2 : -INFINITY;
+        float inv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) inv[i] = __shfl(inv_r, 4 * G + i);  // head 4G+i lives in lane 4G+i
-    if (final) {
-        __bf16* o = P.out + (int64_t)b * kHeads * kDv;
+        for (int i = 0; i < 4; ++i) inv[i] = __shfl(inv_r, 4 * G + i);  // head 4G+i lives in lane 4G+i
+        if (final) {
+            __bf16* o = P.out + (int64_t)row * kHeads * kDv;
 #pragma unroll
-        for (int j = 0; j < kWaveBlocks; ++j) {
-            const int col = dcol<KV>(kWaveBlocks * wave + j, r);
+            for (int j = 0; j < kWaveBlocks * NT; ++j) {
+                const int col = dcol<KV>(vb + j, r);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[(4 * G + i) * kDv + col] = (__bf16)(a.o[j][i] * inv[i]);
+                for (int i = 0; i < 4; ++i) o[(4 * G + i) * kDv + col] = (__bf16)(acc.o[j][i] * inv[i]);
+            }
+            if (lse_wave && G == 0 && P.lse) P.lse[(int64_t)row * kHeads + r] = lse_r;
+        } else if constexpr (MG) {
+            // device-coherent stores (written through to memory), read back by
+            // whichever split workgroup of this row arrives last
+            float* o = P.part_o + sl * kHeads * kDv;
+#pragma unroll
+            for (int j = 0; j < kWaveBlocks * NT; ++j) {
+                const int col = dcol<KV>(vb + j, r);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    __hip_atomic_store(o + (4 * G + i) * kDv + col, acc.o[j][i] * inv[i], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (lse_wave && G == 0)
+                __hip_atomic_store(P.part_lse + sl * kHeads + r, lse_r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            float* o = P.part_o + sl * kHeads * kDv;
+#pragma unroll
+            for (int j = 0; j < kWaveBlocks * NT; ++j) {
+                const int col = dcol<KV>(vb + j, r);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[(4 * G + i) * kDv + col] = acc.o[j][i] * inv[i];
+            }
+            if (lse_wave && G == 0) P.part_lse[sl * kHeads + r] = lse_r;
         }
-        if (wave == 0 && G == 0 && P.lse) P.lse[(int64_t)b * kHeads + r] = lse_r;
-    } else if constexpr (MG) {
-        // device-coherent stores (written through to memory), read back by
-        // whichever split workgroup of this row arrives last
-        float* o = P.part_o + (int64_t)slot * kHeads * kDv;
-#pragma unroll
-        for (int j = 0; j < kWaveBlocks; ++j) {
-            const int col = dcol<KV>(kWaveBlocks * wave + j, r);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                __hip_atomic_store(o + (4 * G + i) * kDv + col, a.o[j][i] * inv[i], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if constexpr (MG) {
+        if (!final) {
+            merge_if_last(P, b, smem);
+            if (NT == 2 && pr.has1) merge_if_last(P, b + 1, smem);
         }
-        if (wave == 0 && G == 0)
-            __hip_atomic_store(P.part_lse + (int64_t)slot * kHeads + r, lse_r, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        merge_if_last(P, b, smem);
-    } else {
-        float* o = P.part_o + (int64_t)slot * kHeads * kDv;
-#pragma unroll
-        for (int j = 0; j < kWaveBlocks; ++j) {
-            const int col = dcol<KV>(kWaveBlocks * wave + j, r);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[(4 * G + i) * kDv + col] = a.o[j][i] * inv[i];
-        }
-        if (wave == 0 && G == 0) P.part_lse[(int64_t)slot * kHeads + r] = lse_r;
     }
 }
 
@@ -1474,10 +1557,43 @@ __device__ __forceinline__ Params stage1_params(const __bf16* q, const int32_t* 
     return P;
 }
 
+// Two query rows of one sequence per workgroup (several query tokens per
+// sequence, uniform count n = uni_q >= 2, bf16 cache): work row w is the
+// pair of rows b n + 2 g, b n + 2 g + 1 of sequence b = w / ceil(n / 2),
+// g = w % ceil(n / 2) (the last of an odd n alone). The split ranges are
+// those of the pair's later row, which sees the most tokens; the earlier
+// row masks what it does not see.
+template <int KV, int QF, bool MG>
+__device__ void split_pair(const Params& P, uint8_t* smem, int nblocks) {
+    const int item = xcd_order(blockIdx.x, nblocks);
+    const int wrow = item / P.nsplit, s = item % P.nsplit;
+    const int n = P.uni_q, gq = (n + 1) >> 1;
+    const int b = wrow / gq, t0q = 2 * (wrow - b * gq);
+    const int row0 = b * n + t0q;
+    const bool has1 = t0q + 1 < n;
+    const int hf = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >> 1;
+    QueryRegs<KV, QF, 2> qr;
+    load_query_pair(P, row0 + (has1 ? hf : 0), qr);
+    const int base = P.indptr[b], entries = P.indptr[b + 1] - base;
+    const int Ls = P.page_size == 1 ? entries : entries > 0 ? (entries - 1) * P.page_size + P.last_page[b] : 0;
+    const int hide0 = P.causal ? n - 1 - t0q : 0;
+    const int hide1 = P.causal && has1 ? hide0 - 1 : hide0;
+    RowPair pr;
+    pr.lim0 = max(0, Ls - hide0);
+    pr.lim1 = max(0, Ls - hide1);
+    pr.has1 = has1;
+    const int L = pr.lim1;
+    const int chunk = ((L + P.nsplit - 1) / P.nsplit + kStepTokens - 1) / kStepTokens * kStepTokens;
+    const int t0 = min(L, s * chunk);
+    const int t1 = min(L, t0 + chunk);
+    run_wg<KV, QF, MG, 2>(P, smem, row0, base, t0, t1, P.nsplit == 1, row0 * P.nsplit + s, false, qr, false, false,
+                          -1, pr);
+}
+
 // MG: the plan merges the split partials here (the last-arriving split of
 // each row); a separate instantiation, so that plans merged by the combine
-// launch run a kernel without the merge code.
-template <int KV, int QF, bool MG>
+// launch run a kernel without the merge code. NT: query rows per workgroup.
+template <int KV, int QF, bool MG, int NT = 1>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Fmt<KV>::kWgsPerCU, Fmt<KV>::kWgsPerCU)))
 void split_kernel(STAGE1_ARGS) {
     // Workgroups beyond the first one per compute unit were dispatched second
@@ -1488,6 +1604,10 @@ void split_kernel(STAGE1_ARGS) {
     if (blockIdx.x >= kNumCUs) __builtin_amdgcn_s_setprio(2);
     const Params P = stage1_params(q_arg, indices_arg, kv_scales_arg, nsplit_arg, uni_len_arg, uni_chunk_arg, P_arg);
     __shared__ __attribute__((aligned(16))) uint8_t smem[Layout<KV>::kBytes];
+    if constexpr (NT == 2) {
+        split_pair<KV, QF, MG>(P, smem, nblocks);
+        return;
+    }
     const int item = xcd_order(blockIdx.x, nblocks);
     const int row = item / P.nsplit, s = item % P.nsplit;
     QueryRegs<KV, QF> qr;
@@ -1910,7 +2030,19 @@ static int launch(const mla_plan_info& plan, const Params& P, hipStream_t stream
                            const_cast<float*>(P.q_amax));
         if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
     }
-    if (plan.mode == 0 && P.counters)
+    if (plan.rows_per_wg == 2) {
+        if constexpr (KV == MLA_KV_BF16 && QF == 0) {
+            if (plan.mode != 0 || P.uni_q < 2) return MLA_ERR_INVALID_ARG;
+            if (P.counters)
+                hipLaunchKernelGGL((split_kernel<KV, QF, true, 2>), dim3(plan.grid), dim3(kThreads), 0, stream, P.q,
+                                   P.indices, P.kv_scales, P.nsplit, P.uni_len, P.uni_chunk, plan.grid, P);
+            else
+                hipLaunchKernelGGL((split_kernel<KV, QF, false, 2>), dim3(plan.grid), dim3(kThreads), 0, stream, P.q,
+                                   P.indices, P.kv_scales, P.nsplit, P.uni_len, P.uni_chunk, plan.grid, P);
+        } else {
+            return MLA_ERR_INVALID_ARG;  // the planner pairs rows on the bf16 cache only
+        }
+    } else if (plan.mode == 0 && P.counters)
         hipLaunchKernelGGL((split_kernel<KV, QF, true>), dim3(plan.grid), dim3(kThreads), 0, stream, P.q, P.indices,
                            P.kv_scales, P.nsplit, P.uni_len, P.uni_chunk, plan.grid, P);
     else if (plan.mode == 0)
@@ -2008,7 +2140,7 @@ static int decode_impl(const void* q, const void* kv, const void* kv_scales, con
                        const MtpArgs* mtp = nullptr, int64_t kv_rows = 0) {
     mla_plan_info plan;
     const int rows = mtp ? mtp->total_q : batch;
-    int rc = mtp ? mtp_plan(batch, mtp->total_q, total_kv, kv_dtype, flags, &plan)
+    int rc = mtp ? mtp_plan(batch, mtp->total_q, mtp->uni_q, total_kv, kv_dtype, flags, &plan)
                  : make_plan(batch, total_kv, kv_dtype, flags, &plan);
     if (rc != MLA_OK) return rc;
     const bool dyn = q_mode == MLA_Q_SCALE_DYNAMIC;

@@ -113,10 +113,11 @@ int make_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_inf
     const int forced_splits = (flags >> MLA_FLAG_SPLITS_SHIFT) & 0xFF;
     const int forced_grid = (flags >> MLA_FLAG_GRID_SHIFT) & 0xFFF;
     if (flags & ~(MLA_FLAG_FORCE_SPLIT | MLA_FLAG_FORCE_PERSISTENT | MLA_FLAG_MIXED_LENGTHS |
-                  MLA_FLAG_COMBINE_LAUNCH | (0xFF << MLA_FLAG_SPLITS_SHIFT) | (0xFFF << MLA_FLAG_GRID_SHIFT)))
+                  MLA_FLAG_COMBINE_LAUNCH | MLA_FLAG_ROW_PER_WG | (0xFF << MLA_FLAG_SPLITS_SHIFT) |
+                  (0xFFF << MLA_FLAG_GRID_SHIFT)))
         return MLA_ERR_INVALID_ARG;
 
-    p->reserved = 0;
+    p->rows_per_wg = 1;
     if (batch == 0) {
         p->mode = 0;
         p->num_splits = 1;
@@ -157,14 +158,28 @@ int make_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_inf
     return MLA_OK;
 }
 
-int mtp_plan(int batch, int total_q, int64_t total_kv, int kv_dtype, int flags, mla_plan_info* p) {
-    if (batch < 0 || total_q < 0 || total_kv < 0 || total_kv > INT32_MAX) return MLA_ERR_INVALID_ARG;
+int mtp_plan(int batch, int total_q, int uni_q, int64_t total_kv, int kv_dtype, int flags, mla_plan_info* p) {
+    if (batch < 0 || total_q < 0 || uni_q < 0 || total_kv < 0 || total_kv > INT32_MAX) return MLA_ERR_INVALID_ARG;
     if (flags & MLA_FLAG_FORCE_PERSISTENT) return MLA_ERR_INVALID_ARG;
-    // every query row reads its sequence: the rows together see about
-    // total_kv * total_q / batch tokens (capped to the planner's range)
-    int64_t tokens = batch > 0 ? total_kv * (int64_t)total_q / batch : 0;
+    if (uni_q > 0 && (int64_t)uni_q * batch != total_q) return MLA_ERR_INVALID_ARG;
+    // On the bf16 cache (one workgroup per CU, registers to spare) a workgroup
+    // carries two query rows of a sequence, so the cache is gathered once for
+    // both: the plan runs over the row pairs, each seeing its sequence.
+    const bool pairs = kv_dtype == MLA_KV_BF16 && uni_q >= 2 && (flags & MLA_FLAG_ROW_PER_WG) == 0;
+    const int64_t work_rows = pairs ? (int64_t)batch * ((uni_q + 1) / 2) : total_q;
+    // the work rows together see about total_kv * work_rows / batch tokens (capped to the planner's range)
+    int64_t tokens = batch > 0 ? total_kv * work_rows / batch : 0;
     if (tokens > INT32_MAX) tokens = INT32_MAX;
-    return make_plan(total_q, tokens, kv_dtype, flags | MLA_FLAG_FORCE_SPLIT, p);
+    const int rc = make_plan((int)work_rows, tokens, kv_dtype, flags | MLA_FLAG_FORCE_SPLIT, p);
+    if (rc != MLA_OK || !pairs) return rc;
+    // partials and arrival counters stay per query row
+    const int s = p->num_splits;
+    const bool merge_ok = (flags & MLA_FLAG_COMBINE_LAUNCH) == 0;
+    p->rows_per_wg = 2;
+    p->num_partials = (s > 1) ? s * total_q : 0;
+    p->combine = (s > 1) ? ((s <= kMaxMergeSplits && total_q <= kMaxCounterRows && merge_ok) ? 2 : 1) : 0;
+    p->workspace_bytes = (s > 1) ? partial_bytes(p->num_partials) : 0;
+    return MLA_OK;
 }
 
 }  // namespace mla
@@ -179,9 +194,16 @@ extern "C" size_t mla_decode_workspace_size(int batch, int64_t total_kv, int kv_
     return p.workspace_bytes;
 }
 
-extern "C" size_t mla_decode_mtp_workspace_size(int batch, int total_q, int64_t total_kv, int kv_dtype, int flags) {
+extern "C" int mla_decode_mtp_plan(int batch, int total_q, int uni_q_len, int64_t total_kv, int kv_dtype, int flags,
+                                   mla_plan_info* plan) {
+    if (!plan) return MLA_ERR_INVALID_ARG;
+    return mla::mtp_plan(batch, total_q, uni_q_len, total_kv, kv_dtype, flags, plan);
+}
+
+extern "C" size_t mla_decode_mtp_workspace_size(int batch, int total_q, int uni_q_len, int64_t total_kv, int kv_dtype,
+                                                int flags) {
     mla_plan_info p;
-    if (mla::mtp_plan(batch, total_q, total_kv, kv_dtype, flags, &p) != MLA_OK) return 0;
+    if (mla::mtp_plan(batch, total_q, uni_q_len, total_kv, kv_dtype, flags, &p) != MLA_OK) return 0;
     return p.workspace_bytes;
 }
 

@@ -34,9 +34,11 @@ int heuristic_splits(int batch, int64_t total_kv, int kv_dtype, bool merge_ok);
 int heuristic_grid(int64_t total_kv, int kv_dtype);
 size_t partial_lse_offset(int num_partials);
 // Plan for total_q query rows over `batch` sequences holding total_kv cache
-// tokens (several query tokens per sequence): always split-K, made as for
-// total_q sequences of the average length.
-int mtp_plan(int batch, int total_q, int64_t total_kv, int kv_dtype, int flags, mla_plan_info* p);
+// tokens (several query tokens per sequence, uni_q each when > 0): always
+// split-K, made as for that many sequences of the average length, where a
+// "sequence" is a query row, or (bf16 cache, uni_q >= 2) a pair of rows that
+// one workgroup carries (rows_per_wg = 2; partials stay per query row).
+int mtp_plan(int batch, int total_q, int uni_q, int64_t total_kv, int kv_dtype, int flags, mla_plan_info* p);
 // Offset of the dynamic fp8 query scale's partial maxima: after the plan's
 // bytes and never inside the arrival-counter region.
 size_t q8_amax_offset(size_t plan_bytes);

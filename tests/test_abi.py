@@ -36,7 +36,7 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("mla_decode", "mla_decode_rows", "mla_decode_paged", "mla_decode_q8", "mla_decode_mtp", "mla_decode_plan",
-              "mla_decode_workspace_size", "mla_decode_q8_workspace_size", "mla_decode_mtp_workspace_size",
+              "mla_decode_workspace_size", "mla_decode_q8_workspace_size", "mla_decode_mtp_workspace_size", "mla_decode_mtp_plan",
               "mla_quantize_q8_debug", "mla_dequant_debug", "mla_hbm_read_probe", "mla_decode_noalloc",
               "mla_status_string", "mla_source_digest"):
         assert n in names
@@ -357,6 +357,42 @@ def test_mtp_plan_is_split_over_rows(mla):
     assert mla.mla_decode_mtp_workspace_size(4, 8, 4 * 8192, 1, mla.flags_for(splits=5)) == \
         mla.mla_decode_workspace_size(8, 8 * 8192, 1, mla.flags_for(splits=5))
     assert mla.mla_decode_mtp_workspace_size(4, 8, 4 * 8192, 1, mla.flags_for(persistent=True)) == 0
+    # the uniform count changes nothing off the bf16 cache
+    for fmt in (1, 2):
+        assert mla.mla_decode_mtp_plan(32, 64, 32 * 1024, fmt, 0, 2) == mla.mla_decode_mtp_plan(32, 64, 32 * 1024, fmt)
+        assert mla.mla_decode_mtp_plan(32, 64, 32 * 1024, fmt).rows_per_wg == 1
+
+
+def test_mtp_plan_pairs_rows_on_the_bf16_cache(mla):
+    """bf16 cache, uniform count n >= 2: workgroups carry row pairs, planned like batch x ceil(n / 2)
+    sequences; partials and counters stay per query row."""
+    for n in (2, 3, 4, 5):
+        B, L = 16, 1024
+        p = mla.mla_decode_mtp_plan(B, B * n, B * L, 0, 0, n)
+        pairs = B * ((n + 1) // 2)
+        single = mla.mla_decode_plan(pairs, pairs * L, 0, mla.FLAG_FORCE_SPLIT)
+        assert p.rows_per_wg == 2 and p.mode == 0
+        assert p.num_splits == single.num_splits and p.grid == single.grid == p.num_splits * pairs
+        s = p.num_splits
+        assert p.num_partials == (s * B * n if s > 1 else 0)
+        assert p.combine == (0 if s == 1 else 2 if s <= 4 else 1)
+        assert p.workspace_bytes == mla.mla_decode_mtp_workspace_size(B, B * n, B * L, 0, 0, n)
+        assert p.workspace_bytes >= (mla.WORKSPACE_COUNTER_BYTES + p.num_partials * 16 * 513 * 4 if s > 1 else 0)
+    # the headline shape: 64 x 8192, two tokens -> the single-token plan's grid
+    p = mla.mla_decode_mtp_plan(64, 128, 64 * 8192, 0, 0, 2)
+    one = mla.mla_decode_plan(64, 64 * 8192, 0)
+    assert (p.rows_per_wg, p.num_splits, p.grid, p.combine) == (2, one.num_splits, one.grid, one.combine)
+    assert p.num_partials == 2 * one.num_partials
+    # one row per workgroup: on request, for one token, and for ragged counts
+    assert mla.mla_decode_mtp_plan(16, 32, 16 * 1024, 0, mla.FLAG_ROW_PER_WG, 2).rows_per_wg == 1
+    assert mla.mla_decode_mtp_plan(16, 16, 16 * 1024, 0, 0, 1).rows_per_wg == 1
+    assert mla.mla_decode_mtp_plan(16, 32, 16 * 1024, 0, 0, 0).rows_per_wg == 1
+    # forced splits and the combine launch carry over; a count that does not match is rejected
+    p = mla.mla_decode_mtp_plan(3, 9, 3000, 0, mla.flags_for(splits=3) | mla.FLAG_COMBINE_LAUNCH, 3)
+    assert (p.rows_per_wg, p.num_splits, p.grid, p.combine, p.num_partials) == (2, 3, 18, 1, 27)
+    with pytest.raises(mla.MlaError):
+        mla.mla_decode_mtp_plan(3, 10, 3000, 0, 0, 3)
+    assert mla.mla_decode_mtp_workspace_size(3, 10, 3000, 0, 0, 3) == 0
 
 
 def test_batch_zero_is_a_noop(raw_lib):

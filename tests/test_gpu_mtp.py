@@ -73,7 +73,7 @@ def run_mtp(mla, case, q, qo, dev, causal, uni=0, flags=0, paged=None, ws_nan=Tr
         indptr = torch.from_numpy(paged["kv_indptr"]).to(dev)
         indices = torch.from_numpy(paged["kv_indices"]).to(dev)
         last = torch.from_numpy(paged["kv_last_page_len"]).to(dev)
-    need = mla.mla_decode_mtp_workspace_size(case.batch, TQ, case.total_kv, case.kv_dtype, flags)
+    need = mla.mla_decode_mtp_workspace_size(case.batch, TQ, case.total_kv, case.kv_dtype, flags, uni)
     ws = None
     if need:
         ws = mla.new_workspace(need, dev, poison=ws_nan)
@@ -105,10 +105,11 @@ def test_mtp_uniform(mla, orc, dev, kv_dtype, qlen):
 
 @pytest.mark.parametrize("kv_dtype", DTYPES)
 def test_mtp_uniform_equals_ragged_indptr(mla, dev, kv_dtype):
-    """The same uniform query counts given as uni_q_len or through qo_indptr give identical results."""
+    """The same uniform query counts given as uni_q_len or through qo_indptr give identical results
+    (one query row per workgroup in both: on the bf16 cache the uniform call would pair rows)."""
     case = syn.make_case(4, [100, 33, 512, 7], kv_dtype, seed=540)
     q, qo = syn.make_mtp_query([3] * 4, seed=541)
-    a = run_mtp(mla, case, q, qo, dev, True, uni=3)
+    a = run_mtp(mla, case, q, qo, dev, True, uni=3, flags=mla.FLAG_ROW_PER_WG)
     b = run_mtp(mla, case, q, qo, dev, True, uni=0)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
@@ -200,3 +201,85 @@ def test_mtp_one_token_ragged_indptr_matches_uniform(mla, dev, kv_dtype):
     a = run_mtp(mla, case, case.q, qo, dev, True, uni=1)
     b = run_mtp(mla, case, case.q, qo, dev, False, uni=0)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---- two query rows per workgroup (bf16 cache, uniform query count >= 2) ----
+
+@pytest.mark.parametrize("qlen", [2, 3, 4, 5])
+@pytest.mark.parametrize("causal", [False, True])
+def test_mtp_pairs(mla, orc, dev, qlen, causal):
+    """Row pairs on the bf16 cache: odd counts (a last row alone), sequences shorter than the
+    query count (the earlier row of a pair sees nothing), an empty sequence, ragged cache lengths
+    across tile and step boundaries."""
+    lens = [300, 0, 1, 2, 64, 1100, 33]
+    case = syn.make_case(len(lens), lens, syn.KV_BF16, seed=600 + qlen, shuffle=True, extra_rows=5)
+    q, qo = syn.make_mtp_query([qlen] * len(lens), seed=610 + qlen)
+    assert mla.mla_decode_mtp_plan(case.batch, q.shape[0], case.total_kv, syn.KV_BF16, 0, qlen).rows_per_wg == 2
+    check(run_mtp(mla, case, q, qo, dev, causal, uni=qlen), mtp_ref(orc, case, q, qo, causal),
+          f"mtp pairs q{qlen} causal={causal}")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 4, 8, 64])
+def test_mtp_pairs_forced_splits(mla, orc, dev, splits):
+    """Every merge form: one split (final rows), 2-4 splits (merged per row by the last-arriving
+    split workgroup), more (combine launch); splits past a short sequence's end are empty."""
+    case = syn.make_case(3, [900, 130, 5], syn.KV_BF16, seed=620 + splits)
+    q, qo = syn.make_mtp_query([3] * 3, seed=621)
+    f = mla.flags_for(splits=splits)
+    p = mla.mla_decode_mtp_plan(3, 9, case.total_kv, syn.KV_BF16, f, 3)
+    assert p.rows_per_wg == 2 and p.num_splits == splits and p.grid == splits * 3 * 2
+    check(run_mtp(mla, case, q, qo, dev, True, uni=3, flags=f), mtp_ref(orc, case, q, qo, True),
+          f"mtp pairs splits={splits}")
+
+
+def test_mtp_pairs_combine_launch(mla, orc, dev):
+    """Two to four splits merged by the combine launch instead of in stage 1."""
+    case = syn.make_case(2, [700, 260], syn.KV_BF16, seed=630)
+    q, qo = syn.make_mtp_query([2, 2], seed=631)
+    f = mla.flags_for(splits=3) | mla.FLAG_COMBINE_LAUNCH
+    assert mla.mla_decode_mtp_plan(2, 4, case.total_kv, syn.KV_BF16, f, 2).combine == 1
+    check(run_mtp(mla, case, q, qo, dev, True, uni=2, flags=f), mtp_ref(orc, case, q, qo, True), "mtp pairs combine")
+
+
+def test_mtp_pairs_paged(mla, orc, dev):
+    lens = [17, 8, 300, 1]
+    case, paged = syn.make_paged_case(4, lens, syn.KV_BF16, 8, seed=640, extra_pages=2)
+    q, qo = syn.make_mtp_query([3] * 4, seed=641)
+    check(run_mtp(mla, case, q, qo, dev, True, uni=3, paged=paged),
+          mtp_ref(orc, oracle_tokens(orc, case, paged), q, qo, True), "mtp pairs paged")
+
+
+def test_mtp_pairs_repeated_calls_bitwise(mla, dev):
+    """Queued calls on one workspace (the stage-1 merge's counters reused) are bit-identical."""
+    case = syn.make_case(4, [600, 90, 1000, 3], syn.KV_BF16, seed=650)
+    q, qo = syn.make_mtp_query([2] * 4, seed=651)
+    f = mla.flags_for(splits=4)
+    assert mla.mla_decode_mtp_plan(4, 8, case.total_kv, syn.KV_BF16, f, 2).combine == 2
+    ref = run_mtp(mla, case, q, qo, dev, True, uni=2, flags=f)
+    t = to_dev(case, dev)
+    qt = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).to(dev)
+    ws = mla.new_workspace(mla.mla_decode_mtp_workspace_size(4, 8, case.total_kv, syn.KV_BF16, f, 2), dev)
+    outs = []
+    for _ in range(20):
+        out = torch.empty((8, 16, 512), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((8, 16), dtype=torch.float32, device=dev)
+        mla.mla_decode_mtp(qt, None, t["kv"], t["kv_scales"], t["kv_indptr"], t["kv_indices"], out, lse, total_q=8,
+                           causal=True, total_kv=case.total_kv, kv_dtype=syn.KV_BF16, uni_q_len=2, workspace=ws,
+                           flags=f)
+        outs.append((out, lse))
+    torch.cuda.synchronize()
+    assert int(ws[:mla.WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0
+    for out, lse in outs:
+        assert np.array_equal(out.float().cpu().numpy(), ref[0]) and np.array_equal(lse.cpu().numpy(), ref[1])
+
+
+def test_mtp_pairs_full_size_sampled(mla, orc, dev):
+    """bf16 64 x 8192 with two causal query tokens per sequence, default plan (row pairs);
+    rows sampled across the batch."""
+    case = syn.make_workload("bf16_b64_kv8192")
+    q, qo = syn.make_mtp_query([2] * case.batch, seed=660)
+    assert mla.mla_decode_mtp_plan(case.batch, q.shape[0], case.total_kv, syn.KV_BF16, 0, 2).rows_per_wg == 2
+    go, gl = run_mtp(mla, case, q, qo, dev, True, uni=2, ws_nan=False)
+    TQ = q.shape[0]
+    sample = sorted({0, 1, 2, 63, 64, TQ // 2 + 1, TQ - 2, TQ - 1})
+    check((go[sample], gl[sample]), mtp_ref(orc, case, q, qo, True, rows=sample), "mtp pairs bf16 64x8192 q2")
