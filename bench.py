@@ -78,6 +78,9 @@ def parse_args():
     ap.add_argument("--no-mtp-grid", action="store_true", help="skip timing the several-query-token variants")
     ap.add_argument("--no-mixed-grid", action="store_true", help="skip timing the mixed-length batches")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay leg")
+    ap.add_argument("--phases", nargs="*", metavar="WORKLOAD", default=None,
+                    help="load the measurement build (phase timestamps) and print the per-phase timeline of "
+                         "these workloads' cold calls (default: the five measured workloads)")
     ap.add_argument("--summarise", metavar="DIR", default=None,
                     help="write the profiles/ summaries from the rocprofv3 runs under DIR and exit (no GPU)")
     return ap.parse_args()
@@ -303,6 +306,76 @@ def measure_graph(name, args, dev, flush):
             "effective_kv_GBps": case.kv_bytes() / (statistics.median(us) * 1e-6) / 1e9}
 
 
+TICK_US = 0.01  # s_memrealtime runs at 100 MHz
+
+
+def phases(args):
+    """The stage-1 and combine workgroups' timelines from the measurement build
+    (include/mla_decode_phases.h): cold calls as in measure(), each workgroup's
+    phase stamps read back after the call. Per call, times are relative to the
+    first stage-1 workgroup's entry; each figure is the median over calls of a
+    median or maximum over the workgroups. Prints a markdown table."""
+    import numpy as np
+    import torch
+
+    import mla_decode_02_amd as mla
+    import synthetic as syn
+
+    assert mla.LIB_PATH.endswith("libmla_decode_phases.so"), mla.LIB_PATH
+    dev = torch.device("cuda:0")
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    names = args.phases or list(syn.WORKLOADS)
+    steps = min(args.steps, 30)
+    print(f"Phase timeline of the stage-1 and combine workgroups (measurement build, source digest "
+          f"`{mla.mla_source_digest()}`; {steps} cold calls each, after {args.warmup} warm-up calls; "
+          "us from the first stage-1 workgroup's entry; med / max over the workgroups, median over calls)\n")
+    print("| workload | plan | entry skew med / max | query + index med | first rows landed med | token steps med / "
+          "max | epilogue stores med | stage-1 merge med / max | stage-1 end med / max | combine start | "
+          "combine end |")
+    print("|" + "---|" * 11)
+    for name in names:
+        case = syn.make_workload(name)
+        q, kv, sc, indptr, indices = upload(case, dev)
+        out = torch.empty((case.batch, 16, 512), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((case.batch, 16), dtype=torch.float32, device=dev)
+        plan = plan_of(mla, case, args.flags)
+        st = torch.zeros(plan.grid * 8, dtype=torch.int64, device=dev)
+        comb = torch.zeros(64 * case.batch * 2, dtype=torch.int64, device=dev)
+        mla.mla_phase_buffers(st, comb)
+        call = prepare(mla, case, q, kv, sc, indptr, indices, out, lse, args.flags, dev)
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        rows = []
+        for _ in range(steps):
+            st.zero_()
+            comb.zero_()
+            flush_read(flush)
+            call()
+            torch.cuda.synchronize()
+            s = st.view(-1, 8).cpu().numpy().astype(np.int64)
+            c = comb.view(-1, 2).cpu().numpy().astype(np.int64)
+            t0 = s[:, 0].min()
+            ok = s[:, 2] > 0  # workgroups that attended tokens
+            d = lambda a, b: (s[ok, b] - s[ok, a]) * TICK_US  # noqa: E731
+            cw = c[:, 0] > 0
+            rows.append([np.median((s[:, 0] - t0) * TICK_US), np.max((s[:, 0] - t0) * TICK_US),
+                         np.median(d(0, 1)), np.median(d(1, 2)), np.median(d(2, 3)), np.max(d(2, 3)),
+                         np.median(d(3, 4)), np.median(d(4, 5)), np.max(d(4, 5)),
+                         np.median((s[:, 5] - t0) * TICK_US), np.max((s[:, 5] - t0) * TICK_US),
+                         (c[cw, 0].min() - t0) * TICK_US if cw.any() else float("nan"),
+                         (c[cw, 1].max() - t0) * TICK_US if cw.any() else float("nan")])
+        mla.mla_phase_buffers(None, None)
+        r = np.median(np.array(rows), axis=0)
+        pl = f"{plan.num_splits} splits, {plan.grid} WGs, " + ("none", "combine launch", "merged in stage 1")[plan.combine]
+        cs = "—" if np.isnan(r[11]) else f"{r[11]:.2f}"
+        ce = "—" if np.isnan(r[12]) else f"{r[12]:.2f}"
+        print(f"| {name} | {pl} | {r[0]:.2f} / {r[1]:.2f} | {r[2]:.2f} | {r[3]:.2f} | {r[4]:.2f} / {r[5]:.2f} | "
+              f"{r[6]:.2f} | {r[7]:.2f} / {r[8]:.2f} | {r[9]:.2f} / {r[10]:.2f} | {cs} | {ce} |", flush=True)
+        del q, kv, sc, indptr, indices, out, lse, st, comb, call
+        torch.cuda.empty_cache()
+
+
 def cpu_baseline(case, target_s):
     """Time the fp64 oracle on a bounded sample of sequences; scale to the whole call."""
     import oracle
@@ -423,6 +496,10 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the decode path runs on a "
               "single MI355X (decode would shard by batch, one share per GPU).", file=sys.stderr)
         sys.exit(2)
+    if args.phases is not None:
+        os.environ["MLA_DECODE_LIBRARY"] = "phases"  # before the package is imported
+        phases(args)
+        return
     import torch
 
     import mla_decode_02_amd as mla

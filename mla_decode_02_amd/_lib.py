@@ -19,7 +19,11 @@ import torch
 from . import build as _build
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmla_decode.so")
+# MLA_DECODE_LIBRARY=phases loads the measurement build of the same sources,
+# whose kernels record phase timestamps (include/mla_decode_phases.h); only
+# bench.py --phases sets it. Otherwise the decode library is loaded.
+PHASES = os.environ.get("MLA_DECODE_LIBRARY", "") == "phases"
+LIB_PATH = os.path.join(_HERE, "libmla_decode_phases.so" if PHASES else "libmla_decode.so")
 
 NUM_HEADS, QK_DIM, V_DIM = 16, 576, 512
 KV_BF16, KV_FP8_E4M3, KV_MXFP4 = 0, 1, 2
@@ -130,6 +134,11 @@ def _load():
     lib.mla_status_string.argtypes = [i32]
     lib.mla_source_digest.restype = ctypes.c_char_p
     lib.mla_source_digest.argtypes = []
+    if PHASES:
+        if not hasattr(lib, "mla_phase_buffers"):
+            raise ImportError(f"{LIB_PATH} is not the measurement build (no mla_phase_buffers)")
+        lib.mla_phase_buffers.restype = i32
+        lib.mla_phase_buffers.argtypes = [vp, vp]
     # A library built from other sources than the ones beside it (an edit not
     # followed by a build) would run kernels that are not the tree's: refuse it.
     built = lib.mla_source_digest().decode()
@@ -147,6 +156,19 @@ _lib = _load()
 
 def mla_status_string(status: int) -> str:
     return _lib.mla_status_string(int(status)).decode()
+
+
+def mla_phase_buffers(stage1, combine) -> None:
+    """Measurement build only: the int64 device tensors the next launches write
+    their phase timestamps into (include/mla_decode_phases.h), or None."""
+    if not PHASES:
+        raise RuntimeError("phase timestamps need the measurement build (MLA_DECODE_LIBRARY=phases)")
+    for t in (stage1, combine):
+        _need(t is None or (t.is_cuda and t.dtype == torch.int64 and t.is_contiguous()),
+              "phase buffers must be contiguous int64 device tensors")
+    rc = _lib.mla_phase_buffers(_ptr(stage1), _ptr(combine))
+    if rc != 0:
+        raise MlaError(rc, "mla_phase_buffers")
 
 
 def mla_source_digest() -> str:

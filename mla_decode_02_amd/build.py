@@ -14,6 +14,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla_decode.so")
+# The measurement build: the same sources with the kernels' phase timestamps
+# (MLA_PHASE_STAMPS=1, include/mla_decode_phases.h); used by bench.py --phases.
+PHASES_LIB = os.path.join(PKG, "libmla_decode_phases.so")
 
 # Every HIP translation unit is built for gfx950 only, without packed-fp32
 # instruction selection (v_pk_{add,mul,fma}_f32).
@@ -28,7 +31,8 @@ HIP_FLAGS = [
 
 # The files the library is compiled from, in the order the digest reads them.
 SOURCES = [os.path.join(CSRC, "mla_decode.hip"), os.path.join(CSRC, "mla_plan.cpp"),
-           os.path.join(CSRC, "mla_plan.h"), os.path.join(INCLUDE, "mla_decode.h")]
+           os.path.join(CSRC, "mla_plan.h"), os.path.join(INCLUDE, "mla_decode.h"),
+           os.path.join(INCLUDE, "mla_decode_phases.h")]
 
 
 def source_digest() -> str:
@@ -49,8 +53,9 @@ def _run(cmd, verbose):
     subprocess.check_call(cmd)
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the HIP kernels and the host planner and link the shared library."""
+def build(verbose: bool = False, phases: bool = True) -> str:
+    """Compile the HIP kernels and the host planner and link the shared library
+    (and, with phases, the measurement build beside it)."""
     obj_dir = os.path.join(PKG, "_build")
     os.makedirs(obj_dir, exist_ok=True)
     plan_o = os.path.join(obj_dir, "mla_plan.o")
@@ -63,6 +68,13 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, hip_o, plan_o], verbose)
     os.replace(tmp, LIB)
+    if phases:
+        phases_o = os.path.join(obj_dir, "mla_decode_phases.o")
+        _run(["hipcc", *HIP_FLAGS, "-DMLA_PHASE_STAMPS=1", "-I", INCLUDE, "-I", CSRC,
+              "-c", os.path.join(CSRC, "mla_decode.hip"), "-o", phases_o], verbose)
+        tmp = PHASES_LIB + ".tmp"
+        _run(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, phases_o, plan_o], verbose)
+        os.replace(tmp, PHASES_LIB)
     return LIB
 
 

@@ -47,6 +47,7 @@
 #include <mutex>
 
 #include "mla_decode.h"
+#include "mla_decode_phases.h"
 #include "mla_plan.h"
 
 namespace mla {
@@ -65,6 +66,55 @@ typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kThreads = 64 * kWaves;
+
+// ---------------------------------------------------------------------------
+// Phase timestamps, in the measurement build only (MLA_PHASE_STAMPS=1, the
+// library libmla_decode_phases.so; the decode library is built without them
+// and contains none of this). Thread 0 of each stage-1 workgroup records the
+// 100 MHz real-time counter (s_memrealtime) at the kPhases points below into
+// the buffer the host set with mla_phase_buffers, [workgroup][phase]; thread
+// 0 of each combine workgroup records its start and end, [workgroup][2].
+//   0 kernel entry
+//   1 query registers and the first index window in hand
+//   2 the first step's rows landed in LDS (after its barrier)
+//   3 every step of the range done
+//   4 the epilogue's stores complete (every thread)
+//   5 the stage-1 merge done (plans that merge in stage 1; else as 4)
+// A persistent workgroup attends several sequences: phases 1-4 are those of
+// its last one.
+// ---------------------------------------------------------------------------
+#ifndef MLA_PHASE_STAMPS
+#define MLA_PHASE_STAMPS 0
+#endif
+constexpr int kPhases = 8;
+#if MLA_PHASE_STAMPS
+__device__ uint64_t* g_phase_stage1;
+__device__ uint64_t* g_phase_combine;
+#endif
+__device__ __forceinline__ void phase_stamp(int k) {
+#if MLA_PHASE_STAMPS
+    if (threadIdx.x == 0 && g_phase_stage1)
+        g_phase_stage1[(size_t)blockIdx.x * kPhases + k] = __builtin_amdgcn_s_memrealtime();
+#else
+    (void)k;
+#endif
+}
+// Phase 4: in the measurement build, wait for every thread's stores first.
+__device__ __forceinline__ void phase_stamp_stores_done() {
+#if MLA_PHASE_STAMPS
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    phase_stamp(4);
+#endif
+}
+__device__ __forceinline__ void phase_stamp_combine(int k) {
+#if MLA_PHASE_STAMPS
+    if (threadIdx.x == 0 && g_phase_combine)
+        g_phase_combine[(size_t)blockIdx.x * 2 + k] = __builtin_amdgcn_s_memrealtime();
+#else
+    (void)k;
+#endif
+}
 constexpr int kTile = 16;                // tokens per MFMA tile
 static_assert(kStepTokens == 2 * kTile, "a step is two MFMA tiles");
 constexpr int kKSteps = kDqk / 32;       // 18 MFMA k-steps over the 576 score dims
@@ -1253,6 +1303,7 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
     // touches the index window (so have the caller's early gathers, issued
     // after it: no gathers are in flight past this point).
     if (idx_dma) wait_vmcnt<0>();
+    phase_stamp(1);
     if constexpr (QF) {
         if (P.q_amax) {
             q_scale = q8_dynamic_scale(q_part, reinterpret_cast<float*>(sbuf), tid);
@@ -1342,6 +1393,7 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
         }
         wait_own<KV>(min(D - 1, nsteps - 1), hf);
         __syncthreads();  // step 0 has landed (and the query codes are written)
+        if (w0 == t0) phase_stamp(2);
         if constexpr (kMx) {
             if (w0 == t0) {
                 // B operand of block u for head r: dims 128 u + 16 G + (0..15) and 128 u + 64 + 16 G + (0..15);
@@ -1451,6 +1503,7 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
         }
     }
 
+    phase_stamp(3);
     // ---- epilogue: every wave of a row holds the same m and l; it writes its own columns ----
     // One row: query row b, the wave's blocks kWaveBlocks * wave + j. Two rows
     // (NT = 2): wave w writes row b + w / 2 (absent: nothing), blocks
@@ -1502,12 +1555,14 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
             if (lse_wave && G == 0) P.part_lse[sl * kHeads + r] = lse_r;
         }
     }
+    phase_stamp_stores_done();
     if constexpr (MG) {
         if (!final) {
             merge_if_last(P, b, smem);
             if (NT == 2 && pr.has1) merge_if_last(P, b + 1, smem);
         }
     }
+    phase_stamp(5);
 }
 
 // Workgroups are handed to the eight XCDs round-robin (workgroup x to XCD
@@ -1596,6 +1651,7 @@ __device__ void split_pair(const Params& P, uint8_t* smem, int nblocks) {
 template <int KV, int QF, bool MG, int NT = 1>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Fmt<KV>::kWgsPerCU, Fmt<KV>::kWgsPerCU)))
 void split_kernel(STAGE1_ARGS) {
+    phase_stamp(0);
     // Workgroups beyond the first one per compute unit were dispatched second
     // to their CU; the SIMD arbiter favours older waves, so these run at a
     // higher wave priority to finish together with the first (MXFP4 32 x 8k
@@ -1666,6 +1722,7 @@ __device__ __forceinline__ int64_t share_start(int64_t p, int64_t T, int64_t G) 
 template <int KV, int QF>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Fmt<KV>::kWgsPerCU, Fmt<KV>::kWgsPerCU)))
 void persistent_kernel(STAGE1_ARGS) {
+    phase_stamp(0);
     if (blockIdx.x >= kNumCUs) __builtin_amdgcn_s_setprio(2);  // as in split_kernel (MXFP4 mixed lengths 46.0 -> 45.6 us)
     const Params P = stage1_params(q_arg, indices_arg, kv_scales_arg, nsplit_arg, uni_len_arg, uni_chunk_arg, P_arg);
     __shared__ __attribute__((aligned(16))) uint8_t smem[Layout<KV>::kBytes];
@@ -1750,6 +1807,7 @@ static int combine_items(int parts) {
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* part_o_arg, const float* part_lse_arg,
                                                                int mode_arg, int nsplit_arg, int items_arg,
                                                                int nblocks, CombineParams C_arg) {
+    phase_stamp_combine(0);
     CombineParams C = C_arg;
     C.part_o = part_o_arg;
     C.part_lse = part_lse_arg;
@@ -1848,6 +1906,11 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* part
         *reinterpret_cast<bf16x4*>(C.out + ((int64_t)b * kHeads + h) * kDv + d) = pk;
         if (quad == 0 && chunk == 0 && C.lse) C.lse[(int64_t)b * kHeads + h] = (Wt > 0.f) ? M + logf(Wt) : -INFINITY;
     }
+#if MLA_PHASE_STAMPS
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    phase_stamp_combine(1);
+#endif
 }
 
 // Decode check: rows -> fp32 through the stage-1 staging (issue_half) and the
@@ -2333,6 +2396,18 @@ extern "C" int mla_quantize_q8_debug(const void* q, int batch, float* q_scale, i
     hipLaunchKernelGGL(q8_debug_kernel, dim3(batch), dim3(256), 0, s, P, codes);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
+
+#if MLA_PHASE_STAMPS
+// Measurement build only (include/mla_decode_phases.h).
+extern "C" int mla_phase_buffers(uint64_t* stage1, uint64_t* combine) {
+    using namespace mla;
+    int rc = check_device();
+    if (rc != MLA_OK) return rc;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_phase_stage1), &stage1, sizeof stage1) != hipSuccess) return MLA_ERR_HIP;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_phase_combine), &combine, sizeof combine) != hipSuccess) return MLA_ERR_HIP;
+    return MLA_OK;
+}
+#endif
 
 extern "C" int mla_hbm_read_probe(const void* buf, size_t bytes, void* stream) {
     using namespace mla;

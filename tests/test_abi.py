@@ -53,6 +53,19 @@ def test_library_is_built_from_the_tree_sources(mla, raw_lib):
     assert f().decode() == build.source_digest() == mla.mla_source_digest()
 
 
+def test_phase_stamps_only_in_the_measurement_build(mla, raw_lib):
+    """The decode library records no timestamps and does not export the phase
+    buffers; the measurement build of the same sources does, with the same digest."""
+    import mla_decode_02_amd.build as build
+
+    assert not hasattr(raw_lib, "mla_phase_buffers")
+    assert not mla.PHASES and mla.LIB_PATH.endswith("libmla_decode.so")
+    ph = ctypes.CDLL(build.PHASES_LIB)
+    assert hasattr(ph, "mla_phase_buffers")
+    ph.mla_source_digest.restype = ctypes.c_char_p
+    assert ph.mla_source_digest().decode() == mla.mla_source_digest()
+
+
 def test_source_digest_follows_every_source_file(tmp_path, monkeypatch):
     """A change to any one source file (kernel, planner, planner header, C ABI
     header) changes the digest."""
