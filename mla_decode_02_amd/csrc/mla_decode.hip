@@ -1239,6 +1239,37 @@ __device__ void merge_if_last(const Params& P, int row, uint8_t* smem) {
 // QF = 1: fp8 query. Q is quantised here (static scale read, or the dynamic
 // scale reduced from the partial maxima); `scale_out` makes this workgroup
 // publish a dynamic scale.
+// Two stage-1 workgroups share a compute unit on the fp8 and MXFP4 caches
+// (launch indices x and x + 256), and the SIMD arbiter favours older waves,
+// so without help the second one finishes last: it runs at priority 2 (MXFP4
+// 32 x 8k 38.2 -> 37.8 us, fp8 256 x 8k 213.3 -> 211.5 us when introduced).
+// That fixed boost overshoots on long ranges: per-workgroup timestamps
+// showed the second workgroups ending about 3.3 us before the first on fp8
+// 64 x 8k (MXFP4 32 x 8k 3.6 us, where priority 1 measured the same). The
+// fp8 plans with two workgroups per compute unit and long ranges (TURNS)
+// therefore let the two take turns at priority 2 step by step instead, which
+// brought the two classes within 1.7 us of each other and the last
+// workgroup's end 1.3 us earlier. A separate instantiation, because the
+// priority switch in the loop costs short ranges about 0.4 us even where it
+// is not taken.
+template <bool TURNS>
+__device__ __forceinline__ void second_wg_priority() {
+    if constexpr (!TURNS) {
+        if (blockIdx.x >= kNumCUs) __builtin_amdgcn_s_setprio(2);
+    }
+}
+template <bool TURNS>
+__device__ __forceinline__ void take_turns_priority(int s) {
+    if constexpr (TURNS) {
+        if ((s + (blockIdx.x >= kNumCUs ? 1 : 0)) & 1) __builtin_amdgcn_s_setprio(2);
+        else __builtin_amdgcn_s_setprio(0);
+    }
+}
+// Tokens per workgroup from which fp8 plans of more than one workgroup per
+// compute unit take turns (fp8 64 x 8k has 1024: -1.4 us; 256 x 1k has 512:
+// +0.5 us with turns).
+constexpr int kTurnsMinTokens = 1024;
+
 // Two query rows per workgroup (NT = 2): row t of the pair sees the sequence's
 // positions [0, lim_t); has1 is false when the pair has no second row (the
 // last row of an odd count).
@@ -1247,7 +1278,7 @@ struct RowPair {
     bool has1 = false;
 };
 
-template <int KV, int QF, bool MG = false, int NT = 1>
+template <int KV, int QF, bool MG = false, int NT = 1, bool TURNS = false>
 __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, int t1, bool final, int slot,
                        bool scale_out, QueryRegs<KV, QF, NT>& qr, bool idx_dma, bool idx_staged,
                        int64_t early_first = -1, RowPair pr = RowPair{}) {
@@ -1463,6 +1494,7 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
         for (int s = 0; s < nsteps; ++s) {
             if (s + 1 < nsteps) wait_own<KV>(min(D - 2, nsteps - 2 - s), hf);
             __syncthreads();
+            take_turns_priority<TURNS>(s);
             if (s + D < nsteps) issue_step(s + D);  // into the slot of step s - 1
             const f32x4* sb = sbuf + (s & 1) * (kWaves * 64);
             f32x4 sc[2];
@@ -1648,16 +1680,11 @@ __device__ void split_pair(const Params& P, uint8_t* smem, int nblocks) {
 // MG: the plan merges the split partials here (the last-arriving split of
 // each row); a separate instantiation, so that plans merged by the combine
 // launch run a kernel without the merge code. NT: query rows per workgroup.
-template <int KV, int QF, bool MG, int NT = 1>
+template <int KV, int QF, bool MG, int NT = 1, bool TURNS = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Fmt<KV>::kWgsPerCU, Fmt<KV>::kWgsPerCU)))
 void split_kernel(STAGE1_ARGS) {
     phase_stamp(0);
-    // Workgroups beyond the first one per compute unit were dispatched second
-    // to their CU; the SIMD arbiter favours older waves, so these run at a
-    // higher wave priority to finish together with the first (MXFP4 32 x 8k
-    // 38.2 -> 37.8 us, fp8 256 x 8k 213.3 -> 211.5 us; one workgroup per CU
-    // unchanged).
-    if (blockIdx.x >= kNumCUs) __builtin_amdgcn_s_setprio(2);
+    second_wg_priority<TURNS>();
     const Params P = stage1_params(q_arg, indices_arg, kv_scales_arg, nsplit_arg, uni_len_arg, uni_chunk_arg, P_arg);
     __shared__ __attribute__((aligned(16))) uint8_t smem[Layout<KV>::kBytes];
     if constexpr (NT == 2) {
@@ -1711,7 +1738,7 @@ void split_kernel(STAGE1_ARGS) {
     const int t0 = min(L, s * chunk);
     const int t1 = min(L, t0 + chunk);
     const bool staged = idx_dma && base == row * Lu && L == Lu;  // then t0, t1 are t0u, t1u
-    run_wg<KV, QF, MG>(P, smem, row, base, t0, t1, P.nsplit == 1, row * P.nsplit + s, blockIdx.x == 0, qr, idx_dma,
+    run_wg<KV, QF, MG, 1, TURNS>(P, smem, row, base, t0, t1, P.nsplit == 1, row * P.nsplit + s, blockIdx.x == 0, qr, idx_dma,
                        staged, early_first);
 }
 
@@ -1723,7 +1750,7 @@ template <int KV, int QF>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Fmt<KV>::kWgsPerCU, Fmt<KV>::kWgsPerCU)))
 void persistent_kernel(STAGE1_ARGS) {
     phase_stamp(0);
-    if (blockIdx.x >= kNumCUs) __builtin_amdgcn_s_setprio(2);  // as in split_kernel (MXFP4 mixed lengths 46.0 -> 45.6 us)
+    second_wg_priority<false>();
     const Params P = stage1_params(q_arg, indices_arg, kv_scales_arg, nsplit_arg, uni_len_arg, uni_chunk_arg, P_arg);
     __shared__ __attribute__((aligned(16))) uint8_t smem[Layout<KV>::kBytes];
     const int64_t T = P.total, Gn = P.grid;
@@ -2093,6 +2120,8 @@ static int launch(const mla_plan_info& plan, const Params& P, hipStream_t stream
                            const_cast<float*>(P.q_amax));
         if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
     }
+    const bool turns = KV == MLA_KV_FP8_E4M3 && plan.mode == 0 && plan.rows_per_wg == 1 && plan.grid > kNumCUs &&
+                       (int64_t)P.total >= (int64_t)kTurnsMinTokens * plan.grid;
     if (plan.rows_per_wg == 2) {
         if constexpr (KV == MLA_KV_BF16 && QF == 0) {
             if (plan.mode != 0 || P.uni_q < 2) return MLA_ERR_INVALID_ARG;
@@ -2104,6 +2133,16 @@ static int launch(const mla_plan_info& plan, const Params& P, hipStream_t stream
                                    P.indices, P.kv_scales, P.nsplit, P.uni_len, P.uni_chunk, plan.grid, P);
         } else {
             return MLA_ERR_INVALID_ARG;  // the planner pairs rows on the bf16 cache only
+        }
+    } else if (turns) {
+        // fp8, two workgroups per compute unit, long ranges: the two take turns at priority 2
+        if constexpr (KV == MLA_KV_FP8_E4M3) {
+            if (P.counters)
+                hipLaunchKernelGGL((split_kernel<KV, QF, true, 1, true>), dim3(plan.grid), dim3(kThreads), 0, stream,
+                                   P.q, P.indices, P.kv_scales, P.nsplit, P.uni_len, P.uni_chunk, plan.grid, P);
+            else
+                hipLaunchKernelGGL((split_kernel<KV, QF, false, 1, true>), dim3(plan.grid), dim3(kThreads), 0,
+                                   stream, P.q, P.indices, P.kv_scales, P.nsplit, P.uni_len, P.uni_chunk, plan.grid, P);
         }
     } else if (plan.mode == 0 && P.counters)
         hipLaunchKernelGGL((split_kernel<KV, QF, true>), dim3(plan.grid), dim3(kThreads), 0, stream, P.q, P.indices,
