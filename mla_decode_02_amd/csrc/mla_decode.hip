@@ -1142,6 +1142,89 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t merge_rsrc(const float* p, uin
 // partials were written by workgroups on other XCDs).
 constexpr int kCoherentLoad = 0x11;
 
+// The last-arriving split's merge of S = 5..8 bf16 partials [column][head]
+// (the formula of merge_if_last), with every partial's loads in one round:
+// thread t takes the 16-byte chunks t + 256 m (m < 4) of each partial, chunk
+// k holding column k / 2, heads 8 (k % 2) .. +7. The weights
+// w_s,h = exp(lse_s,h - M_h) / sum_s exp(lse_s,h - M_h) are formed once per
+// head in LDS; the sums pass through an LDS transpose ([column][head], rows
+// padded to 17 floats against bank conflicts) so that the output rows are
+// written as whole 8-byte pieces. The ring's LDS is free here: every wave
+// has left the token loop.
+__device__ void merge_bf16(const Params& P, int row, uint8_t* smem, int S) {
+    const int tid = threadIdx.x;
+    float* s_lse = reinterpret_cast<float*>(smem + 64);  // [8][16]
+    float* s_w = s_lse + 8 * kHeads;                      // [8][16]
+    float* s_out = s_w + 8 * kHeads;                      // [512][17]
+    static_assert(64 + 16 * 8 * kHeads + 4 * kDv * 17 <= Layout<MLA_KV_MXFP4>::kBytes,
+                  "the bf16 merge's LDS fits every format's stage-1 layout");
+    // the lse values first (the weights are formed while the partials are in flight), then every partial chunk
+    const __amdgpu_buffer_rsrc_t rl = merge_rsrc(P.part_lse + (int64_t)row * S * kHeads, S * kHeads * 4);
+    float lse_t = -INFINITY;
+    if (tid < S * kHeads)
+        lse_t = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * tid, 0, kCoherentLoad));
+    const __amdgpu_buffer_rsrc_t ro = merge_rsrc(P.part_o + (int64_t)row * S * kHeads * kDv, S * kHeads * kDv * 4);
+    u32x4 v[kMaxMergeSplitsBf16][4];
+#pragma unroll
+    for (int sl = 0; sl < kMaxMergeSplitsBf16; ++sl)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            v[sl][m] = sl < S ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                    ro, 4 * sl * kHeads * kDv + 16 * (tid + 256 * m), 0, kCoherentLoad))
+                              : u32x4{0u, 0u, 0u, 0u};
+    if (tid < kMaxMergeSplitsBf16 * kHeads) s_lse[tid] = lse_t;
+    __syncthreads();
+    if (tid < kHeads) {
+        float M = -INFINITY;
+        for (int sl = 0; sl < S; ++sl) M = fmaxf(M, s_lse[sl * kHeads + tid]);
+        float W = 0.f;
+        for (int sl = 0; sl < S; ++sl) {
+            const float l = s_lse[sl * kHeads + tid];
+            if (l != -INFINITY) W += __expf(l - M);  // empty splits (lse = -inf) carry no weight
+        }
+        const float inv = (W > 0.f) ? 1.f / W : 0.f;
+        for (int sl = 0; sl < kMaxMergeSplitsBf16; ++sl) {
+            const float l = s_lse[sl * kHeads + tid];
+            s_w[sl * kHeads + tid] = (sl < S && l != -INFINITY) ? __expf(l - M) * inv : 0.f;
+        }
+        if (P.lse) P.lse[(int64_t)row * kHeads + tid] = (W > 0.f) ? M + logf(W) : -INFINITY;
+    }
+    __syncthreads();
+    const int h0 = 8 * (tid & 1);  // the heads of this thread's chunks (k % 2 = t % 2)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int col = (tid + 256 * m) >> 1;
+        float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sl = 0; sl < kMaxMergeSplitsBf16; ++sl) {
+            if (sl < S) {
+                const f32x4 w0 = *reinterpret_cast<const f32x4*>(s_w + sl * kHeads + h0);
+                const f32x4 w1 = *reinterpret_cast<const f32x4*>(s_w + sl * kHeads + h0 + 4);
+                const bf16x8 x = __builtin_bit_cast(bf16x8, v[sl][m]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    a[e] += w0[e] * (float)x[e];
+                    a[4 + e] += w1[e] * (float)x[4 + e];
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_out[col * 17 + h0 + e] = a[e];
+    }
+    __syncthreads();
+    // out row: head h = t / 16 writes columns 4 q .. 4 q + 3, q = t % 16 + 16 n
+    __bf16* out = P.out + (int64_t)row * kHeads * kDv;
+    const int h = tid >> 4;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+        const int c0 = 4 * ((tid & 15) + 16 * n);
+        bf16x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk[e] = (__bf16)s_out[(c0 + e) * 17 + h];
+        *reinterpret_cast<bf16x4*>(out + h * kDv + c0) = pk;
+    }
+}
+
 // Split-K with the merge in stage 1: the partial of this workgroup (slot
 // `slot` of query row `row`) has been written with device-coherent stores.
 // Each workgroup waits for its own stores to complete, then counts itself in
@@ -1167,6 +1250,10 @@ __device__ void merge_if_last(const Params& P, int row, uint8_t* smem) {
     }
     __syncthreads();
     if (!*flag) return;
+    if (S > kMaxMergeSplits) {
+        merge_bf16(P, row, smem, S);
+        return;
+    }
     constexpr int kBatch = 4;  // partials whose loads are in flight together
     constexpr int kQuads = kDv / 4 / 16;
     const int h = tid >> 4, q = tid & 15;
@@ -1566,13 +1653,28 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
             // device-coherent stores (written through to memory), read back by
             // whichever split workgroup of this row arrives last
             float* o = P.part_o + sl * kHeads * kDv;
+            if (P.nsplit > kMaxMergeSplits) {
+                // 5..8 splits: a bf16 partial [column][head] at the start of the
+                // slot, the four heads 4G..4G+3 of a column in one 8-byte store
+                uint64_t* ob = reinterpret_cast<uint64_t*>(o);
 #pragma unroll
-            for (int j = 0; j < kWaveBlocks * NT; ++j) {
-                const int col = dcol<KV>(vb + j, r);
+                for (int j = 0; j < kWaveBlocks * NT; ++j) {
+                    const int col = dcol<KV>(vb + j, r);
+                    bf16x4 pk;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    __hip_atomic_store(o + (4 * G + i) * kDv + col, acc.o[j][i] * inv[i], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+                    for (int i = 0; i < 4; ++i) pk[i] = (__bf16)(acc.o[j][i] * inv[i]);
+                    __hip_atomic_store(ob + (col * kHeads + 4 * G) / 4, __builtin_bit_cast(uint64_t, pk),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < kWaveBlocks * NT; ++j) {
+                    const int col = dcol<KV>(vb + j, r);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        __hip_atomic_store(o + (4 * G + i) * kDv + col, acc.o[j][i] * inv[i], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                }
             }
             if (lse_wave && G == 0)
                 __hip_atomic_store(P.part_lse + sl * kHeads + r, lse_r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -7,7 +7,9 @@
 //               splits) rounded up to the 32-token workgroup step. One partial
 //               slot per (b, s); when splits > 1 the partials of a sequence
 //               are merged by its last-arriving split workgroup (up to
-//               kMaxMergeSplits splits) or by a combine launch.
+//               kMaxMergeSplits splits; up to kMaxMergeSplitsBf16 of at least
+//               kMergeBf16MinTokens tokens each, from bf16 partials) or by a
+//               combine launch.
 //               (Flash-decoding split-K: the split partial plus log-sum-exp
 //               merge of amd-mixed-mla submission 593653, `_flash_fp8_split_s1`
 //               and `_flash_fp8_split_s2`.)
@@ -151,7 +153,13 @@ int make_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_inf
         // The last-arriving split of a row merges the row's partials alone,
         // so that merge pays only while it reads a few of them; many splits
         // (short batches of long sequences) merge in the wide combine launch.
-        const bool merge_in_stage1 = s <= kMaxMergeSplits && batch <= kMaxCounterRows && merge_ok;
+        // (not on the MXFP4 cache: bound by instruction issue, its last arrivals' longer merge
+        // lengthened the tail, 64 x 8k 59.0 -> 59.7 us, where fp8 64 x 8k gained 61.8 -> 61.1 us
+        // and bf16 32 x 8k 59.9 -> 57.8 us)
+        const bool long_splits =
+            kv_dtype != MLA_KV_MXFP4 && total_kv >= (int64_t)kMergeBf16MinTokens * s * batch;
+        const bool merge_in_stage1 = (s <= kMaxMergeSplits || (s <= kMaxMergeSplitsBf16 && long_splits)) &&
+                                     batch <= kMaxCounterRows && merge_ok;
         p->combine = (s > 1) ? (merge_in_stage1 ? 2 : 1) : 0;
         p->workspace_bytes = (s > 1) ? partial_bytes(p->num_partials) : 0;
     }

@@ -140,8 +140,11 @@ def test_heuristic_plan_invariants(mla, B, L, kv_dtype):
     if p.mode == 0:
         assert 1 <= p.num_splits <= 64
         assert p.grid == p.num_splits * B
-        # the last-arriving split merges up to 4 splits; more merge in a combine launch
-        assert p.combine == (0 if p.num_splits == 1 else 2 if p.num_splits <= 4 else 1)
+        # the last-arriving split merges up to 4 splits, or up to 8 of at least 1024 tokens each (from bf16
+        # partials); more merge in a combine launch
+        S = p.num_splits
+        merged = S <= 4 or (S <= 8 and kv_dtype != 2 and B * L >= 1024 * S * B)
+        assert p.combine == (0 if S == 1 else 2 if merged else 1)
         assert p.num_partials == (p.num_splits * B if p.num_splits > 1 else 0)
     else:
         assert 1 <= p.grid <= 4095 and p.num_partials == p.grid + B - 1 and p.combine == 1
@@ -477,8 +480,9 @@ def test_split_ranges_cover_tokens_once(L, S):
 
 def test_plan_merge_rule(mla):
     """Split-K plans of 2..4 splits merge in the last-arriving split workgroup
-    (combine = 2) unless MLA_FLAG_COMBINE_LAUNCH asks for the combine launch;
-    more splits, or more query rows than the counter region holds, use the launch.
+    (combine = 2) unless MLA_FLAG_COMBINE_LAUNCH asks for the combine launch, and
+    so do 5..8 splits of at least 1024 tokens each; more splits, shorter ones, or
+    more query rows than the counter region holds, use the launch.
     The partials always start after the counter region."""
     for s in range(1, 10):
         p = mla.mla_decode_plan(8, 8 * 4096, 1, mla.flags_for(splits=s))
@@ -488,6 +492,15 @@ def test_plan_merge_rule(mla):
         assert q.workspace_bytes == p.workspace_bytes
         if s > 1:
             assert p.workspace_bytes > mla.WORKSPACE_COUNTER_BYTES + s * 8 * 16 * 512 * 4
+    # 5..8 splits merge in stage 1 (bf16 partials) when every split holds at least 1024 tokens on average
+    for s in range(5, 10):
+        for L in (1024 * s - 1, 1024 * s, 8192):
+            p = mla.mla_decode_plan(8, 8 * L, 1, mla.flags_for(splits=s))
+            assert p.combine == (2 if s <= 8 and L >= 1024 * s else 1), (s, L)
+            assert mla.mla_decode_plan(8, 8 * L, 1, mla.flags_for(splits=s) | mla.FLAG_COMBINE_LAUNCH).combine == 1
+    assert mla.mla_decode_plan(64, 64 * 8192, 1, 0).combine == 2  # the 8-split fp8 64 x 8192 plan
+    assert mla.mla_decode_plan(8, 8 * 8192, 0, mla.flags_for(splits=8)).combine == 2  # bf16 too
+    assert mla.mla_decode_plan(8, 8 * 8192, 2, mla.flags_for(splits=8)).combine == 1  # not MXFP4
     rows = mla.WORKSPACE_COUNTER_BYTES // 4
     assert mla.mla_decode_plan(rows, rows * 64, 1, mla.flags_for(splits=2)).combine == 2
     assert mla.mla_decode_plan(rows + 1, (rows + 1) * 64, 1, mla.flags_for(splits=2)).combine == 1

@@ -502,6 +502,33 @@ def test_merge_in_stage1_against_oracle_and_combine_launch(mla, orc, dev, kv_dty
         assert np.abs(a[1][fin] - b[1][fin]).max() <= 1e-5
 
 
+@pytest.mark.parametrize("kv_dtype", [syn.KV_BF16, syn.KV_FP8])
+@pytest.mark.parametrize("lens", [[12000, 9000, 0, 12500], [20000, 13000, 3, 0]])
+def test_merge_bf16_partials_5_to_8_splits(mla, orc, dev, kv_dtype, lens):
+    """5..8 splits of at least 1024 tokens each (bf16 and fp8 caches) merge in the last-arriving
+    split from bf16 partials, all in one round: within the oracle's bounds, the same as the combine
+    launch up to the partials' rounding, the counters back at zero, and ten queued calls
+    on one workspace bitwise equal. Sequences of 3 and 0 tokens leave most or all of
+    their splits empty."""
+    case = syn.make_case(4, lens, kv_dtype, seed=95, shuffle=True)
+    ref = oracle_ref(orc, case)
+    for splits in (5, 6, 7, 8):
+        f = mla.flags_for(splits=splits)
+        assert mla.mla_decode_plan(case.batch, case.total_kv, kv_dtype, f).combine == 2
+        ws = new_workspace(mla, case, dev, f)
+        a = run_gpu(mla, case, dev, flags=f, ws=ws)
+        check(a, ref, f"bf16-partial merge, {splits} splits")
+        assert int(torch.count_nonzero(ws[: mla.WORKSPACE_COUNTER_BYTES])) == 0, "arrival counters not left at zero"
+        b = run_gpu(mla, case, dev, flags=f | mla.FLAG_COMBINE_LAUNCH)
+        assert np.abs(a[0] - b[0]).max() <= 2 * U_BF16 * max(np.abs(b[0]).max(), 1e-3)
+        fin = np.isfinite(b[1])
+        assert np.array_equal(np.isneginf(a[1]), np.isneginf(b[1]))
+        assert np.abs(a[1][fin] - b[1][fin]).max() <= 1e-5
+        for _ in range(10):
+            c = run_gpu(mla, case, dev, flags=f, ws=ws)
+            assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
+
+
 @pytest.mark.parametrize("kv_dtype", [syn.KV_FP8, syn.KV_MXFP4])
 def test_merge_in_stage1_back_to_back_calls_bitwise(mla, dev, kv_dtype):
     """The merge reads the partials in slot order whichever split arrives last,
