@@ -44,17 +44,21 @@ def _capture(fn):
     return g
 
 
-@pytest.mark.parametrize("merge_in_stage1", [False, True])
+@pytest.mark.parametrize("merge", ["launch", "merged3", "merged8"])
 @pytest.mark.parametrize("kv_dtype", DTYPES)
-def test_captured_decode_replays(mla, dev, kv_dtype, merge_in_stage1):
+def test_captured_decode_replays(mla, dev, kv_dtype, merge):
     """A captured call replays bit-identically to eager calls, with the combine
-    launch (default plan here) and with the partials merged by the last-arriving
-    split (3 splits; its arrival counters are reset inside the kernel)."""
-    case = syn.make_case(6, [1000, 3, 700, 0, 2000, 64], kv_dtype, seed=620 + kv_dtype, shuffle=True)
+    launch (default plan here), with the partials merged by the last-arriving
+    split (3 splits; its arrival counters are reset inside the kernel), and with
+    8 long splits merged there from bf16 partials (bf16 and fp8 caches)."""
+    if merge == "merged8" and kv_dtype == syn.KV_MXFP4:
+        pytest.skip("MXFP4 merges 8 splits in the combine launch")
+    lens = [12000, 9000, 0, 12500] if merge == "merged8" else [1000, 3, 700, 0, 2000, 64]
+    case = syn.make_case(len(lens), lens, kv_dtype, seed=620 + kv_dtype, shuffle=True)
     t = to_dev(case, dev)
     B = case.batch
-    flags = mla.flags_for(splits=3) if merge_in_stage1 else 0
-    assert mla.mla_decode_plan(B, case.total_kv, kv_dtype, flags).combine == (2 if merge_in_stage1 else 1)
+    flags = {"launch": 0, "merged3": mla.flags_for(splits=3), "merged8": mla.flags_for(splits=8)}[merge]
+    assert mla.mla_decode_plan(B, case.total_kv, kv_dtype, flags).combine == (1 if merge == "launch" else 2)
     out = torch.empty((B, 16, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, 16), dtype=torch.float32, device=dev)
     ws = mla.new_workspace(mla.mla_decode_workspace_size(B, case.total_kv, kv_dtype, flags), dev)
