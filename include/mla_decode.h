@@ -83,11 +83,10 @@ extern "C" {
  * Workspace layout. When a plan has split partials (workspace_bytes > 0), the
  * first MLA_WORKSPACE_COUNTER_BYTES bytes of the workspace hold one 32-bit
  * arrival counter per query row, used by plans with combine = 2 (split-K with
- * 2 to 4 splits, or on the bf16 and fp8 caches 5 to 8 splits of at least 1024
- * tokens each on average, over at most 16384 query rows, unless
- * MLA_FLAG_COMBINE_LAUNCH is set): each split workgroup counts itself in after
- * writing its partial (5 to 8 splits: in bf16, so that the merge loads them all
- * at once),
+ * 2 to 4 splits, or on the bf16 and fp8 caches 5 to 8 splits, over at most
+ * 16384 query rows, unless MLA_FLAG_COMBINE_LAUNCH is set): each split
+ * workgroup counts itself in after writing its partial (5 to 8 splits: in
+ * bf16, so that the merge loads them all at once),
  * and the one that arrives last merges the row's partials (the log-sum-exp
  * merge of flash-decoding split partials; submission 593653,
  * `_flash_fp8_split_s2`) and sets the counter back to zero.

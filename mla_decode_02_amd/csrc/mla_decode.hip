@@ -1143,85 +1143,101 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t merge_rsrc(const float* p, uin
 constexpr int kCoherentLoad = 0x11;
 
 // The last-arriving split's merge of S = 5..8 bf16 partials [column][head]
-// (the formula of merge_if_last), with every partial's loads in one round:
-// thread t takes the 16-byte chunks t + 256 m (m < 4) of each partial, chunk
-// k holding column k / 2, heads 8 (k % 2) .. +7. The weights
-// w_s,h = exp(lse_s,h - M_h) / sum_s exp(lse_s,h - M_h) are formed once per
-// head in LDS; the sums pass through an LDS transpose ([column][head], rows
-// padded to 17 floats against bank conflicts) so that the output rows are
-// written as whole 8-byte pieces. The ring's LDS is free here: every wave
-// has left the token loop.
-__device__ void merge_bf16(const Params& P, int row, uint8_t* smem, int S) {
-    const int tid = threadIdx.x;
-    float* s_lse = reinterpret_cast<float*>(smem + 64);  // [8][16]
-    float* s_w = s_lse + 8 * kHeads;                      // [8][16]
-    float* s_out = s_w + 8 * kHeads;                      // [512][17]
-    static_assert(64 + 16 * 8 * kHeads + 4 * kDv * 17 <= Layout<MLA_KV_MXFP4>::kBytes,
-                  "the bf16 merge's LDS fits every format's stage-1 layout");
-    // the lse values first (the weights are formed while the partials are in flight), then every partial chunk
+// (the formula of merge_if_last) on the MFMA. For 16 output columns the sum
+// over slots s of w_s,h x_s[c][h] is a matrix product: the partials' chunks
+// as a [column] x [slot, head'] matrix (one 16-byte chunk, 8 heads' of one
+// slot, is the A-operand k-block of a lane) times the [slot, head'] x [head]
+// matrix that holds w_s,h where head' = h and zero elsewhere
+// (v_mfma_f32_16x16x32_bf16: two slots per k-step, four k-steps). The products
+// are exact and summed in fp32; each weight enters as two bf16 terms, hi = w
+// rounded and lo = w - hi rounded, which carry it to about 2^-17 relative.
+// Every lane forms the weights of its head from that head's lse values itself
+// (no LDS, no barrier), and all loads are issued in one round, lse first.
+// Lane (G, r) of wave w holds row r of the A tiles, column
+// 128 w + 32 (r / 4) + 4 t + r % 4 of tile t, chunk half G % 2 of slot
+// 2 ks + G / 2 at k-step ks; the products then leave it output columns
+// 128 w + 32 G .. +31 of head r, written as four 16-byte pieces.
+__device__ void merge_bf16(const Params& P, int row, int S) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int G = lane >> 4, r = lane & 15;
+    // Every load is issued, without a branch on S: the slots sl >= S lie past
+    // the end of either buffer, so theirs return zero without touching memory
+    // (their lse is taken as -inf below). A load under a branch on S would
+    // sit behind a wait for the loads before it.
+    // l[k] is the lse of slot k ^ s1 (s1 = G / 2), so that e[2 ks] below is
+    // always the weight of this lane's slot 2 ks + s1 (no lane-dependent index)
+    const int s1 = G >> 1;
     const __amdgpu_buffer_rsrc_t rl = merge_rsrc(P.part_lse + (int64_t)row * S * kHeads, S * kHeads * 4);
-    float lse_t = -INFINITY;
-    if (tid < S * kHeads)
-        lse_t = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * tid, 0, kCoherentLoad));
+    float l[kMaxMergeSplitsBf16];
+#pragma unroll
+    for (int k = 0; k < kMaxMergeSplitsBf16; ++k)
+        l[k] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * ((k ^ s1) * kHeads + r), 0, kCoherentLoad));
     const __amdgpu_buffer_rsrc_t ro = merge_rsrc(P.part_o + (int64_t)row * S * kHeads * kDv, S * kHeads * kDv * 4);
-    u32x4 v[kMaxMergeSplitsBf16][4];
+    const int cA = 128 * wave + 32 * (r >> 2) + (r & 3);  // this lane's A column in tile 0
+    bf16x8 x[8][4];                                         // [tile][k-step]
 #pragma unroll
-    for (int sl = 0; sl < kMaxMergeSplitsBf16; ++sl)
+    for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-            v[sl][m] = sl < S ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                    ro, 4 * sl * kHeads * kDv + 16 * (tid + 256 * m), 0, kCoherentLoad))
-                              : u32x4{0u, 0u, 0u, 0u};
-    if (tid < kMaxMergeSplitsBf16 * kHeads) s_lse[tid] = lse_t;
-    __syncthreads();
-    if (tid < kHeads) {
-        float M = -INFINITY;
-        for (int sl = 0; sl < S; ++sl) M = fmaxf(M, s_lse[sl * kHeads + tid]);
-        float W = 0.f;
-        for (int sl = 0; sl < S; ++sl) {
-            const float l = s_lse[sl * kHeads + tid];
-            if (l != -INFINITY) W += __expf(l - M);  // empty splits (lse = -inf) carry no weight
-        }
-        const float inv = (W > 0.f) ? 1.f / W : 0.f;
-        for (int sl = 0; sl < kMaxMergeSplitsBf16; ++sl) {
-            const float l = s_lse[sl * kHeads + tid];
-            s_w[sl * kHeads + tid] = (sl < S && l != -INFINITY) ? __expf(l - M) * inv : 0.f;
-        }
-        if (P.lse) P.lse[(int64_t)row * kHeads + tid] = (W > 0.f) ? M + logf(W) : -INFINITY;
+        for (int ks = 0; ks < 4; ++ks)
+            x[t][ks] = __builtin_bit_cast(
+                bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                            ro, 4 * (2 * ks + s1) * kHeads * kDv + 16 * (2 * (cA + 4 * t) + (G & 1)), 0,
+                            kCoherentLoad));
+    // w_s,r = exp(lse_s - M) / sum_s exp(lse_s - M); empty splits (lse = -inf)
+    // and absent slots weigh 0. The sum adds slot pairs (2 j, 2 j + 1) first,
+    // which gives every lane of head r the same W whichever order it holds
+    // the pair in.
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kMaxMergeSplitsBf16; ++k) {
+        if ((k ^ s1) >= S) l[k] = -INFINITY;
+        M = fmaxf(M, l[k]);
     }
-    __syncthreads();
-    const int h0 = 8 * (tid & 1);  // the heads of this thread's chunks (k % 2 = t % 2)
+    float e[kMaxMergeSplitsBf16], W = 0.f;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int col = (tid + 256 * m) >> 1;
-        float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < kMaxMergeSplitsBf16; ++k) e[k] = l[k] == -INFINITY ? 0.f : __expf(l[k] - M);
 #pragma unroll
-        for (int sl = 0; sl < kMaxMergeSplitsBf16; ++sl) {
-            if (sl < S) {
-                const f32x4 w0 = *reinterpret_cast<const f32x4*>(s_w + sl * kHeads + h0);
-                const f32x4 w1 = *reinterpret_cast<const f32x4*>(s_w + sl * kHeads + h0 + 4);
-                const bf16x8 x = __builtin_bit_cast(bf16x8, v[sl][m]);
+    for (int j = 0; j < kMaxMergeSplitsBf16 / 2; ++j) W += e[2 * j] + e[2 * j + 1];
+    const float inv = (W > 0.f) ? 1.f / W : 0.f;
+    if (wave == 0 && G == 0 && P.lse) P.lse[(int64_t)row * kHeads + r] = (W > 0.f) ? M + logf(W) : -INFINITY;
+    // B operands: lane (G, r) holds k-slots 8 G .. +7, i.e. heads' 8 (G % 2) .. +7 of
+    // slot 2 ks + G / 2; its one nonzero is head' = r, when r lies in that half
+    const bool own = (r >> 3) == (G & 1);
+    bf16x8 bh[4], bl[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    a[e] += w0[e] * (float)x[e];
-                    a[4 + e] += w1[e] * (float)x[4 + e];
-                }
-            }
+    for (int ks = 0; ks < 4; ++ks) {
+        const float w = e[2 * ks] * inv;
+        const __bf16 hi = (__bf16)w;
+        const __bf16 lo = (__bf16)(w - (float)hi);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const bool at = own && k == (r & 7);
+            bh[ks][k] = at ? hi : (__bf16)0.f;
+            bl[ks][k] = at ? lo : (__bf16)0.f;
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s_out[col * 17 + h0 + e] = a[e];
     }
-    __syncthreads();
-    // out row: head h = t / 16 writes columns 4 q .. 4 q + 3, q = t % 16 + 16 n
-    __bf16* out = P.out + (int64_t)row * kHeads * kDv;
-    const int h = tid >> 4;
+    f32x4 acc[8];
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-        const int c0 = 4 * ((tid & 15) + 16 * n);
-        bf16x4 pk;
+    for (int t = 0; t < 8; ++t) {
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pk[e] = (__bf16)s_out[(c0 + e) * 17 + h];
-        *reinterpret_cast<bf16x4*>(out + h * kDv + c0) = pk;
+        for (int ks = 0; ks < 4; ++ks) {
+            acc[t] = mfma32(x[t][ks], bh[ks], acc[t]);
+            acc[t] = mfma32(x[t][ks], bl[ks], acc[t]);
+        }
+    }
+    // tile t, row 4 G + i is column 128 w + 32 G + 4 t + i of head r
+    __bf16* out = P.out + ((int64_t)row * kHeads + r) * kDv + 128 * wave + 32 * G;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        bf16x8 pk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pk[i] = (__bf16)acc[2 * p][i];
+            pk[4 + i] = (__bf16)acc[2 * p + 1][i];
+        }
+        *reinterpret_cast<bf16x8*>(out + 8 * p) = pk;
     }
 }
 
@@ -1251,7 +1267,7 @@ __device__ void merge_if_last(const Params& P, int row, uint8_t* smem) {
     __syncthreads();
     if (!*flag) return;
     if (S > kMaxMergeSplits) {
-        merge_bf16(P, row, smem, S);
+        merge_bf16(P, row, S);
         return;
     }
     constexpr int kBatch = 4;  // partials whose loads are in flight together

@@ -7,9 +7,8 @@
 //               splits) rounded up to the 32-token workgroup step. One partial
 //               slot per (b, s); when splits > 1 the partials of a sequence
 //               are merged by its last-arriving split workgroup (up to
-//               kMaxMergeSplits splits; up to kMaxMergeSplitsBf16 of at least
-//               kMergeBf16MinTokens tokens each, from bf16 partials) or by a
-//               combine launch.
+//               kMaxMergeSplits splits; up to kMaxMergeSplitsBf16 on the bf16
+//               and fp8 caches, from bf16 partials) or by a combine launch.
 //               (Flash-decoding split-K: the split partial plus log-sum-exp
 //               merge of amd-mixed-mla submission 593653, `_flash_fp8_split_s1`
 //               and `_flash_fp8_split_s2`.)
@@ -56,16 +55,22 @@ size_t partial_lse_offset(int num_partials) {
 //   for short sequences, one workgroup per compute unit with at least one
 //   32-token step each, since latency rather than bandwidth bounds them.
 // A third rule applies when the split partials can be merged by the last-
-// arriving split (merge_ok: up to kMaxMergeSplits splits): if one workgroup
-// per compute unit fills the chip with that few splits and each split is
-// short, that plan saves the combine launch, which costs more than the second
-// workgroup per compute unit gains on short splits. Long splits keep two
-// workgroups per compute unit to stream.
+// arriving split (merge_ok) and the first two rules' split count could not
+// be (more than 8 splits on the bf16 and fp8 caches, more than 4 on MXFP4):
+// if one workgroup per compute unit fills the chip with at most
+// kMaxMergeSplits splits and each split is short, that plan saves the
+// combine launch, which costs more than the second workgroup per compute
+// unit gains on short splits. Long splits keep two workgroups per compute
+// unit to stream.
 // Measured optima this reproduces (cold, MI355X): 4 x 1k: 32 splits (bf16
-// 14.8 vs 18.1 us at 8 splits); 32 x 1k fp8: 8 (17.4 us, against 19.4 at 4
-// merged); 64 x 1k bf16: 4; 64 x 1k fp8: 4 merged (20.7 us, against 23.4 at
-// 8; MXFP4 equal, 23.1 both); 256 x 1k fp8: 2 (39.7 us merged, against 41.9
-// at 1); 64 x 8k fp8: 8 (66.1 us, against 79.7 at 4 merged); 32 x 8k MXFP4: 16.
+// 14.8 vs 18.1 us at 8 splits; 14.2 against 15.2 at 8 merged); 32 x 1k fp8:
+// 8 merged (17.0 us, against 17.6 with the combine launch and 19.4 at 4
+// merged); 64 x 1k bf16: 4; 64 x 1k fp8: 8 merged (20.4 us, against 20.9 at
+// 4 merged and 23.4 at 8 with the combine launch); 64 x 1k MXFP4: 4 merged
+// (equal to 8 with the launch, 23.1 both); 256 x 1k fp8: 2 (39.7 us merged,
+// against 41.9 at 1); 64 x 8k fp8: 8 merged (66.1 us, against 79.7 at 4
+// merged, when both merged on the VALU); 32 x 8k fp8: 16 (40.4 us, against
+// 43.4 at 8 merged); 32 x 8k MXFP4: 16.
 int heuristic_splits(int batch, int64_t total_kv, int kv_dtype, bool merge_ok) {
     if (batch <= 0) return 1;
     const int64_t avg = cdiv(total_kv, batch);
@@ -78,7 +83,8 @@ int heuristic_splits(int batch, int64_t total_kv, int kv_dtype, bool merge_ok) {
     const int64_t fill = rule((int64_t)kNumCUs * wgs_per_cu(kv_dtype), kMinTokensPerWg);
     const int64_t per_cu = rule(kNumCUs, kStepTokens);
     const int64_t s = fill > per_cu ? fill : per_cu;
-    if (merge_ok && batch <= kMaxCounterRows && s > kMaxMergeSplits && per_cu > 1 && per_cu <= kMaxMergeSplits &&
+    if (merge_ok && batch <= kMaxCounterRows && s > max_stage1_merge_splits(kv_dtype) && per_cu > 1 &&
+        per_cu <= kMaxMergeSplits &&
         (int64_t)batch * per_cu >= kNumCUs && cdiv(avg, per_cu) <= kShortSplitTokens)
         return (int)per_cu;
     return (int)s;
@@ -153,13 +159,13 @@ int make_plan(int batch, int64_t total_kv, int kv_dtype, int flags, mla_plan_inf
         // The last-arriving split of a row merges the row's partials alone,
         // so that merge pays only while it reads a few of them; many splits
         // (short batches of long sequences) merge in the wide combine launch.
-        // (not on the MXFP4 cache: bound by instruction issue, its last arrivals' longer merge
-        // lengthened the tail, 64 x 8k 59.0 -> 59.7 us, where fp8 64 x 8k gained 61.8 -> 61.1 us
-        // and bf16 32 x 8k 59.9 -> 57.8 us)
-        const bool long_splits =
-            kv_dtype != MLA_KV_MXFP4 && total_kv >= (int64_t)kMergeBf16MinTokens * s * batch;
-        const bool merge_in_stage1 = (s <= kMaxMergeSplits || (s <= kMaxMergeSplitsBf16 && long_splits)) &&
-                                     batch <= kMaxCounterRows && merge_ok;
+        // 5..8 splits merge there from bf16 partials on the MFMA: against the
+        // combine launch fp8 64 x 8k 60.3 -> 58.8 us (with the merge before
+        // it on the VALU 61.8 -> 61.1), fp8 32 x 1k 17.6 -> 17.0, bf16
+        // 32 x 1k 20.6 -> 20.2. Not on the MXFP4 cache, bound by instruction
+        // issue, where the last arrivals' merge lengthens the tail: 64 x 8k
+        // 58.8 -> 59.2 us.
+        const bool merge_in_stage1 = s <= max_stage1_merge_splits(kv_dtype) && batch <= kMaxCounterRows && merge_ok;
         p->combine = (s > 1) ? (merge_in_stage1 ? 2 : 1) : 0;
         p->workspace_bytes = (s > 1) ? partial_bytes(p->num_partials) : 0;
     }

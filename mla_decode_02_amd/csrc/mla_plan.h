@@ -23,11 +23,14 @@ constexpr int kQ8AmaxParts = 256;     // partial maxima of the dynamic fp8 query
 constexpr size_t kCounterBytes = MLA_WORKSPACE_COUNTER_BYTES;          // arrival counters ahead of the partials
 constexpr int kMaxCounterRows = (int)(kCounterBytes / sizeof(uint32_t));  // query rows with a counter
 constexpr int kMaxMergeSplits = 4;    // split-K plans merged by the last-arriving split, fp32 partials
-// 5..8 splits of at least kMergeBf16MinTokens tokens each are merged there
-// too on the bf16 and fp8 caches, from bf16 partials, so that one round of
-// loads holds them all (more splits, shorter ones, or MXFP4: a combine launch)
+// 5..8 splits are merged there too on the bf16 and fp8 caches, from bf16
+// partials, so that one round of loads holds them all (more splits, or
+// MXFP4: a combine launch)
 constexpr int kMaxMergeSplitsBf16 = 8;
-constexpr int kMergeBf16MinTokens = 1024;
+// Most splits the last-arriving split merges on a cache format.
+constexpr int max_stage1_merge_splits(int kv_dtype) {
+    return kv_dtype == MLA_KV_MXFP4 ? kMaxMergeSplits : kMaxMergeSplitsBf16;
+}
 constexpr int64_t kShortSplitTokens = 256;  // longest split the one-workgroup-per-CU merged plan is chosen for
 
 // Stage-1 workgroups resident per compute unit (bound by the LDS ring size:

@@ -140,10 +140,10 @@ def test_heuristic_plan_invariants(mla, B, L, kv_dtype):
     if p.mode == 0:
         assert 1 <= p.num_splits <= 64
         assert p.grid == p.num_splits * B
-        # the last-arriving split merges up to 4 splits, or up to 8 of at least 1024 tokens each (from bf16
+        # the last-arriving split merges up to 4 splits, or up to 8 on the bf16 and fp8 caches (from bf16
         # partials); more merge in a combine launch
         S = p.num_splits
-        merged = S <= 4 or (S <= 8 and kv_dtype != 2 and B * L >= 1024 * S * B)
+        merged = S <= 4 or (S <= 8 and kv_dtype != 2)
         assert p.combine == (0 if S == 1 else 2 if merged else 1)
         assert p.num_partials == (p.num_splits * B if p.num_splits > 1 else 0)
     else:
@@ -481,23 +481,27 @@ def test_split_ranges_cover_tokens_once(L, S):
 def test_plan_merge_rule(mla):
     """Split-K plans of 2..4 splits merge in the last-arriving split workgroup
     (combine = 2) unless MLA_FLAG_COMBINE_LAUNCH asks for the combine launch, and
-    so do 5..8 splits of at least 1024 tokens each; more splits, shorter ones, or
-    more query rows than the counter region holds, use the launch.
+    so do 5..8 splits on the bf16 and fp8 caches; more splits, MXFP4 plans of more
+    than 4, or more query rows than the counter region holds, use the launch.
     The partials always start after the counter region."""
     for s in range(1, 10):
         p = mla.mla_decode_plan(8, 8 * 4096, 1, mla.flags_for(splits=s))
-        assert p.combine == (0 if s == 1 else 2 if s <= 4 else 1)
+        assert p.combine == (0 if s == 1 else 2 if s <= 8 else 1)
+        m = mla.mla_decode_plan(8, 8 * 4096, 2, mla.flags_for(splits=s))
+        assert m.combine == (0 if s == 1 else 2 if s <= 4 else 1)
         q = mla.mla_decode_plan(8, 8 * 4096, 1, mla.flags_for(splits=s) | mla.FLAG_COMBINE_LAUNCH)
         assert q.combine == (0 if s == 1 else 1)
         assert q.workspace_bytes == p.workspace_bytes
         if s > 1:
             assert p.workspace_bytes > mla.WORKSPACE_COUNTER_BYTES + s * 8 * 16 * 512 * 4
-    # 5..8 splits merge in stage 1 (bf16 partials) when every split holds at least 1024 tokens on average
+    # 5..8 splits merge in stage 1 (bf16 partials) on the bf16 and fp8 caches, short splits included
     for s in range(5, 10):
-        for L in (1024 * s - 1, 1024 * s, 8192):
-            p = mla.mla_decode_plan(8, 8 * L, 1, mla.flags_for(splits=s))
-            assert p.combine == (2 if s <= 8 and L >= 1024 * s else 1), (s, L)
-            assert mla.mla_decode_plan(8, 8 * L, 1, mla.flags_for(splits=s) | mla.FLAG_COMBINE_LAUNCH).combine == 1
+        for L in (1, 32 * s - 1, 1024 * s, 8192):
+            for fmt in (0, 1):
+                p = mla.mla_decode_plan(8, 8 * L, fmt, mla.flags_for(splits=s))
+                assert p.combine == (2 if s <= 8 else 1), (s, L, fmt)
+                f = mla.flags_for(splits=s) | mla.FLAG_COMBINE_LAUNCH
+                assert mla.mla_decode_plan(8, 8 * L, fmt, f).combine == 1
     assert mla.mla_decode_plan(64, 64 * 8192, 1, 0).combine == 2  # the 8-split fp8 64 x 8192 plan
     assert mla.mla_decode_plan(8, 8 * 8192, 0, mla.flags_for(splits=8)).combine == 2  # bf16 too
     assert mla.mla_decode_plan(8, 8 * 8192, 2, mla.flags_for(splits=8)).combine == 1  # not MXFP4
@@ -521,17 +525,27 @@ def test_rows_validation(raw_lib):
 
 
 def test_short_splits_take_one_workgroup_per_cu_merged(mla):
-    """Short splits on a batch that fills the chip at one workgroup per CU with at
-    most 4 splits take that plan, merged by the last-arriving split (fp8 64 x 1k:
-    4 merged splits); the rule needs the merge (MLA_FLAG_COMBINE_LAUNCH keeps the
-    8-split plan), leaves long splits at two workgroups per CU (64 x 8k: 8) and
-    leaves batches that one workgroup per CU cannot fill within 4 splits (32 x 1k: 8)."""
-    p = mla.mla_decode_plan(64, 64 * 1024, 1)
+    """Where the plan at two workgroups per CU would need the combine launch, short
+    splits on a batch that fills the chip at one workgroup per CU with at most 4
+    splits take that plan, merged by the last-arriving split (MXFP4 64 x 1k: 4 merged
+    splits, not 8 with the launch). On the bf16 and fp8 caches 8 splits merge in
+    stage 1 themselves (fp8 64 x 1k and 32 x 1k: 8 merged). MLA_FLAG_COMBINE_LAUNCH
+    keeps the 8-split plan; long splits keep two workgroups per CU (64 x 8k: 8), and
+    batches that one workgroup per CU cannot fill within 4 splits keep their plan
+    (MXFP4 32 x 1k: 8 with the launch)."""
+    p = mla.mla_decode_plan(64, 64 * 1024, 2)
     assert (p.num_splits, p.combine) == (4, 2)
+    p = mla.mla_decode_plan(64, 64 * 1024, 2, mla.FLAG_COMBINE_LAUNCH)
+    assert (p.num_splits, p.combine) == (8, 1)
+    p = mla.mla_decode_plan(64, 64 * 1024, 1)
+    assert (p.num_splits, p.combine) == (8, 2)
     p = mla.mla_decode_plan(64, 64 * 1024, 1, mla.FLAG_COMBINE_LAUNCH)
     assert (p.num_splits, p.combine) == (8, 1)
     assert mla.mla_decode_plan(64, 64 * 8192, 1).num_splits == 8
+    assert mla.mla_decode_plan(64, 64 * 8192, 2).num_splits == 8
     p = mla.mla_decode_plan(32, 32 * 1024, 1)
+    assert (p.num_splits, p.combine) == (8, 2)
+    p = mla.mla_decode_plan(32, 32 * 1024, 2)
     assert (p.num_splits, p.combine) == (8, 1)
     p = mla.mla_decode_plan(256, 256 * 1024, 1)
     assert (p.num_splits, p.combine) == (2, 2)

@@ -478,17 +478,18 @@ def test_paged_full_size_page8(mla, orc, dev, name):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("kv_dtype", [syn.KV_BF16, syn.KV_FP8, syn.KV_MXFP4])
 def test_merge_in_stage1_against_oracle_and_combine_launch(mla, orc, dev, kv_dtype):
-    """Every split count the merge takes (2..4) and two beyond it, on ragged,
+    """Split counts of the fp32-partial merge (2..4), of the bf16-partial one (5, 8: bf16
+    and fp8 caches; MXFP4 takes the combine launch) and one beyond both (9), on ragged,
     shuffled sequences with an empty one and ones shorter than the splits: the
     merged result within the oracle's bounds, the same as the combine launch's
     up to the merge's rounding, and the arrival counters back to zero after each
     call (the next call depends on it)."""
     case = syn.make_case(6, [700, 1, 0, 2048, 33, 515], kv_dtype, seed=91, shuffle=True)
     ref = oracle_ref(orc, case)
-    for splits in (2, 3, 4, 5, 8):
+    for splits in (2, 3, 4, 5, 8, 9):
         f = mla.flags_for(splits=splits)
         plan = mla.mla_decode_plan(case.batch, case.total_kv, kv_dtype, f)
-        assert plan.combine == (2 if splits <= 4 else 1)
+        assert plan.combine == (2 if splits <= 4 or (splits <= 8 and kv_dtype != syn.KV_MXFP4) else 1)
         ws = new_workspace(mla, case, dev, f)
         a = run_gpu(mla, case, dev, flags=f, ws=ws)
         check(a, ref, f"merge in stage 1, {splits} splits")
@@ -503,13 +504,13 @@ def test_merge_in_stage1_against_oracle_and_combine_launch(mla, orc, dev, kv_dty
 
 
 @pytest.mark.parametrize("kv_dtype", [syn.KV_BF16, syn.KV_FP8])
-@pytest.mark.parametrize("lens", [[12000, 9000, 0, 12500], [20000, 13000, 3, 0]])
+@pytest.mark.parametrize("lens", [[12000, 9000, 0, 12500], [20000, 13000, 3, 0], [700, 33, 1500, 256]])
 def test_merge_bf16_partials_5_to_8_splits(mla, orc, dev, kv_dtype, lens):
-    """5..8 splits of at least 1024 tokens each (bf16 and fp8 caches) merge in the last-arriving
-    split from bf16 partials, all in one round: within the oracle's bounds, the same as the combine
-    launch up to the partials' rounding, the counters back at zero, and ten queued calls
-    on one workspace bitwise equal. Sequences of 3 and 0 tokens leave most or all of
-    their splits empty."""
+    """5..8 splits (bf16 and fp8 caches) merge in the last-arriving split from bf16
+    partials on the MFMA, all in one round: within the oracle's bounds, the same as
+    the combine launch up to the partials' rounding, the counters back at zero, and
+    ten queued calls on one workspace bitwise equal. Long and short splits; sequences
+    of 3 and 0 tokens leave most or all of their splits empty."""
     case = syn.make_case(4, lens, kv_dtype, seed=95, shuffle=True)
     ref = oracle_ref(orc, case)
     for splits in (5, 6, 7, 8):
@@ -692,14 +693,14 @@ def test_merge_in_stage1_two_streams(mla, dev):
 # The mla_decode export itself (the Python binding calls mla_decode_rows)
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("kv_dtype", DTYPES)
-@pytest.mark.parametrize("flags_kind", ["default", "one", "merged3", "combine8", "persistent"])
+@pytest.mark.parametrize("flags_kind", ["default", "one", "merged3", "merged8", "combine8", "persistent"])
 def test_mla_decode_export_through_ctypes(mla, orc, dev, kv_dtype, flags_kind):
     """mla_decode called through ctypes with raw device pointers, in every merge form,
     against the oracle and bit for bit against the binding's call (mla_decode_rows)."""
     import ctypes
 
     flags = {"default": 0, "one": mla.flags_for(splits=1), "merged3": mla.flags_for(splits=3),
-             "combine8": mla.flags_for(splits=8),
+             "merged8": mla.flags_for(splits=8), "combine8": mla.flags_for(splits=8) | mla.FLAG_COMBINE_LAUNCH,
              "persistent": mla.flags_for(persistent=True, grid=40)}[flags_kind]
     case = syn.make_case(5, [640, 1, 0, 333, 2048], kv_dtype, seed=620 + kv_dtype, shuffle=True, extra_rows=9)
     t = to_dev(case, dev)

@@ -49,10 +49,10 @@ def phases_lib(mla):
     lib.mla_phase_buffers(None, None)
 
 
-@pytest.mark.parametrize("flags_kind", ["combine8", "merged3", "one"])
+@pytest.mark.parametrize("flags_kind", ["combine8", "merged8", "merged3", "one"])
 def test_phase_stamps_ordered_and_results_identical(mla, dev, phases_lib, flags_kind):
-    flags = {"combine8": mla.flags_for(splits=8), "merged3": mla.flags_for(splits=3),
-             "one": mla.flags_for(splits=1)}[flags_kind]
+    flags = {"combine8": mla.flags_for(splits=8) | mla.FLAG_COMBINE_LAUNCH, "merged8": mla.flags_for(splits=8),
+             "merged3": mla.flags_for(splits=3), "one": mla.flags_for(splits=1)}[flags_kind]
     case = syn.make_case(6, [700, 33, 1500, 256, 1, 999], syn.KV_FP8, seed=680, shuffle=True)
     plan = mla.mla_decode_plan(case.batch, case.total_kv, case.kv_dtype, flags)
     t = to_dev(case, dev)

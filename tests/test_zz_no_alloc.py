@@ -67,10 +67,11 @@ def run_noalloc(f, case, dev, flags):
 @pytest.mark.parametrize("kv_dtype", DTYPES)
 @pytest.mark.parametrize("plan", ["default", "merged3", "combine8", "merged8", "persistent"])
 def test_noalloc_equals_mla_decode_large_then_small(mla, orc, dev, noalloc, kv_dtype, plan):
-    flags = {"default": 0, "merged3": mla.flags_for(splits=3), "combine8": mla.flags_for(splits=8),
-             "merged8": mla.flags_for(splits=8), "persistent": mla.flags_for(persistent=True, grid=64)}[plan]
+    flags = {"default": 0, "merged3": mla.flags_for(splits=3),
+             "combine8": mla.flags_for(splits=8) | mla.FLAG_COMBINE_LAUNCH, "merged8": mla.flags_for(splits=8),
+             "persistent": mla.flags_for(persistent=True, grid=64)}[plan]
     big = syn.make_case(6, [3000, 1, 0, 777, 5000, 64], kv_dtype, seed=700 + kv_dtype, shuffle=True, extra_rows=3)
-    if plan == "merged8":  # 8 splits of over 1024 tokens: merged in stage 1 from bf16 partials
+    if plan == "merged8":  # 8 splits: merged in stage 1 from bf16 partials (bf16 and fp8 caches)
         big = syn.make_case(4, [12000, 9000, 0, 12500], kv_dtype, seed=720 + kv_dtype, shuffle=True, extra_rows=3)
         assert mla.mla_decode_plan(big.batch, big.total_kv, kv_dtype, flags).combine == (1 if kv_dtype == syn.KV_MXFP4
                                                                                           else 2)
