@@ -97,6 +97,7 @@ def check(got, ref, name=""):
     assert not np.any(bad), f"{name}: {bad.sum()} outputs outside the band, max err {err.max():.3e}"
     if len(ref) > 2:
         allow = U_BF16 * (ref[2] + np.abs(ro)) + GATE_SLACK
+        print(f"{name}: largest |gpu - oracle| / rounding bound {float((err / allow).max()) if err.size else 0.0:.3f}")
         over = err > allow
         if np.any(over):
             i = np.unravel_index(np.argmax(err - allow), err.shape)
