@@ -313,6 +313,15 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
                  : "=&s"(save) : "v"(g), "s"(lds) : "memory");
 }
+
+// Element i of a read-only int array at a uniform address, as a scalar load
+// (through the constant address space). Its wait is on the scalar counter,
+// so it never drains the LDS-DMA loads in flight. The same read written as
+// an ordinary load after the DMA asm (whose memory clobber rules out the
+// scalar form) becomes a vector load whose wait, vmcnt(0), drains them.
+__device__ __forceinline__ int32_t ld_scalar(const int32_t* p, int64_t i) {
+    return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
 // Wave-uniform 32-bit LDS address of a pointer into shared memory.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)p);
@@ -1002,6 +1011,23 @@ __device__ __forceinline__ void wait_own(int groups, int hi) {
     else wait_vmcnt<N * k0>();
 }
 
+// Wait until at most X + e ops(hi) of this wave's vector memory operations
+// are outstanding: those issued after the ones waited for are X single
+// operations and the gathers of e steps (e < kRing).
+template <int KV, int X, int E = 0>
+__device__ __forceinline__ void wait_behind(int e, int hi) {
+    constexpr int k0 = Fmt<KV>::ops(0), k1 = Fmt<KV>::ops(1);
+    static_assert(X + E * k0 <= 63 && X + E * k1 <= 63, "vmcnt holds at most 63");
+    if constexpr (E < Fmt<KV>::kRing - 1) {
+        if (e > E) {
+            wait_behind<KV, X, E + 1>(e, hi);
+            return;
+        }
+    }
+    if (hi) wait_vmcnt<X + E * k1>();
+    else wait_vmcnt<X + E * k0>();
+}
+
 constexpr int kQGroups = kHeads * kDqk / 8;                   // 8-element groups of one query row
 constexpr int kQPer = (kQGroups + kThreads - 1) / kThreads;  // of them per thread (fp8 query)
 template <int KV>
@@ -1069,6 +1095,30 @@ __device__ __forceinline__ void issue_early(const Params& P, uint8_t* smem, int6
                            smem + (d % R) * L::kStepBytes + tile * Fmt<KV>::kTileBytes, lane, hf);
 }
 
+// The bf16 query row b into ring slot D with LDS-DMA (bf16 and fp8 caches,
+// one row per workgroup), laid out in score-operand order: the 16 bytes that
+// lane (G, r) of a wave of half hf takes as its k-step kHalfK hf + j operand
+// sit at 1024 (kHalfK hf + j) + 16 lane, so run_wg reads Q^T with one linear
+// ds_read_b128 per k-step. Issued first at entry, ahead of the index window
+// and the early gathers, and waited for with an exact count (run_wg), so that
+// the wait for Q leaves those in flight; the compiler's own wait for query
+// registers loaded from memory would drain them, as it does not see the DMA
+// loads. Waves 0 and 1 issue five loads, waves 2 and 3 four.
+template <int KV>
+__device__ __forceinline__ void dma_query(const Params& P, int b, uint8_t* smem) {
+    constexpr int D = Fmt<KV>::kRing - 1;
+    static_assert(Layout<KV>::kStepBytes >= kHeads * kDqk * 2, "a ring slot holds the bf16 query");
+    uint8_t* qs = smem + D * Layout<KV>::kStepBytes;
+    const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, r = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const __bf16* qrow = P.q + ((int64_t)b * kHeads + r) * kDqk;
+#pragma unroll
+    for (int m = 0; m < 5; ++m) {
+        const int blk = 4 * m + wave;  // k-step block kHalfK hf + j
+        if (blk < 2 * kHalfK) dma16(qrow + dbase<KV>(blk, G), lds_addr(qs + 1024 * blk));
+    }
+}
+
 // One query row in registers, with the scales read alongside it.
 //   bf16 query (bf16 and fp8 caches): this wave's half of Q^T, straight in
 //   the score operand layout.
@@ -1089,6 +1139,18 @@ struct QueryRegs {
     int qsc[kSplit ? 6 : 1];  // split query: e8m0 codes of qB (head r, k block G)
     float kv_scale, q_scale, q_part;
 };
+
+// The scales of QueryRegs alone, for a query that comes through LDS
+// (dma_query); read as scalar loads.
+template <int KV, int QF>
+__device__ __forceinline__ void query_scales(const Params& P, QueryRegs<KV, QF>& q) {
+    static_assert(!QF, "the fp8 query reads its scale with the query");
+    q.kv_scale = 1.0f;
+    if constexpr (KV == MLA_KV_FP8_E4M3)
+        q.kv_scale = __builtin_bit_cast(float, ld_scalar(reinterpret_cast<const int32_t*>(P.kv_scales), 0));
+    q.q_scale = 1.0f;
+    q.q_part = 0.0f;
+}
 
 template <int KV, int QF>
 __device__ __forceinline__ void load_query(const Params& P, int b, QueryRegs<KV, QF>& q) {
@@ -1372,6 +1434,9 @@ __device__ __forceinline__ void take_turns_priority(int s) {
 // compute unit take turns (fp8 64 x 8k has 1024: -1.4 us; 256 x 1k has 512:
 // +0.5 us with turns).
 constexpr int kTurnsMinTokens = 1024;
+// Splits per sequence from which fp8 plans load the bf16 query into registers
+// rather than through LDS (launch).
+constexpr int kQRegsMinSplits = 32;
 
 // Two query rows per workgroup (NT = 2): row t of the pair sees the sequence's
 // positions [0, lim_t); has1 is false when the pair has no second row (the
@@ -1381,7 +1446,7 @@ struct RowPair {
     bool has1 = false;
 };
 
-template <int KV, int QF, bool MG = false, int NT = 1, bool TURNS = false>
+template <int KV, int QF, bool MG = false, int NT = 1, bool TURNS = false, bool QL = false>
 __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, int t1, bool final, int slot,
                        bool scale_out, QueryRegs<KV, QF, NT>& qr, bool idx_dma, bool idx_staged,
                        int64_t early_first = -1, RowPair pr = RowPair{}) {
@@ -1417,10 +1482,29 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
     const float kv_scale = qr.kv_scale, q_part = qr.q_part;
     float q_scale = qr.q_scale;
     const __bf16* qseq = P.q + (int64_t)b * kHeads * kDqk;
+    // The caller's early gathers (the first e_early steps of the first
+    // window) when it issued them for the range this workgroup runs, the
+    // only case in which they can be kept: the waits up to the first step
+    // then leave them in flight. -1: none, or for another range.
+    const int e_early = (early_first >= 0 && idx_staged)
+                            ? min(D, (min(kIdxWindow, t1 - t0) + kStepTokens - 1) / kStepTokens)
+                            : -1;
     // Consume Q and the scales here: the compiler's wait for these loads must
     // not land inside the token loop, where the count it waits for would also
     // drain the gathers in flight (it does not see the LDS-DMA loads).
-    if constexpr (NT == 2) {
+    if constexpr (QL) {
+        // Q^T through ring slot D (dma_query), issued before the caller's
+        // index DMA (kIdxPer operations) and early gathers
+        static_assert(NT == 1 && !QF && !kSplit, "the query through LDS: bf16 query, one row, bf16 or fp8 cache");
+        if (e_early >= 0) wait_behind<KV, kIdxPer<KV>>(e_early, hf);
+        else if (idx_dma && early_first < 0) wait_vmcnt<kIdxPer<KV>>();
+        else wait_vmcnt<0>();
+        __syncthreads();  // every wave's share of Q has landed
+        const uint8_t* qs = smem + D * L::kStepBytes;
+#pragma unroll
+        for (int j = 0; j < kHalfK; ++j)
+            qB[j] = *reinterpret_cast<const bf16x8*>(qs + 1024 * (kHalfK * hf + j) + 16 * lane);
+    } else if constexpr (NT == 2) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -1434,9 +1518,13 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
     }
     asm volatile("" ::"v"(kv_scale), "v"(q_part), "v"(q_scale));
     // The caller's index DMA, kept or not, has landed before anything else
-    // touches the index window (so have the caller's early gathers, issued
-    // after it: no gathers are in flight past this point).
-    if (idx_dma) wait_vmcnt<0>();
+    // touches the index window. The early gathers issued after it stay in
+    // flight when they may be kept (e_early >= 0, checked below); otherwise
+    // they have landed too and no gathers are in flight past this point.
+    if (idx_dma) {
+        if (e_early >= 0) wait_behind<KV, 0>(e_early, hf);
+        else wait_vmcnt<0>();
+    }
     phase_stamp(1);
     if constexpr (QF) {
         if (P.q_amax) {
@@ -1504,6 +1592,8 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
             keep = __all(keep);
         }
         if (!keep) {
+            // this wave's early gathers into the same slots have landed first
+            if (w0 == t0 && e_early >= 0) wait_vmcnt<0>();
 #pragma unroll
             for (int d = 0; d < D; ++d)
                 if (d < nsteps) issue_step(d);
@@ -1798,7 +1888,9 @@ __device__ void split_pair(const Params& P, uint8_t* smem, int nblocks) {
 // MG: the plan merges the split partials here (the last-arriving split of
 // each row); a separate instantiation, so that plans merged by the combine
 // launch run a kernel without the merge code. NT: query rows per workgroup.
-template <int KV, int QF, bool MG, int NT = 1, bool TURNS = false>
+// QL: the bf16 query comes through LDS (dma_query; bf16 and fp8 caches), else
+// it is loaded into registers.
+template <int KV, int QF, bool MG, int NT = 1, bool TURNS = false, bool QL = (KV != MLA_KV_MXFP4 && QF == 0)>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Fmt<KV>::kWgsPerCU, Fmt<KV>::kWgsPerCU)))
 void split_kernel(STAGE1_ARGS) {
     phase_stamp(0);
@@ -1811,8 +1903,15 @@ void split_kernel(STAGE1_ARGS) {
     }
     const int item = xcd_order(blockIdx.x, nblocks);
     const int row = item / P.nsplit, s = item % P.nsplit;
+    // The bf16 query through LDS: its DMA first of all (dma_query).
+    static_assert(!QL || (KV != MLA_KV_MXFP4 && !QF), "the query through LDS: bf16 query, bf16 or fp8 cache");
     QueryRegs<KV, QF> qr;
-    load_query<KV, QF>(P, row, qr);
+    if constexpr (QL) {
+        query_scales<KV, QF>(P, qr);
+        dma_query<KV>(P, row, smem);
+    } else {
+        load_query<KV, QF>(P, row, qr);
+    }
     // Sequences of one common length Lu (page size 1, one query row each):
     // sequence b's entries would start at b * Lu, so this split's first index
     // window is requested now, with the query, before kv_indptr arrives. It
@@ -1833,6 +1932,7 @@ void split_kernel(STAGE1_ARGS) {
         (KV != MLA_KV_MXFP4 && idx_dma && P.kv_rows > 0) ? (int64_t)row * Lu + t0u : -1;
     if (early_first >= 0) issue_early<KV>(P, smem, early_first, min(Fmt<KV>::kIdxWindow, t1u - t0u));
     // the sequence of this query row, and the cache tokens the causal reading hides from it
+    // (the reads of kv_indptr, qo_indptr and kv_last_page_len are scalar loads: ld_scalar)
     int b = row, hide = 0;
     if (P.uni_q > 0 || P.qo_indptr) {
         int t, n;
@@ -1841,23 +1941,25 @@ void split_kernel(STAGE1_ARGS) {
             n = P.uni_q;
             t = row - b * n;
         } else {
-            b = count_le(P.qo_indptr, P.batch, row, reinterpret_cast<int*>(smem + Layout<KV>::kIdxOff));
-            const int r0 = P.qo_indptr[b];
-            n = P.qo_indptr[b + 1] - r0;
+            b = __builtin_amdgcn_readfirstlane(
+                count_le(P.qo_indptr, P.batch, row, reinterpret_cast<int*>(smem + Layout<KV>::kIdxOff)));
+            const int r0 = ld_scalar(P.qo_indptr, b);
+            n = ld_scalar(P.qo_indptr, b + 1) - r0;
             t = row - r0;
         }
         if (P.causal) hide = n - 1 - t;
     }
-    const int base = P.indptr[b], entries = P.indptr[b + 1] - base;
+    const int base = ld_scalar(P.indptr, b), entries = ld_scalar(P.indptr, b + 1) - base;
     // tokens of the sequence: its entries, or (pages - 1) full pages plus the last page's tokens
-    const int Ls = P.page_size == 1 ? entries : entries > 0 ? (entries - 1) * P.page_size + P.last_page[b] : 0;
+    const int Ls =
+        P.page_size == 1 ? entries : entries > 0 ? (entries - 1) * P.page_size + ld_scalar(P.last_page, b) : 0;
     const int L = max(0, Ls - hide);
     const int chunk = ((L + P.nsplit - 1) / P.nsplit + kStepTokens - 1) / kStepTokens * kStepTokens;
     const int t0 = min(L, s * chunk);
     const int t1 = min(L, t0 + chunk);
     const bool staged = idx_dma && base == row * Lu && L == Lu;  // then t0, t1 are t0u, t1u
-    run_wg<KV, QF, MG, 1, TURNS>(P, smem, row, base, t0, t1, P.nsplit == 1, row * P.nsplit + s, blockIdx.x == 0, qr, idx_dma,
-                       staged, early_first);
+    run_wg<KV, QF, MG, 1, TURNS, QL>(P, smem, row, base, t0, t1, P.nsplit == 1, row * P.nsplit + s, blockIdx.x == 0,
+                                     qr, idx_dma, staged, early_first);
 }
 
 // Largest p whose share [floor(p T / G), floor((p+1) T / G)) starts at or before t.
@@ -2240,37 +2342,42 @@ static int launch(const mla_plan_info& plan, const Params& P, hipStream_t stream
     }
     const bool turns = KV == MLA_KV_FP8_E4M3 && plan.mode == 0 && plan.rows_per_wg == 1 && plan.grid > kNumCUs &&
                        (int64_t)P.total >= (int64_t)kTurnsMinTokens * plan.grid;
+    // fp8 plans of many splits per sequence load the bf16 query into registers
+    // (the query through LDS measured slower there, ‡: 4 x 1k, 32 splits,
+    // 12.8 -> 13.2 us; 4 x 8k, 64 splits, 18.2 -> 18.9; every other shape
+    // measured 0.3 to 1.6 us faster with it)
+    const bool q_regs = KV == MLA_KV_FP8_E4M3 && QF == 0 && plan.num_splits >= kQRegsMinSplits && !P.counters;
+#define MLA_SPLIT_ARGS                                                                                             \
+    dim3(plan.grid), dim3(kThreads), 0, stream, P.q, P.indices, P.kv_scales, P.nsplit, P.uni_len, P.uni_chunk, \
+        plan.grid, P
     if (plan.rows_per_wg == 2) {
         if constexpr (KV == MLA_KV_BF16 && QF == 0) {
             if (plan.mode != 0 || P.uni_q < 2) return MLA_ERR_INVALID_ARG;
-            if (P.counters)
-                hipLaunchKernelGGL((split_kernel<KV, QF, true, 2>), dim3(plan.grid), dim3(kThreads), 0, stream, P.q,
-                                   P.indices, P.kv_scales, P.nsplit, P.uni_len, P.uni_chunk, plan.grid, P);
-            else
-                hipLaunchKernelGGL((split_kernel<KV, QF, false, 2>), dim3(plan.grid), dim3(kThreads), 0, stream, P.q,
-                                   P.indices, P.kv_scales, P.nsplit, P.uni_len, P.uni_chunk, plan.grid, P);
+            if (P.counters) hipLaunchKernelGGL((split_kernel<KV, QF, true, 2>), MLA_SPLIT_ARGS);
+            else hipLaunchKernelGGL((split_kernel<KV, QF, false, 2>), MLA_SPLIT_ARGS);
         } else {
             return MLA_ERR_INVALID_ARG;  // the planner pairs rows on the bf16 cache only
         }
     } else if (turns) {
         // fp8, two workgroups per compute unit, long ranges: the two take turns at priority 2
         if constexpr (KV == MLA_KV_FP8_E4M3) {
-            if (P.counters)
-                hipLaunchKernelGGL((split_kernel<KV, QF, true, 1, true>), dim3(plan.grid), dim3(kThreads), 0, stream,
-                                   P.q, P.indices, P.kv_scales, P.nsplit, P.uni_len, P.uni_chunk, plan.grid, P);
-            else
-                hipLaunchKernelGGL((split_kernel<KV, QF, false, 1, true>), dim3(plan.grid), dim3(kThreads), 0,
-                                   stream, P.q, P.indices, P.kv_scales, P.nsplit, P.uni_len, P.uni_chunk, plan.grid, P);
+            if (P.counters) hipLaunchKernelGGL((split_kernel<KV, QF, true, 1, true>), MLA_SPLIT_ARGS);
+            else if (q_regs) hipLaunchKernelGGL((split_kernel<KV, QF, false, 1, true, false>), MLA_SPLIT_ARGS);
+            else hipLaunchKernelGGL((split_kernel<KV, QF, false, 1, true>), MLA_SPLIT_ARGS);
         }
-    } else if (plan.mode == 0 && P.counters)
-        hipLaunchKernelGGL((split_kernel<KV, QF, true>), dim3(plan.grid), dim3(kThreads), 0, stream, P.q, P.indices,
-                           P.kv_scales, P.nsplit, P.uni_len, P.uni_chunk, plan.grid, P);
-    else if (plan.mode == 0)
-        hipLaunchKernelGGL((split_kernel<KV, QF, false>), dim3(plan.grid), dim3(kThreads), 0, stream, P.q, P.indices,
-                           P.kv_scales, P.nsplit, P.uni_len, P.uni_chunk, plan.grid, P);
-    else
-        hipLaunchKernelGGL((persistent_kernel<KV, QF>), dim3(plan.grid), dim3(kThreads), 0, stream, P.q, P.indices,
-                           P.kv_scales, P.nsplit, P.uni_len, P.uni_chunk, plan.grid, P);
+    } else if (plan.mode == 0 && P.counters) {
+        hipLaunchKernelGGL((split_kernel<KV, QF, true>), MLA_SPLIT_ARGS);
+    } else if (plan.mode == 0) {
+        if (q_regs) {
+            if constexpr (KV == MLA_KV_FP8_E4M3)
+                hipLaunchKernelGGL((split_kernel<KV, QF, false, 1, false, false>), MLA_SPLIT_ARGS);
+        } else {
+            hipLaunchKernelGGL((split_kernel<KV, QF, false>), MLA_SPLIT_ARGS);
+        }
+    } else {
+        hipLaunchKernelGGL((persistent_kernel<KV, QF>), MLA_SPLIT_ARGS);
+    }
+#undef MLA_SPLIT_ARGS
     if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
     if (plan.combine == 1) {
         CombineParams C;
