@@ -1966,11 +1966,18 @@ void split_kernel(STAGE1_ARGS) {
 __device__ __forceinline__ int share_of(int64_t t, int64_t T, int64_t G) { return (int)(((t + 1) * G - 1) / T); }
 __device__ __forceinline__ int64_t share_start(int64_t p, int64_t T, int64_t G) { return p * T / G; }
 
-template <int KV, int QF>
+// The persistent grid: workgroup p attends the tokens [floor(p T / G),
+// floor((p+1) T / G)) of the concatenated sequences and writes one partial
+// per sequence it touches, into slot p + b. TURNS: the two workgroups of a
+// compute unit take turns at priority 2 (as the split plans with long ranges
+// do). The bf16 query on the bf16 and fp8 caches comes through LDS
+// (dma_query), the sequence bounds as scalar loads.
+template <int KV, int QF, bool TURNS = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Fmt<KV>::kWgsPerCU, Fmt<KV>::kWgsPerCU)))
 void persistent_kernel(STAGE1_ARGS) {
     phase_stamp(0);
-    second_wg_priority<false>();
+    second_wg_priority<TURNS>();
+    constexpr bool QLP = KV != MLA_KV_MXFP4 && QF == 0;
     const Params P = stage1_params(q_arg, indices_arg, kv_scales_arg, nsplit_arg, uni_len_arg, uni_chunk_arg, P_arg);
     __shared__ __attribute__((aligned(16))) uint8_t smem[Layout<KV>::kBytes];
     const int64_t T = P.total, Gn = P.grid;
@@ -1988,18 +1995,24 @@ void persistent_kernel(STAGE1_ARGS) {
     }
     bool scale_out = blockIdx.x == 0;
     // first sequence b with indptr[b] <= g0 < indptr[b+1]
-    const int lo = count_le(P.indptr, P.batch, (int)g0, reinterpret_cast<int*>(smem + Layout<KV>::kIdxOff));
+    const int lo = __builtin_amdgcn_readfirstlane(
+        count_le(P.indptr, P.batch, (int)g0, reinterpret_cast<int*>(smem + Layout<KV>::kIdxOff)));
     for (int b = lo; b < P.batch; ++b) {
-        const int s = P.indptr[b], e = P.indptr[b + 1];
+        const int s = ld_scalar(P.indptr, b), e = ld_scalar(P.indptr, b + 1);
         if (s >= g1) break;
         const int t0 = (int)max<int64_t>(g0, s), t1 = (int)min<int64_t>(g1, e);
         if (t0 >= t1) continue;
         const bool whole = (s >= g0) && (e <= g1);
         __syncthreads();  // the previous sequence's epilogue has finished reading LDS
         QueryRegs<KV, QF> qr;
-        load_query<KV, QF>(P, b, qr);
+        if constexpr (QLP) {
+            query_scales<KV, QF>(P, qr);
+            dma_query<KV>(P, b, smem);
+        } else {
+            load_query<KV, QF>(P, b, qr);
+        }
         // page size 1: entries are tokens
-        run_wg<KV, QF>(P, smem, b, s, t0 - s, t1 - s, whole, p + b, scale_out, qr, false, false);
+        run_wg<KV, QF, false, 1, TURNS, QLP>(P, smem, b, s, t0 - s, t1 - s, whole, p + b, scale_out, qr, false, false);
         scale_out = false;
     }
 }
@@ -2343,9 +2356,9 @@ static int launch(const mla_plan_info& plan, const Params& P, hipStream_t stream
     const bool turns = KV == MLA_KV_FP8_E4M3 && plan.mode == 0 && plan.rows_per_wg == 1 && plan.grid > kNumCUs &&
                        (int64_t)P.total >= (int64_t)kTurnsMinTokens * plan.grid;
     // fp8 plans of many splits per sequence load the bf16 query into registers
-    // (the query through LDS measured slower there, ‡: 4 x 1k, 32 splits,
-    // 12.8 -> 13.2 us; 4 x 8k, 64 splits, 18.2 -> 18.9; every other shape
-    // measured 0.3 to 1.6 us faster with it)
+    // (with it through LDS, 4 x 1k at 32 splits measured 12.8 -> 13.2 us and
+    // 4 x 8k at 64 splits 18.2 -> 18.9, against the same library with the
+    // register query; every other shape measured 0.3 to 1.6 us faster)
     const bool q_regs = KV == MLA_KV_FP8_E4M3 && QF == 0 && plan.num_splits >= kQRegsMinSplits && !P.counters;
 #define MLA_SPLIT_ARGS                                                                                             \
     dim3(plan.grid), dim3(kThreads), 0, stream, P.q, P.indices, P.kv_scales, P.nsplit, P.uni_len, P.uni_chunk, \
@@ -2375,7 +2388,16 @@ static int launch(const mla_plan_info& plan, const Params& P, hipStream_t stream
             hipLaunchKernelGGL((split_kernel<KV, QF, false>), MLA_SPLIT_ARGS);
         }
     } else {
-        hipLaunchKernelGGL((persistent_kernel<KV, QF>), MLA_SPLIT_ARGS);
+        // the persistent grid's shares take turns at priority 2 on the same terms as the split plans
+        // (fp8 64 mixed lengths, 512 workgroups of about 1100 tokens: 79.8 -> 77.2 us together with the
+        // bf16 query through LDS and the scalar kv_indptr reads)
+        const bool pturns = KV == MLA_KV_FP8_E4M3 && plan.grid > kNumCUs &&
+                            (int64_t)P.total >= (int64_t)kTurnsMinTokens * plan.grid;
+        if (pturns) {
+            if constexpr (KV == MLA_KV_FP8_E4M3) hipLaunchKernelGGL((persistent_kernel<KV, QF, true>), MLA_SPLIT_ARGS);
+        } else {
+            hipLaunchKernelGGL((persistent_kernel<KV, QF>), MLA_SPLIT_ARGS);
+        }
     }
 #undef MLA_SPLIT_ARGS
     if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
