@@ -154,9 +154,10 @@ struct Params {
     int uni_q;
     int causal;
     int rows;
-    // Split-K with page size 1 and one row per sequence, when total is a
-    // multiple of batch: uni_len = total / batch and its split chunk (the
-    // length every sequence has when the lengths are equal); else 0.
+    // Split-K with one row per sequence, when total (tokens) is a multiple of
+    // batch, the page size a power of two and uni_len = total / batch a
+    // multiple of it: uni_len and its split chunk (the length every sequence
+    // has when the lengths are equal); else 0.
     int uni_len;
     int uni_chunk;
     // Split-K partials merged by the last-arriving split workgroup of each
@@ -1032,6 +1033,10 @@ constexpr int kQGroups = kHeads * kDqk / 8;                   // 8-element group
 constexpr int kQPer = (kQGroups + kThreads - 1) / kThreads;  // of them per thread (fp8 query)
 template <int KV>
 constexpr int kIdxPer = Fmt<KV>::kIdxWindow / kThreads;      // index entries per thread and window
+// Byte offset, in the score exchange buffer, of the staged page entries of a
+// first index window (dma_pages); its first 64 bytes stay free for the fp8
+// query's scale reduction.
+constexpr int kPageStageOff = 64;
 
 // Entries [w0, w0 + n) of a sequence whose kv_indices entries start at
 // `base`, as cache rows: thread tid takes entry w0 + tid + k * kThreads into
@@ -1065,6 +1070,25 @@ __device__ __forceinline__ void dma_idx(const Params& P, int first, int n, int32
 #pragma unroll
     for (int k = 0; k < kIdxPer<KV>; ++k)
         dma4(P.indices + first + min(tid + k * kThreads, n - 1), lds_addr(idx + k * kThreads + wave0));
+}
+
+// Page size > 1: the page entries [first, first + np) of kv_indices (1 <=
+// np <= 1024) into the page staging area of the score exchange buffer,
+// entry first + i at word i; run_wg expands them into the index window. The
+// same number of LDS-DMA operations per thread as dma_idx (loads k and k + 4
+// write the same words), so the waits that count dma_idx's hold for it.
+template <int KV>
+__device__ __forceinline__ void dma_pages(const Params& P, int first, int np, uint8_t* smem) {
+    static_assert(kIdxPer<KV> == 4 || kIdxPer<KV> == 8, "dma_idx's operation count");
+    static_assert(kPageStageOff + 4 * 4 * kThreads <= 2 * Layout<KV>::kSbufBytes,
+                  "the page staging fits the exchange buffer");
+    int32_t* st = reinterpret_cast<int32_t*>(smem + Layout<KV>::kSbufOff + kPageStageOff);
+    const int tid = threadIdx.x, wave0 = tid & ~63;
+#pragma unroll
+    for (int k = 0; k < kIdxPer<KV>; ++k) {
+        const int i = tid + (k & 3) * kThreads;
+        dma4(P.indices + first + min(i, np - 1), lds_addr(st + (k & 3) * kThreads + wave0));
+    }
 }
 
 // Row of prologue token j (< n) of this wave's tile half: the row a
@@ -1548,6 +1572,19 @@ __device__ void run_wg(const Params& P, uint8_t* smem, int b, int base, int t0, 
 #pragma unroll
             for (int k = 0; k < kPer; ++k)
                 if (tid + k * kThreads < n) idx[tid + k * kThreads] = iv[k];
+        } else if (P.page_size > 1) {
+            // the caller staged this window's page entries (dma_pages; the page size is then a
+            // power of two, ps = 2^sh): token t0 + j is row st[(t0 + j) >> sh - t0 >> sh] << sh
+            // plus (t0 + j) & (ps - 1)
+            const int sh = __builtin_ctz((unsigned)P.page_size), p0 = t0 >> sh;
+            const int32_t* st = reinterpret_cast<const int32_t*>(smem + L::kSbufOff + kPageStageOff);
+            // not unrolled: the unrolled form holds every entry's load at once and raised every
+            // stage-1 kernel's register count (by 16 VGPRs on the fp8 cache; MXFP4 spilled)
+#pragma unroll 1
+            for (int k = 0; k < kPer; ++k) {
+                const int j = tid + k * kThreads, t = t0 + j;
+                if (j < n) idx[j] = (st[(t >> sh) - p0] << sh) | (t & (P.page_size - 1));
+            }
         }
         __syncthreads();
         const int nsteps = (n + kStepTokens - 1) / kStepTokens;
@@ -1917,19 +1954,28 @@ void split_kernel(STAGE1_ARGS) {
     // window is requested now, with the query, before kv_indptr arrives. It
     // is kept when kv_indptr confirms the guess and read again otherwise; the
     // guessed entries lie within kv_indices [batch * Lu] either way.
-    const int Lu = P.uni_len;
+    // With pages (page size ps > 1, a power of two dividing Lu) the sequence
+    // holds Pu = Lu / ps of them, guessed to start at entry b * Pu: the
+    // window's page entries are staged (dma_pages) and expanded into rows by
+    // run_wg.
+    const int Lu = P.uni_len, ps = P.page_size;
+    const int Pu = ps == 1 ? Lu : Lu / ps;  // kv_indices entries of one sequence
     const int t0u = min(Lu, s * P.uni_chunk), t1u = min(Lu, t0u + P.uni_chunk);
     const bool idx_dma = t1u > t0u;  // Lu > 0
-    if (idx_dma)
-        dma_idx<KV>(P, row * Lu + t0u, min(Fmt<KV>::kIdxWindow, t1u - t0u),
-                    reinterpret_cast<int32_t*>(smem + Layout<KV>::kIdxOff));
+    if (idx_dma) {
+        const int nu = min(Fmt<KV>::kIdxWindow, t1u - t0u);
+        if (ps == 1)
+            dma_idx<KV>(P, row * Lu + t0u, nu, reinterpret_cast<int32_t*>(smem + Layout<KV>::kIdxOff));
+        else
+            dma_pages<KV>(P, row * Pu + t0u / ps, (t0u + nu - 1) / ps - t0u / ps + 1, smem);
+    }
     // With the cache size known, the first steps' rows of a contiguous cache
     // are requested as well (kept by run_wg where kv_indices agrees). Not on
     // the MXFP4 cache: the wait for the query registers also drains LDS-DMA
     // loads issued before it, which would put the query split behind the
     // first rows instead of beside them.
     const int64_t early_first =
-        (KV != MLA_KV_MXFP4 && idx_dma && P.kv_rows > 0) ? (int64_t)row * Lu + t0u : -1;
+        (KV != MLA_KV_MXFP4 && idx_dma && ps == 1 && P.kv_rows > 0) ? (int64_t)row * Lu + t0u : -1;
     if (early_first >= 0) issue_early<KV>(P, smem, early_first, min(Fmt<KV>::kIdxWindow, t1u - t0u));
     // the sequence of this query row, and the cache tokens the causal reading hides from it
     // (the reads of kv_indptr, qo_indptr and kv_last_page_len are scalar loads: ld_scalar)
@@ -1957,7 +2003,7 @@ void split_kernel(STAGE1_ARGS) {
     const int chunk = ((L + P.nsplit - 1) / P.nsplit + kStepTokens - 1) / kStepTokens * kStepTokens;
     const int t0 = min(L, s * chunk);
     const int t1 = min(L, t0 + chunk);
-    const bool staged = idx_dma && base == row * Lu && L == Lu;  // then t0, t1 are t0u, t1u
+    const bool staged = idx_dma && base == row * Pu && L == Lu;  // then t0, t1 are t0u, t1u
     run_wg<KV, QF, MG, 1, TURNS, QL>(P, smem, row, base, t0, t1, P.nsplit == 1, row * P.nsplit + s, blockIdx.x == 0,
                                      qr, idx_dma, staged, early_first);
 }
@@ -2547,7 +2593,13 @@ static int decode_impl(const void* q, const void* kv, const void* kv_scales, con
     P.rows = rows;
     P.uni_len = 0;
     P.uni_chunk = 0;
-    if (plan.mode == 0 && page_size == 1 && !mtp && total_kv > 0 && total_kv % batch == 0) {
+    // With pages, only for a power-of-two page size (run_wg expands the
+    // staged page entries with shifts) and a common length that is a whole
+    // number of pages: then the batch holds at least batch * Lu / page_size
+    // page entries whatever its lengths, so the guessed window never reads
+    // past kv_indices.
+    if (plan.mode == 0 && !mtp && total_kv > 0 && total_kv % batch == 0 && (page_size & (page_size - 1)) == 0 &&
+        (total_kv / batch) % page_size == 0) {
         const int Lu = (int)(total_kv / batch), ns = plan.num_splits;
         P.uni_len = Lu;
         P.uni_chunk = ((Lu + ns - 1) / ns + kStepTokens - 1) / kStepTokens * kStepTokens;  // as the kernel splits
