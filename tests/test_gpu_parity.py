@@ -464,6 +464,26 @@ def test_page_size_one_is_mla_decode(mla, dev, kv_dtype):
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+def test_paged_equal_length_index_guess(mla, orc, dev, kv_dtype):
+    """With equal lengths that are whole pages of a power-of-two size, stage 1 stages
+    each split's first page entries before kv_indptr arrives, guessing sequence b's
+    pages to start at entry b * Lu / page_size, and expands them into rows once the
+    guess is confirmed. Kept (equal lengths; one index window and several), rejected
+    (the same total over unequal lengths, an empty sequence among them) and not made
+    (a page size that is no power of two; a length that is not whole pages): every
+    result within the oracle's bounds, on shuffled physical pages."""
+    cases = [("kept", [2048] * 4, 8, 0), ("kept, split", [2048] * 4, 8, 3), ("kept, windows", [4608] * 2, 16, 1),
+             ("kept, big pages", [1024] * 3, 64, 0), ("rejected", [128, 0, 192, 192], 8, 0),
+             ("rejected, split", [256, 512, 0, 256], 8, 3), ("no power of two", [1200] * 3, 12, 0),
+             ("not whole pages", [100] * 4, 8, 0)]
+    for name, lens, ps, splits in cases:
+        case, paged = syn.make_paged_case(len(lens), lens, kv_dtype, ps, seed=90 + ps + splits, extra_pages=3)
+        flags = mla.flags_for(splits=splits) if splits else 0
+        check(run_gpu_paged(mla, case, paged, dev, flags=flags), oracle_ref_paged(orc, case, paged),
+              f"{name}, page_size={ps}")
+
+
 @pytest.mark.parametrize("name", list(syn.PAGED))
 def test_paged_full_size_page8(mla, orc, dev, name):
     """The pages' paged configuration for kv >= 8192: 8-row pages over shuffled physical
