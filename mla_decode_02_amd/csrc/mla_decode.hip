@@ -1870,16 +1870,23 @@ __device__ __forceinline__ int count_le(const int32_t* ptr, int n, int v, int* c
 
 // The stage-1 kernels take the fields their first loads need ahead of Params
 // as plain arguments: those arrive in SGPRs when the waves start (kernel
-// argument preloading), so the query and index requests leave without first
-// waiting for the kernel-argument segment to be read.
+// argument preloading, 14 SGPRs), so the query, index and first row requests
+// leave without first waiting for the kernel-argument segment to be read.
+// kv_rows comes as 32 bits, clamped: a smaller bound on the rows gathered
+// before kv_indices arrives stays inside the cache buffer.
 // (The launched grid size comes the same way: gridDim is read from the
 // kernel-argument segment.)
 #define STAGE1_ARGS                                                                                       \
-    const __bf16 *q_arg, const int32_t *indices_arg, const void *kv_scales_arg, int nsplit_arg, int uni_len_arg, \
-        int uni_chunk_arg, int nblocks, Params P_arg
+    const __bf16 *q_arg, const int32_t *indices_arg, const void *kv_scales_arg, const uint8_t *kv_arg,          \
+        int nsplit_arg, int uni_len_arg, int uni_chunk_arg, int nblocks, int page_size_arg, int kv_rows_arg,       \
+        Params P_arg
 __device__ __forceinline__ Params stage1_params(const __bf16* q, const int32_t* indices, const void* kv_scales,
-                                                int nsplit, int uni_len, int uni_chunk, const Params& P_arg) {
+                                                const uint8_t* kv, int nsplit, int uni_len, int uni_chunk,
+                                                int page_size, int kv_rows, const Params& P_arg) {
     Params P = P_arg;
+    P.kv = kv;
+    P.page_size = page_size;
+    P.kv_rows = kv_rows;
     P.q = q;
     P.indices = indices;
     P.kv_scales = kv_scales;
@@ -1932,7 +1939,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Fmt<KV
 void split_kernel(STAGE1_ARGS) {
     phase_stamp(0);
     second_wg_priority<TURNS>();
-    const Params P = stage1_params(q_arg, indices_arg, kv_scales_arg, nsplit_arg, uni_len_arg, uni_chunk_arg, P_arg);
+    const Params P = stage1_params(q_arg, indices_arg, kv_scales_arg, kv_arg, nsplit_arg, uni_len_arg, uni_chunk_arg,
+                                   page_size_arg, kv_rows_arg, P_arg);
     __shared__ __attribute__((aligned(16))) uint8_t smem[Layout<KV>::kBytes];
     if constexpr (NT == 2) {
         split_pair<KV, QF, MG>(P, smem, nblocks);
@@ -2024,7 +2032,8 @@ void persistent_kernel(STAGE1_ARGS) {
     phase_stamp(0);
     second_wg_priority<TURNS>();
     constexpr bool QLP = KV != MLA_KV_MXFP4 && QF == 0;
-    const Params P = stage1_params(q_arg, indices_arg, kv_scales_arg, nsplit_arg, uni_len_arg, uni_chunk_arg, P_arg);
+    const Params P = stage1_params(q_arg, indices_arg, kv_scales_arg, kv_arg, nsplit_arg, uni_len_arg, uni_chunk_arg,
+                                   page_size_arg, kv_rows_arg, P_arg);
     __shared__ __attribute__((aligned(16))) uint8_t smem[Layout<KV>::kBytes];
     const int64_t T = P.total, Gn = P.grid;
     const int p = xcd_order(blockIdx.x, nblocks);
@@ -2407,8 +2416,8 @@ static int launch(const mla_plan_info& plan, const Params& P, hipStream_t stream
     // register query; every other shape measured 0.3 to 1.6 us faster)
     const bool q_regs = KV == MLA_KV_FP8_E4M3 && QF == 0 && plan.num_splits >= kQRegsMinSplits && !P.counters;
 #define MLA_SPLIT_ARGS                                                                                             \
-    dim3(plan.grid), dim3(kThreads), 0, stream, P.q, P.indices, P.kv_scales, P.nsplit, P.uni_len, P.uni_chunk, \
-        plan.grid, P
+    dim3(plan.grid), dim3(kThreads), 0, stream, P.q, P.indices, P.kv_scales, P.kv, P.nsplit, P.uni_len,       \
+        P.uni_chunk, plan.grid, P.page_size, (int)std::min<int64_t>(P.kv_rows, INT32_MAX), P
     if (plan.rows_per_wg == 2) {
         if constexpr (KV == MLA_KV_BF16 && QF == 0) {
             if (plan.mode != 0 || P.uni_q < 2) return MLA_ERR_INVALID_ARG;
