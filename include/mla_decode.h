@@ -205,11 +205,12 @@ int mla_decode_noalloc(const void* q, const void* kv, const void* kv_scales, con
  *            must be below it. 0 = unknown, which is exactly mla_decode.
  *   all other arguments, the outputs, the errors and the results as for
  *   mla_decode; MLA_ERR_INVALID_ARG also for kv_rows < 0.
- * With kv_rows known and every sequence of the same length L (total_kv a
- * multiple of batch), each stage-1 workgroup requests the first rows of its
- * token range as a contiguous cache would place them (sequence b at rows
- * b * L .. b * L + L - 1, clamped below kv_rows) together with its query and
- * kv_indices reads, before kv_indices has arrived. It keeps them only when
+ * With kv_rows known, each stage-1 workgroup requests the first rows of its
+ * token range as a contiguous cache would place them (entry t of kv_indices
+ * in row t, clamped below kv_rows) together with its query and kv_indices
+ * reads, before kv_indices has arrived: on split-K plans when every sequence
+ * has the same length (total_kv a multiple of batch, so the range is known
+ * before kv_indptr too), on the persistent grid always. It keeps them only when
  * kv_indices names exactly those rows and gathers again otherwise, so the
  * result does not depend on the cache layout; a contiguous cache saves one
  * dependent memory round trip at start-up. The bf16 and fp8 caches do this;

@@ -1098,11 +1098,12 @@ __device__ __forceinline__ int64_t early_row(const Params& P, int64_t first, int
     return min(first + min(j, n - 1), P.kv_rows - 1);
 }
 
-// Equal lengths and a known cache size: the gathers of the first D steps of
-// a range whose kv_indices entries are guessed to be first, first + 1, ...
-// (the rows a contiguous cache gives the sequence), issued with the query and
-// index requests so that the first rows arrive in the same memory round trip.
-// run_wg keeps them only where kv_indices confirms every row.
+// A known cache size: the gathers of the first D steps of a range whose
+// kv_indices entries are guessed to be first, first + 1, ... (the rows a
+// contiguous cache gives the sequence), issued with the query and index
+// requests so that the first rows arrive in the same memory round trip (split
+// plans with equal lengths, and every share of the persistent grid). run_wg
+// keeps them only where kv_indices confirms every row.
 template <int KV>
 __device__ __forceinline__ void issue_early(const Params& P, uint8_t* smem, int64_t first, int n) {
     using L = Layout<KV>;
@@ -2024,8 +2025,10 @@ __device__ __forceinline__ int64_t share_start(int64_t p, int64_t T, int64_t G) 
 // floor((p+1) T / G)) of the concatenated sequences and writes one partial
 // per sequence it touches, into slot p + b. TURNS: the two workgroups of a
 // compute unit take turns at priority 2 (as the split plans with long ranges
-// do). The bf16 query on the bf16 and fp8 caches comes through LDS
-// (dma_query), the sequence bounds as scalar loads.
+// do). The sequence bounds are scalar loads. On the bf16 and fp8 caches each
+// sequence's bf16 query comes through LDS (dma_query), requested together
+// with the first index window and, with the cache size known, the first
+// steps' rows of a contiguous cache.
 template <int KV, int QF, bool TURNS = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Fmt<KV>::kWgsPerCU, Fmt<KV>::kWgsPerCU)))
 void persistent_kernel(STAGE1_ARGS) {
@@ -2060,14 +2063,27 @@ void persistent_kernel(STAGE1_ARGS) {
         const bool whole = (s >= g0) && (e <= g1);
         __syncthreads();  // the previous sequence's epilogue has finished reading LDS
         QueryRegs<KV, QF> qr;
+        // page size 1: entries are tokens; this share holds entries [t0, t1) of sequence b
+        bool idx_dma = false;
+        int64_t early_first = -1;
         if constexpr (QLP) {
+            // the query, the first index window and, with the cache size known, the first
+            // steps' rows of a contiguous cache (entry t0 + j in row t0 + j; kept by run_wg
+            // where kv_indices agrees) are requested together, as the split plans do
             query_scales<KV, QF>(P, qr);
             dma_query<KV>(P, b, smem);
+            const int nu = min(Fmt<KV>::kIdxWindow, t1 - t0);
+            dma_idx<KV>(P, t0, nu, reinterpret_cast<int32_t*>(smem + Layout<KV>::kIdxOff));
+            idx_dma = true;
+            if (P.kv_rows > 0) {
+                early_first = t0;
+                issue_early<KV>(P, smem, early_first, nu);
+            }
         } else {
             load_query<KV, QF>(P, b, qr);
         }
-        // page size 1: entries are tokens
-        run_wg<KV, QF, false, 1, TURNS, QLP>(P, smem, b, s, t0 - s, t1 - s, whole, p + b, scale_out, qr, false, false);
+        run_wg<KV, QF, false, 1, TURNS, QLP>(P, smem, b, s, t0 - s, t1 - s, whole, p + b, scale_out, qr, idx_dma,
+                                             idx_dma, early_first);
         scale_out = false;
     }
 }

@@ -629,10 +629,13 @@ def _with_indices(case, indices, rows=None):
 
 @pytest.mark.parametrize("kv_dtype", DTYPES)
 def test_early_gathers_match_the_plain_call(mla, orc, dev, kv_dtype):
-    """With equal lengths and the cache size known, stage 1 requests the rows a
-    contiguous cache holds before kv_indices arrives, and keeps them only where
-    kv_indices agrees. Whatever the indices, the result is bit-identical to the
-    call without early requests (kv_rows = 0), and within the oracle's bounds:
+    """With the cache size known, stage 1 requests the rows a contiguous cache
+    holds before kv_indices arrives (split plans: with equal lengths, before
+    kv_indptr too; the persistent grid: each share's first rows of a sequence),
+    and keeps them only where kv_indices agrees. Whatever the indices, the
+    result is bit-identical to the call without early requests (kv_rows = 0),
+    on split plans and on persistent grids whose shares start inside
+    sequences, and within the oracle's bounds:
     contiguous indices (all kept), shuffled (all gathered again), contiguous
     but for a few entries in the first steps of some ranges (only those waves
     gather again), and a cache with fewer rows than tokens (indices repeat;
@@ -652,7 +655,8 @@ def test_early_gathers_match_the_plain_call(mla, orc, dev, kv_dtype):
              ("patched", _with_indices(base, patched)), ("repeating", _with_indices(base, repeating, rows=small))]
     for name, case in cases:
         ref = oracle_ref(orc, case)
-        for flags in (0, mla.flags_for(splits=3), mla.flags_for(splits=1)):
+        for flags in (0, mla.flags_for(splits=3), mla.flags_for(splits=1),
+                      mla.flags_for(persistent=True, grid=5), mla.flags_for(persistent=True, grid=64)):
             early = _run_rows(mla, case, dev, None, flags)
             plain = _run_rows(mla, case, dev, 0, flags)
             assert np.array_equal(early[0], plain[0]), f"{name} flags={flags:#x}: out differs from the plain call"
@@ -661,13 +665,16 @@ def test_early_gathers_match_the_plain_call(mla, orc, dev, kv_dtype):
 
 
 def test_early_gathers_unequal_lengths(mla, orc, dev):
-    """Lengths that differ (the guessed range is rejected once kv_indptr arrives):
-    the early requests are dropped and the result equals the plain call's."""
+    """Lengths that differ: the split plan's guessed range is rejected once
+    kv_indptr arrives and its early requests are dropped; the persistent grid's
+    requests (each share's first rows, contiguous here) are kept. Either way
+    the result equals the plain call's."""
     case = syn.make_case(5, [700, 700, 0, 2000, 33], syn.KV_FP8, seed=97)
     case = _with_indices(case, np.arange(case.total_kv, dtype=np.int32))
-    a = _run_rows(mla, case, dev, None)
-    b = _run_rows(mla, case, dev, 0)
-    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    for flags in (0, mla.flags_for(persistent=True, grid=7), mla.flags_for(persistent=True, grid=40)):
+        a = _run_rows(mla, case, dev, None, flags)
+        b = _run_rows(mla, case, dev, 0, flags)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), f"flags={flags:#x}"
     check(run_gpu(mla, case, dev), oracle_ref(orc, case), "early gathers, unequal lengths")
     with pytest.raises(ValueError):  # a bound beyond the cache tensor is refused before any launch
         _run_rows(mla, case, dev, int(case.kv.shape[0]) + 1)
