@@ -8,9 +8,11 @@
 // the tokens, output over the first 512 dims of the same rows.
 //
 // Stage 1: one workgroup of four waves attends one token range of one query
-// row, in 32-token steps (two 16-token tiles). At wave start the query and,
-// on batches of equal lengths, a guessed first window of kv_indices are
-// requested together with the sequence's kv_indptr entries. Per step:
+// row (or, on the bf16 cache with several query tokens, of two rows), in
+// 32-token steps (two 16-token tiles). At wave start the query, the first
+// window of kv_indices (guessed on split plans with equal lengths, before
+// kv_indptr arrives) and, with the cache's row count known, the first steps'
+// rows of a contiguous cache are requested together. Per step:
 //   1. The step's 32 cache rows are gathered through kv_indices straight from
 //      HBM into an LDS ring with LDS-DMA loads (global_load_lds_dwordx4; the
 //      MXFP4 scales with two-byte DMAs), kRing - 1 steps ahead of use. Each
@@ -35,9 +37,11 @@
 //      of the same staged rows: V is the first 512 columns of K, so each row is
 //      fetched from HBM once.
 // The loop is software-pipelined with one barrier per step. The result is the
-// final bf16 output + lse, or an fp32 partial (normalised O and its lse) for
-// the combine kernel (flash-decoding split partials and log-sum-exp merge:
-// submission 593653, `_flash_fp8_split_s1` / `_flash_fp8_split_s2`).
+// final bf16 output + lse, or a split partial (normalised O and its lse;
+// fp32, or bf16 on plans of 5 to 8 splits merged in stage 1) that the
+// last-arriving split of the row or the combine kernel merges (flash-decoding
+// split partials and log-sum-exp merge: submission 593653,
+// `_flash_fp8_split_s1` / `_flash_fp8_split_s2`).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
